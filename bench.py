@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 MoE decode layer on one MI355X.
+
+A step is one whole layer -- moe_route, moe_sort_by_expert, moe_mxfp4_forward
+(router GEMV + top-k, the sort by expert, every active expert's fused dequant
+GEMVs and the weighted combine plus the shared expert) -- on the next of
+`--sets` distinct layer weight sets, so consecutive steps never reuse expert
+weights and the 256 MB Infinity Cache cannot serve them.  Steps are replayed
+from a HIP graph of one pass over all sets; inputs are resident in HBM before
+the timed region starts.
+
+Prints one JSON line:
+  value        layer GB/s: algorithmic bytes of a layer / time per layer
+  ms_per_step  time per layer
+  roofline     the forward's kernels (expert weights, the dominant bytes):
+               expert bytes per launch / mean launch span, measured with HIP
+               events that take the kernels' own begin/end timestamps
+  cpu_baseline the float64 oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer µs & HBM GB/s (% of 8 TB/s), 2560×768×512e top-8, M=1/4"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes_per_expert(H, I):
+    return 2 * I * (H // 2 + H // 32) + H * (I // 2 + I // 32)
+
+
+def layer_bytes(wl, D):
+    """Algorithmic bytes of one layer: every weight the method must read once
+    (router, D active routed experts + shared), activations in, output out."""
+    bias = 0
+    if wl.routing == "overlap":
+        bias = wl.M * wl.E * 4
+    elif wl.routing == "zipf":
+        bias = wl.E * 4
+    expert = (D + int(wl.shared)) * expert_bytes_per_expert(wl.H, wl.I)
+    return expert, wl.E * wl.H * 4 + wl.M * wl.H * 2 + wl.M * wl.H * 4 + bias + expert
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def device_sets(torch, wl, nsets):
+    """x / router / bias from the seeded numpy generator; the expert banks are
+    filled on the device with torch's seeded generator (same distribution:
+    uniform code bytes, scale bytes uniform over [120, 127]) -- 1.6 GB per set
+    would take about a minute per 40 sets on the host."""
+    from mxfp4_expert_weight_amd import synth
+    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, to_device
+    out = []
+    n, H, I = wl.E + 1, wl.H, wl.I
+    for l in range(nsets):
+        ls = synth.layer_set(wl, l, banks=False)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(wl.seed * 1_000_003 + l)
+        u8 = dict(dtype=torch.uint8, device="cuda", generator=g)
+        out.append(DeviceLayerSet(
+            to_device(ls.x_bits), to_device(ls.w_router), to_device(ls.bias), ls.bias_row_stride,
+            torch.randint(0, 256, (n, 2 * I, H // 2), **u8), torch.randint(120, 128, (n, 2 * I, H // 32), **u8),
+            torch.randint(0, 256, (n, H, I // 2), **u8), torch.randint(120, 128, (n, H, I // 32), **u8),
+            wl.M, H, I, wl.E, wl.k, wl.shared))
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(wl, seconds_budget=20.0):
+    """The oracle as it stands, on host-generated sets of the same workload."""
+    import numpy as np
+
+    import oracle
+    from mxfp4_expert_weight_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    times, nbytes, tokens = [], [], 0
+    start = time.time()
+    l = 0
+    while l < wl.sets and (time.time() - start) < seconds_budget:
+        ls = synth.layer_set(wl, l)
+        t0 = time.perf_counter()
+        if wl.M <= 8:
+            r = oracle.moe_layer(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s,
+                                 wl.k, wl.shared)
+            D = r["num_active"]
+            frac = 1.0
+        else:   # large batches: a bounded token sample, scaled to the layer
+            sample = list(range(0, wl.M, max(1, wl.M // 4)))[:4]
+            oracle.moe_layer_tokens(sample, ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s,
+                                    ls.w2_q, ls.w2_s, wl.k, wl.shared)
+            D = int(np.unique(oracle.topk_softmax(oracle.router_logits(
+                oracle.bf16_bits_to_f64(ls.x_bits), ls.w_router, ls.bias), wl.k)[0]).size)
+            frac = len(sample) / wl.M
+        dt = time.perf_counter() - t0
+        times.append(dt / frac)
+        nbytes.append(layer_bytes(wl, D)[1])
+        tokens += wl.M if frac == 1.0 else len(sample)
+        l += 1
+    sec = sum(times) / len(times)
+    gbs = sum(nbytes) / len(nbytes) / sec / 1e9
+    kind = "whole layers" if wl.M <= 8 else "4 tokens per layer, time scaled to M tokens"
+    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} layer sets of {wl.name} ({kind}); {sec * 1e3:.1f} ms per layer",
+            "us_per_layer": sec * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="ling_m1")
+    ap.add_argument("--sets", type=int, default=None, help="layer sets rotated (default: the workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (reference for rocprof byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(how the layer would shard is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mxfp4_expert_weight_amd import binding, synth
+    from mxfp4_expert_weight_amd.layer import LayerBuffers, run_layer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.lib()
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy probe: 3 x 1 GiB device-to-device copies")
+        return
+
+    wl = synth.WORKLOADS[args.workload]
+    nsets = args.sets or wl.sets
+    t0 = time.time()
+    sets = device_sets(torch, wl, nsets)
+    log(f"[bench] {nsets} layer sets of {wl.name} on the device in {time.time() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
+    buf = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
+    weights = [d.weights() for d in sets]
+
+    # one eager pass: loads the kernels and records each set's distinct-expert count
+    D = []
+    for d, w in zip(sets, weights):
+        run_layer(d, buf, w)
+        D.append(int(buf.num_active.item()))
+    log(f"[bench] distinct routed experts per set: min {min(D)} max {max(D)} mean {sum(D) / len(D):.2f}")
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(n):
+                run_layer(sets[i % nsets], buf, weights[i % nsets])
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            for i in range(n):
+                run_layer(sets[i % nsets], buf, weights[i % nsets])
+        return g
+
+    g_full = capture(nsets)
+    rem = args.steps % nsets
+    g_rem = capture(rem) if rem else None
+    reps = args.steps // nsets
+
+    for _ in range(math.ceil(args.warmup / nsets)):
+        g_full.replay()
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    for _ in range(reps):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    step_sets = [i % nsets for i in range(args.steps)]
+    exp_b = [layer_bytes(wl, D[l])[0] for l in step_sets]
+    lay_b = [layer_bytes(wl, D[l])[1] for l in step_sets]
+    layer_gbs = sum(lay_b) / (ms_total * 1e-3) / 1e9
+    log(f"[bench] {args.steps} steps in {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms): "
+        f"{ms_per_step * 1e3:.2f} us/layer, {layer_gbs:.0f} GB/s")
+
+    # Roofline of the forward's kernels: per-launch spans from HIP events bound to
+    # the kernels' own begin/end timestamps, over the same K steps (eager).
+    hev = HipEvents()
+    n_ev = min(args.steps, 4000)
+    starts = [hev.create() for _ in range(n_ev)]
+    stops = [hev.create() for _ in range(n_ev)]
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    for i in range(n_ev):
+        d, w = sets[step_sets[i]], weights[step_sets[i]]
+        binding.moe_route(d.x, d.w_router, d.bias, d.bias_row_stride, d.M, d.H, d.E, d.k, buf.logits,
+                          buf.ids, buf.weights, stream)
+        binding.moe_sort_by_expert(buf.ids, d.M, d.k, d.E, buf.offsets, buf.pairs, buf.active,
+                                   buf.num_active, stream)
+        binding.moe_mxfp4_forward_timed(d.x, w, d.M, d.k, buf.weights, buf.offsets, buf.pairs, buf.active,
+                                        buf.num_active, buf.y, buf.ws, buf.ws_bytes, starts[i], stops[i],
+                                        stream)
+    torch.cuda.synchronize()
+    spans = [hev.elapsed_ms(starts[i], stops[i]) for i in range(n_ev)]
+    for e in starts + stops:
+        hev.destroy(e)
+    fwd_ms = sum(spans) / n_ev
+    fwd_bytes = sum(exp_b[:n_ev]) / n_ev
+    achieved = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    log(f"[bench] forward kernels: {fwd_ms * 1e3:.2f} us per launch, {fwd_bytes / 1e6:.2f} MB expert "
+        f"weights, {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(layer_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "hidden": wl.H, "inter": wl.I, "experts": wl.E,
+                   "top_k": wl.k, "shared_expert": wl.shared, "routing": wl.routing,
+                   "layer_sets_rotated": nsets, "weights": "MXFP4 (E2M1 + E8M0/32)",
+                   "activations": "bf16"},
+        "us_per_layer": ms_per_step * 1e3,
+        "layer_bytes": sum(lay_b) / len(lay_b),
+        "layer_frac_of_hbm_peak": layer_gbs / HBM_PEAK_GBS,
+        "mean_distinct_experts": sum(D[l] for l in step_sets) / len(step_sets),
+        "roofline": {"bound": "hbm", "kernel": "moe_mxfp4_forward (gateup_kernel + down_kernel)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "us_per_launch": fwd_ms * 1e3, "bytes_per_launch": fwd_bytes},
+    }
+    if not args.no_cpu_baseline:
+        del sets
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * moe_mxfp4.h -- C ABI of the MI355X (gfx950) MXFP4 expert-weight MoE decode layer.
+ *
+ * The layer (the decode-time MoE of "3 Ways to Improve MoE Inference on NVIDIA
+ * DGX Spark", digest sections 1-3 and 5): a router scores all E experts of each
+ * token and keeps the top-k (8 of 512) with renormalised softmax weights; one
+ * shared expert always runs; all (token, expert) pairs are sorted by expert so
+ * each expert's MXFP4 weights are read once per batch (MoE-SpeQ article, section
+ * 4.2); each expert computes h = SiLU(x Wg^T) * (x Wu^T) and h Wd^T; a weighted
+ * cross-expert reduction forms y (MoE-SpeQ article, section 3.2).
+ *
+ * Conventions shared by every call
+ *  - Pointers marked "device" are HIP device pointers owned by the caller; the
+ *    library allocates nothing, keeps no state between calls and never copies
+ *    device data to the host.  All work is enqueued on `stream` (a hipStream_t;
+ *    NULL = the default stream) and is asynchronous; no call synchronises.
+ *  - Argument checks run on the host before anything is enqueued and return a
+ *    status; nothing is launched when a check fails.  MOE_ERR_HIP means a launch
+ *    was rejected by the HIP runtime (e.g. no gfx950 device).  No call aborts,
+ *    throws or falls back to another implementation.
+ *  - Calls that share a workspace or output buffer on one stream are ordered by
+ *    the stream; concurrent calls on different streams must not share them.
+ *  - MXFP4 tensor [N][K] (K % 32 == 0), row-major:
+ *      codes  uint8 [N][K/2]:  byte j of a row holds element 2j in its low nibble
+ *                              and element 2j+1 in its high nibble;
+ *      scales uint8 [N][K/32]: E8M0 byte s of block b scales elements 32b..32b+31
+ *                              of the row by 2^(s-127).
+ *    A 4-bit code c is E2M1: sign = bit 3, magnitude = {0,0.5,1,1.5,2,3,4,6}[c&7].
+ *    (The pages name MXFP4 but do not define it; this is the OCP MX v1.0 format.)
+ *    Dequantisation is exact for scale bytes in [2, 252]; outside that range
+ *    results are undefined (the layer's workloads use [120, 127]).
+ *  - Activations are bf16 bit patterns (uint16).  Outputs are float32.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,       /* a required pointer is NULL                              */
+  MOE_ERR_SHAPE = 2,      /* a size is outside the documented limits                 */
+  MOE_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned where required          */
+  MOE_ERR_WORKSPACE = 4,  /* workspace smaller than moe_workspace_bytes(...)          */
+  MOE_ERR_HIP = 5         /* the HIP runtime rejected a launch                       */
+} moe_status;
+
+/* Limits checked by every call. */
+#define MOE_MAX_EXPERTS 1024   /* E (routed experts)                        */
+#define MOE_MAX_TOPK 32        /* k, also k <= E                            */
+#define MOE_MAX_HIDDEN 8192    /* H, multiple of 32                         */
+#define MOE_MAX_INTER 4096     /* I, multiple of 32                         */
+#define MOE_MAX_TOKENS 65536   /* M                                         */
+
+/* Expert bank of one layer: E routed experts, then (if has_shared) the shared
+ * expert at index E.  All four pointers are device pointers, 16-byte aligned.
+ *   w13_q [E+S][2I][H/2], w13_s [E+S][2I][H/32]: rows 0..I-1 are W_gate, rows
+ *        I..2I-1 are W_up (each [I][H], reduction over H);
+ *   w2_q  [E+S][H][I/2],  w2_s  [E+S][H][I/32]:  W_down [H][I] (reduction over I). */
+typedef struct {
+  const uint8_t* w13_q;
+  const uint8_t* w13_s;
+  const uint8_t* w2_q;
+  const uint8_t* w2_s;
+  int32_t num_experts;  /* E */
+  int32_t hidden;       /* H */
+  int32_t inter;        /* I */
+  int32_t has_shared;   /* S: 0 or 1 */
+} moe_mxfp4_weights;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status st);
+
+/* Bytes of device workspace moe_mxfp4_forward needs for these sizes
+ * (0 if the sizes are outside the limits). */
+size_t moe_workspace_bytes(int32_t M, int32_t top_k, int32_t E, int32_t H, int32_t I);
+
+/* Router: logits, top-k and renormalised weights ("NVIDIA three-layer
+ * optimisation" news rewrite, paragraph on sparse activation and expert
+ * routing; the gate stays in high precision per the MoE-SpeQ article, 2.1).
+ *   x            device bf16 [M][H]
+ *   w_router     device fp32 [E][H]
+ *   logit_bias   device fp32, NULL (no bias), [E] (bias_row_stride = 0) or
+ *                [M][E] (bias_row_stride = E); added to the logits before top-k
+ *   logits       device fp32 [M][E], output: x . w_router[e] + bias, fp32
+ *                accumulation of exact bf16*fp32 products
+ *   topk_ids     device int32 [M][k], output: per token the k largest logits in
+ *                descending order, ties to the lower expert index
+ *   topk_weights device fp32 [M][k], output: exp(l_i - l_max) / sum over the kept
+ *                experts (the softmax renormalised over the top-k)
+ * Limits: 1 <= M <= MOE_MAX_TOKENS, 32 <= H <= MOE_MAX_HIDDEN, H % 32 == 0,
+ * 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS; x and w_router 16-byte aligned. */
+moe_status moe_route(const uint16_t* x, const float* w_router, const float* logit_bias,
+                     int64_t bias_row_stride, int32_t M, int32_t H, int32_t E, int32_t top_k,
+                     float* logits, int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* The top-k + renormalised softmax step of moe_route alone, on given logits
+ * (device fp32 [M][E]); outputs as in moe_route.  Same limits on M, E, k. */
+moe_status moe_topk_softmax(const float* logits, int32_t M, int32_t E, int32_t top_k,
+                            int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* Sort the M*k flattened pairs p = t*k + s by expert, stably (MoE-SpeQ article,
+ * section 4.2: collect every token's expert assignments, order them by expert
+ * id, run each expert once over its tokens).
+ *   topk_ids        device int32 [M][k], values in [0, E)
+ *   expert_offsets  device int32 [E+1], output: pairs of expert e occupy
+ *                   sorted_pairs[expert_offsets[e] .. expert_offsets[e+1])
+ *   sorted_pairs    device int32 [M*k], output: pair indices, ascending within an expert
+ *   active_experts  device int32 [E], output: the D experts with at least one
+ *                   pair, ascending, in entries 0..D-1 (the rest untouched)
+ *   num_active      device int32 [1], output: D
+ * Limits as moe_route.  Ids outside [0, E) are skipped (they take no place in the
+ * output and expert_offsets[E] counts only the valid ones). */
+moe_status moe_sort_by_expert(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_t E,
+                              int32_t* expert_offsets, int32_t* sorted_pairs,
+                              int32_t* active_experts, int32_t* num_active, void* stream);
+
+/* The experts and the combine: for every active expert e and each of its pairs
+ * p = t*k + s, h = SiLU(x_t Wg_e^T) * (x_t Wu_e^T) and
+ *   y_t = sum_s topk_weights[t][s] * (h Wd_e^T) + (shared expert of x_t, weight 1).
+ * Reads the sort outputs on the device (num_active is never copied to the host).
+ *   x                      device bf16 [M][H], 16-byte aligned
+ *   w                      host pointer to the expert bank descriptor
+ *   topk_weights           device fp32 [M][k]
+ *   expert_offsets, sorted_pairs, active_experts, num_active: moe_sort_by_expert outputs
+ *   y                      device fp32 [M][H], output (overwritten)
+ *   workspace              device, >= moe_workspace_bytes(M, k, E, H, I) bytes, 256-byte
+ *                          aligned; its contents on entry are ignored
+ * Limits as moe_route plus 32 <= I <= MOE_MAX_INTER, I % 32 == 0. */
+moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                             const float* topk_weights, const int32_t* expert_offsets,
+                             const int32_t* sorted_pairs, const int32_t* active_experts,
+                             const int32_t* num_active, float* y, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* moe_mxfp4_forward, plus timing: `start_event` / `stop_event` (hipEvent_t, may be
+ * NULL) take the begin timestamp of the forward's first kernel and the end
+ * timestamp of its last kernel (hipExtLaunchKernelGGL), so hipEventElapsedTime
+ * gives the kernels' own execution span without queueing gaps before it.
+ * For measurement; results are those of moe_mxfp4_forward. */
+moe_status moe_mxfp4_forward_timed(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
+                                   int32_t top_k, const float* topk_weights,
+                                   const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                                   const int32_t* active_experts, const int32_t* num_active, float* y,
+                                   void* workspace, size_t workspace_bytes, void* start_event,
+                                   void* stop_event, void* stream);
+
+/* Dequantise an MXFP4 tensor [rows][cols] (layout above) to fp32 with the same
+ * device routine the expert kernels use (exposes it for exact checks).
+ *   q device uint8 [rows][cols/2], s device uint8 [rows][cols/32], out device fp32 [rows][cols]
+ * Limits: rows >= 1, cols >= 32, cols % 32 == 0, rows*cols < 2^40; q 16-byte aligned. */
+moe_status moe_mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
+                                float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

@@ -1,0 +1,169 @@
+"""ctypes binding of libmoe_mxfp4.so -- argument marshalling only.
+
+Every function has the name and argument order of the C call declared in
+include/moe_mxfp4.h.  Pointer arguments accept a torch tensor (its
+``data_ptr()``), an int address, or None (NULL).  ``stream`` is a hipStream_t
+handle (int); None means the current torch stream when torch has a GPU, else
+the default stream.  A non-OK status raises MoeError carrying the status.
+There is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mxfp4.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "include", "moe_mxfp4.h")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class moe_mxfp4_weights(ctypes.Structure):
+    _fields_ = [
+        ("w13_q", ctypes.c_void_p),
+        ("w13_s", ctypes.c_void_p),
+        ("w2_q", ctypes.c_void_p),
+        ("w2_s", ctypes.c_void_p),
+        ("num_experts", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("has_shared", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "moe_route": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "moe_topk_softmax": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_sort_by_expert": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
+    "moe_mxfp4_forward": (ctypes.c_int, [_P, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P, _P,
+                                         _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_forward_timed": (ctypes.c_int, [_P, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P,
+                                               _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
+    "moe_mxfp4_dequantize": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is not built; run `python -m mxfp4_expert_weight_amd.build` "
+                "(there is no CPU fallback)")
+        # torch ships its own libamdhip64 (soname libamdhip64.so.7).  Importing torch
+        # first makes this library bind to that same runtime instead of loading a
+        # second HIP runtime into the process (streams would not be shared).
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/moe_mxfp4.h declares."""
+    src = open(HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(s):
+    if s is not None:
+        return s
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+    except ImportError:
+        pass
+    return None
+
+
+def _check(st: int, where: str):
+    if st != MOE_OK:
+        raise MoeError(st, where)
+
+
+def status_string(st: int) -> str:
+    return lib().moe_status_string(st).decode()
+
+
+def moe_workspace_bytes(M, top_k, E, H, I) -> int:
+    return lib().moe_workspace_bytes(M, top_k, E, H, I)
+
+
+def moe_route(x, w_router, logit_bias, bias_row_stride, M, H, E, top_k, logits, topk_ids,
+              topk_weights, stream=None):
+    _check(lib().moe_route(_ptr(x), _ptr(w_router), _ptr(logit_bias), bias_row_stride, M, H, E,
+                           top_k, _ptr(logits), _ptr(topk_ids), _ptr(topk_weights), _stream(stream)),
+           "moe_route")
+
+
+def moe_topk_softmax(logits, M, E, top_k, topk_ids, topk_weights, stream=None):
+    _check(lib().moe_topk_softmax(_ptr(logits), M, E, top_k, _ptr(topk_ids), _ptr(topk_weights),
+                                  _stream(stream)), "moe_topk_softmax")
+
+
+def moe_sort_by_expert(topk_ids, M, top_k, E, expert_offsets, sorted_pairs, active_experts,
+                       num_active, stream=None):
+    _check(lib().moe_sort_by_expert(_ptr(topk_ids), M, top_k, E, _ptr(expert_offsets),
+                                    _ptr(sorted_pairs), _ptr(active_experts), _ptr(num_active),
+                                    _stream(stream)), "moe_sort_by_expert")
+
+
+def make_weights(w13_q, w13_s, w2_q, w2_s, num_experts, hidden, inter, has_shared) -> moe_mxfp4_weights:
+    return moe_mxfp4_weights(_ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
+                             num_experts, hidden, inter, int(has_shared))
+
+
+def moe_mxfp4_forward(x, w: moe_mxfp4_weights, M, top_k, topk_weights, expert_offsets, sorted_pairs,
+                      active_experts, num_active, y, workspace, workspace_bytes, stream=None):
+    _check(lib().moe_mxfp4_forward(_ptr(x), ctypes.byref(w) if w is not None else None, M, top_k,
+                                   _ptr(topk_weights), _ptr(expert_offsets), _ptr(sorted_pairs),
+                                   _ptr(active_experts), _ptr(num_active), _ptr(y), _ptr(workspace),
+                                   workspace_bytes, _stream(stream)), "moe_mxfp4_forward")
+
+
+def moe_mxfp4_forward_timed(x, w: moe_mxfp4_weights, M, top_k, topk_weights, expert_offsets,
+                            sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes,
+                            start_event, stop_event, stream=None):
+    _check(lib().moe_mxfp4_forward_timed(_ptr(x), ctypes.byref(w) if w is not None else None, M, top_k,
+                                         _ptr(topk_weights), _ptr(expert_offsets), _ptr(sorted_pairs),
+                                         _ptr(active_experts), _ptr(num_active), _ptr(y),
+                                         _ptr(workspace), workspace_bytes, start_event, stop_event,
+                                         _stream(stream)), "moe_mxfp4_forward_timed")
+
+
+def moe_mxfp4_dequantize(q, s, rows, cols, out, stream=None):
+    _check(lib().moe_mxfp4_dequantize(_ptr(q), _ptr(s), rows, cols, _ptr(out), _stream(stream)),
+           "moe_mxfp4_dequantize")

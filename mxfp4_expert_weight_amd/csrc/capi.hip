@@ -1,0 +1,142 @@
+// C ABI of the MXFP4 MoE layer: host-side argument checks, then launches.
+// Nothing here allocates, synchronises or keeps state.
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_route_sizes(int32_t M, int32_t E, int32_t k) {
+  if (M < 1 || M > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (k < 1 || k > MOE_MAX_TOPK || k > E) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+moe_status check_hidden(int32_t H) {
+  if (H < 32 || H > MOE_MAX_HIDDEN || H % 32) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+moe_status check_inter(int32_t I) {
+  if (I < 32 || I > MOE_MAX_INTER || I % 32) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is outside the supported limits";
+    case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace is smaller than moe_workspace_bytes()";
+    case MOE_ERR_HIP: return "the HIP runtime rejected a launch";
+  }
+  return "unknown status";
+}
+
+size_t moe_workspace_bytes(int32_t M, int32_t top_k, int32_t E, int32_t H, int32_t I) {
+  if (check_route_sizes(M, E, top_k) != MOE_OK || check_hidden(H) != MOE_OK ||
+      check_inter(I) != MOE_OK)
+    return 0;
+  return workspace_bytes(M, top_k, I);
+}
+
+moe_status moe_route(const uint16_t* x, const float* w_router, const float* logit_bias,
+                     int64_t bias_row_stride, int32_t M, int32_t H, int32_t E, int32_t top_k,
+                     float* logits, int32_t* topk_ids, float* topk_weights, void* stream) {
+  if (!x || !w_router || !logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  moe_status st = check_route_sizes(M, E, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_hidden(H)) != MOE_OK) return st;
+  if (logit_bias && bias_row_stride != 0 && bias_row_stride != E) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_router_logits(x, w_router, logit_bias, logit_bias ? bias_row_stride : 0, M, H,
+                                      E, logits, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_topk_softmax(logits, M, E, top_k, topk_ids, topk_weights, s));
+}
+
+moe_status moe_topk_softmax(const float* logits, int32_t M, int32_t E, int32_t top_k,
+                            int32_t* topk_ids, float* topk_weights, void* stream) {
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  moe_status st = check_route_sizes(M, E, top_k);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_topk_softmax(logits, M, E, top_k, topk_ids, topk_weights, (hipStream_t)stream));
+}
+
+moe_status moe_sort_by_expert(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_t E,
+                              int32_t* expert_offsets, int32_t* sorted_pairs,
+                              int32_t* active_experts, int32_t* num_active, void* stream) {
+  if (!topk_ids || !expert_offsets || !sorted_pairs || !active_experts || !num_active)
+    return MOE_ERR_NULL;
+  moe_status st = check_route_sizes(M, E, top_k);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_sort_by_expert(topk_ids, M * top_k, E, expert_offsets, sorted_pairs,
+                                          active_experts, num_active, (hipStream_t)stream));
+}
+
+moe_status moe_mxfp4_forward_timed(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
+                                   int32_t top_k, const float* topk_weights,
+                                   const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                                   const int32_t* active_experts, const int32_t* num_active, float* y,
+                                   void* workspace, size_t workspace_bytes_, void* start_event,
+                                   void* stop_event, void* stream) {
+  if (!x || !w || !topk_weights || !expert_offsets || !sorted_pairs || !active_experts ||
+      !num_active || !y || !workspace)
+    return MOE_ERR_NULL;
+  if (!w->w13_q || !w->w13_s || !w->w2_q || !w->w2_s) return MOE_ERR_NULL;
+  moe_status st = check_route_sizes(M, w->num_experts, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_hidden(w->hidden)) != MOE_OK) return st;
+  if ((st = check_inter(w->inter)) != MOE_OK) return st;
+  if (w->has_shared != 0 && w->has_shared != 1) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w->w13_q) || !aligned16(w->w13_s) || !aligned16(w->w2_q) ||
+      !aligned16(w->w2_s) || ((uintptr_t)workspace & 255u))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes_ < workspace_bytes(M, top_k, w->inter)) return MOE_ERR_WORKSPACE;
+
+  ForwardArgs a;
+  a.x = x;
+  a.w13_q = w->w13_q; a.w13_s = w->w13_s; a.w2_q = w->w2_q; a.w2_s = w->w2_s;
+  a.topk_weights = topk_weights;
+  a.offsets = expert_offsets; a.sorted_pairs = sorted_pairs;
+  a.active = active_experts; a.num_active = num_active;
+  a.y = y;
+  a.hdr = reinterpret_cast<WorkspaceHeader*>(workspace);
+  a.h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + workspace_h_offset());
+  a.M = M; a.k = top_k; a.E = w->num_experts; a.H = w->hidden; a.I = w->inter;
+  a.has_shared = w->has_shared;
+  return hip_status(launch_forward(a, (hipStream_t)stream, (hipEvent_t)start_event,
+                                   (hipEvent_t)stop_event));
+}
+
+moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                             const float* topk_weights, const int32_t* expert_offsets,
+                             const int32_t* sorted_pairs, const int32_t* active_experts,
+                             const int32_t* num_active, float* y, void* workspace,
+                             size_t workspace_bytes_, void* stream) {
+  return moe_mxfp4_forward_timed(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs,
+                                 active_experts, num_active, y, workspace, workspace_bytes_, nullptr,
+                                 nullptr, stream);
+}
+
+moe_status moe_mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
+                                float* out, void* stream) {
+  if (!q || !s || !out) return MOE_ERR_NULL;
+  if (rows < 1 || cols < 32 || cols % 32 || rows * cols >= (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  if ((rows * (cols / 8) + 255) / 256 > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+  if (!aligned16(q) || ((uintptr_t)out & 15u)) return MOE_ERR_ALIGN;
+  return hip_status(launch_dequant(q, s, rows, cols, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

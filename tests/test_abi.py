@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host with the documented
+status before anything is enqueued.  Only invalid calls are made here (fake,
+never-dereferenced addresses), so no kernel is launched."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from mxfp4_expert_weight_amd import binding as B
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from mxfp4_expert_weight_amd import build
+        build.build(verbose=False)
+    return B.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = B.header_functions()
+    assert set(names) >= {"moe_route", "moe_sort_by_expert", "moe_mxfp4_forward",
+                          "moe_mxfp4_dequantize", "moe_topk_softmax", "moe_workspace_bytes",
+                          "moe_status_string"}
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for st in range(6):
+        assert B.status_string(st)
+    assert B.status_string(0) == "ok"
+
+
+def test_workspace_bytes(lib):
+    ws = B.moe_workspace_bytes(1, 8, 512, 2560, 768)
+    assert ws >= 256 + (8 + 1) * 768 * 2 and ws % 256 == 0
+    assert B.moe_workspace_bytes(512, 8, 512, 2560, 768) > ws
+    assert B.moe_workspace_bytes(1, 8, 512, 2561, 768) == 0        # H % 32
+    assert B.moe_workspace_bytes(1, 9, 8, 256, 128) == 0           # k > E
+    assert B.moe_workspace_bytes(0, 8, 512, 2560, 768) == 0        # M < 1
+    assert B.moe_workspace_bytes(1, 8, 2048, 2560, 768) == 0       # E > limit
+
+
+A = 0x100000        # 16-byte-aligned fake addresses: only reached on invalid calls
+MIS = 0x100008      # 8-byte aligned, not 16
+
+
+def _status(fn, *args):
+    with pytest.raises(B.MoeError) as ei:
+        fn(*args)
+    return ei.value.status
+
+
+def test_route_host_checks(lib):
+    r = B.moe_route
+    assert _status(r, None, A, None, 0, 1, 2560, 512, 8, A, A, A, 0) == B.MOE_ERR_NULL
+    assert _status(r, A, A, None, 0, 0, 2560, 512, 8, A, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(r, A, A, None, 0, 1, 2559, 512, 8, A, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(r, A, A, None, 0, 1, 2560, 512, 0, A, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(r, A, A, None, 0, 1, 2560, 4, 8, A, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(r, A, A, None, 0, 1, 2560, 512, 33, A, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(r, A, A, A, 7, 1, 2560, 512, 8, A, A, A, 0) == B.MOE_ERR_SHAPE   # bias stride
+    assert _status(r, MIS, A, None, 0, 1, 2560, 512, 8, A, A, A, 0) == B.MOE_ERR_ALIGN
+    assert _status(r, A, MIS, None, 0, 1, 2560, 512, 8, A, A, A, 0) == B.MOE_ERR_ALIGN
+
+
+def test_topk_and_sort_host_checks(lib):
+    assert _status(B.moe_topk_softmax, None, 1, 512, 8, A, A, 0) == B.MOE_ERR_NULL
+    assert _status(B.moe_topk_softmax, A, 1, 1025, 8, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(B.moe_topk_softmax, A, 70000, 512, 8, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(B.moe_sort_by_expert, A, 1, 8, 512, A, A, A, None, 0) == B.MOE_ERR_NULL
+    assert _status(B.moe_sort_by_expert, A, 1, 0, 512, A, A, A, A, 0) == B.MOE_ERR_SHAPE
+
+
+def test_forward_host_checks(lib):
+    w = B.make_weights(A, A, A, A, 512, 2560, 768, 1)
+    ws = B.moe_workspace_bytes(4, 8, 512, 2560, 768)
+    f = B.moe_mxfp4_forward
+    args = [A, w, 4, 8, A, A, A, A, A, A, A, ws, 0]
+    assert _status(f, *([None] + args[1:])) == B.MOE_ERR_NULL
+    assert _status(f, *(args[:1] + [None] + args[2:])) == B.MOE_ERR_NULL
+    bad = B.make_weights(A, None, A, A, 512, 2560, 768, 1)
+    assert _status(f, *(args[:1] + [bad] + args[2:])) == B.MOE_ERR_NULL
+    for shape in [(512, 2560, 700, 1), (512, 2560, 768, 2), (512, 0, 768, 1), (0, 2560, 768, 1)]:
+        bw = B.make_weights(A, A, A, A, *shape)
+        assert _status(f, *(args[:1] + [bw] + args[2:])) == B.MOE_ERR_SHAPE, shape
+    mis = B.make_weights(A, A, MIS, A, 512, 2560, 768, 1)
+    assert _status(f, *(args[:1] + [mis] + args[2:])) == B.MOE_ERR_ALIGN
+    assert _status(f, *(args[:10] + [A + 16, ws, 0])) == B.MOE_ERR_ALIGN      # workspace 256-aligned
+    assert _status(f, *(args[:11] + [ws - 1, 0])) == B.MOE_ERR_WORKSPACE
+
+
+def test_dequant_host_checks(lib):
+    d = B.moe_mxfp4_dequantize
+    assert _status(d, None, A, 4, 64, A, 0) == B.MOE_ERR_NULL
+    assert _status(d, A, A, 4, 48, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(d, A, A, 0, 64, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(d, MIS, A, 4, 64, A, 0) == B.MOE_ERR_ALIGN
+
+
+def test_library_has_no_oracle_or_fallback():
+    """The product path never routes through the oracle or a CPU fallback."""
+    pkg = os.path.dirname(B.__file__)
+    for root, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(root, fn)).read()
+                assert "import oracle" not in src and "from oracle" not in src, fn

@@ -1,0 +1,124 @@
+"""GPU parity of the integer and exact steps, element by element against the
+oracle: MXFP4 dequantisation (bit-exact), top-k ids (exact) with their
+weights, and the stable sort by expert (exact)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import U, need_gpu, say
+from mxfp4_expert_weight_amd import binding as B, synth
+from mxfp4_expert_weight_amd.layer import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- dequant --
+
+def _dequant_gpu(torch, q, s):
+    rows, cols = q.shape[0], q.shape[1] * 2
+    dq, ds = to_device(q), to_device(s)
+    out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+    B.moe_mxfp4_dequantize(dq, ds, rows, cols, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_dequant_exhaustive_bit_exact():
+    torch = need_gpu()
+    # row r uses scale byte 2 + r for every block; each row holds all 256 code bytes
+    scales = np.arange(2, 253, dtype=np.uint8)
+    q = np.tile(np.arange(256, dtype=np.uint8), (scales.size, 1))
+    s = np.repeat(scales[:, None], 512 // 32, axis=1)
+    say("dequant exhaustive 16 codes x 2 nibbles x scales 2..252")
+    got = _dequant_gpu(torch, q, s)
+    ref = oracle.dequant_mxfp4(q, s)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)   # representable
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("shape", [(1536, 2560), (2560, 768), (3, 32), (7, 96)])
+def test_dequant_random_expert_shapes(shape):
+    torch = need_gpu()
+    rng = np.random.default_rng(shape[0])
+    q = synth.random_bytes(rng, (shape[0], shape[1] // 2))
+    s = synth.random_scales(rng, (shape[0], shape[1] // 32))
+    say(f"dequant random {shape}")
+    got = _dequant_gpu(torch, q, s)
+    assert np.array_equal(got.astype(np.float64), oracle.dequant_mxfp4(q, s))
+
+
+# ---------------------------------------------------------------- top-k --
+
+def _topk_gpu(torch, logits, k):
+    M, E = logits.shape
+    dl = to_device(logits.astype(np.float32))
+    ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, k), dtype=torch.float32, device="cuda")
+    B.moe_topk_softmax(dl, M, E, k, ids, w)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("E,k,M,kind", [
+    (16, 2, 64, "ties"), (512, 8, 300, "normal"), (512, 8, 200, "ties"), (1024, 32, 50, "ties"),
+    (100, 7, 33, "normal"), (1, 1, 5, "normal"), (64, 64, 3, "ties"), (1000, 1, 17, "signed_zero"),
+    (512, 8, 4096, "normal"),
+])
+def test_topk_softmax_exact_ids(E, k, M, kind):
+    torch = need_gpu()
+    rng = np.random.default_rng(E * 1000 + k)
+    if kind == "ties":
+        logits = rng.integers(-4, 5, size=(M, E)).astype(np.float32) * np.float32(0.5)
+    elif kind == "signed_zero":
+        logits = np.where(rng.random((M, E)) < 0.5, np.float32(0.0), np.float32(-0.0))
+        logits[:, 7] = -1.0
+    else:
+        logits = rng.standard_normal((M, E)).astype(np.float32) * np.float32(3.0)
+    say(f"topk E={E} k={k} M={M} {kind}")
+    ids, w = _topk_gpu(torch, logits, k)
+    # the decision is taken on the very same fp32 values on both sides
+    ref_ids, ref_w = oracle.topk_softmax(logits.astype(np.float64), k)
+    assert np.array_equal(ids, ref_ids)
+    spread = float(np.max(np.ptp(np.take_along_axis(logits, ref_ids.astype(np.int64), 1), axis=1)))
+    assert np.max(np.abs(w - ref_w)) <= (spread + k + 8) * 2 * U
+
+
+# ---------------------------------------------------------------- sort --
+
+def _sort_gpu(torch, ids, E):
+    M, k = ids.shape
+    di = to_device(ids.astype(np.int32))
+    off = torch.empty((E + 1,), dtype=torch.int32, device="cuda")
+    pairs = torch.empty((M * k,), dtype=torch.int32, device="cuda")
+    act = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    na = torch.empty((1,), dtype=torch.int32, device="cuda")
+    B.moe_sort_by_expert(di, M, k, E, off, pairs, act, na)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), pairs.cpu().numpy(), act.cpu().numpy(), int(na.item())
+
+
+@pytest.mark.parametrize("M,k,E,dist", [
+    (1, 8, 512, "uniform"), (4, 8, 512, "overlap"), (32, 8, 512, "zipf"), (512, 8, 512, "uniform"),
+    (1, 1, 1, "uniform"), (777, 3, 1000, "uniform"), (64, 4, 16, "uniform"), (100, 32, 1024, "uniform"),
+    (4096, 8, 512, "zipf"), (65536, 1, 7, "uniform"),
+])
+def test_sort_by_expert_exact(M, k, E, dist):
+    torch = need_gpu()
+    rng = np.random.default_rng(M * 31 + k)
+    if dist == "zipf":
+        p = np.arange(1, E + 1) ** -1.1
+        p /= p.sum()
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(M)])
+    elif dist == "overlap":
+        pool = rng.choice(E, size=12, replace=False)
+        ids = np.stack([rng.choice(pool, size=k, replace=False) for _ in range(M)])
+    else:
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(M)])
+    say(f"sort M={M} k={k} E={E} {dist}")
+    off, pairs, act, D = _sort_gpu(torch, ids, E)
+    r_off, r_pairs, r_act, r_D = oracle.sort_by_expert(ids, E)
+    assert D == r_D
+    assert np.array_equal(off, r_off)
+    assert np.array_equal(pairs, r_pairs)
+    assert np.array_equal(act[:D], r_act)
+    assert np.all(act[D:] == -7)          # entries past D are left untouched

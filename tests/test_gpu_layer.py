@@ -1,0 +1,130 @@
+"""GPU parity of the whole layer (route -> sort -> forward through the C ABI,
+the launch sequence bench.py times) against the float64 oracle.
+
+Output bar: |gpu - ref| <= 1e-2 (|ref| + rms(ref)) per element.  Routing: ids
+exact except where the oracle's order is decided by less than the fp32 error
+bound (then validity is checked and that token's output is left out, since
+another expert set is an equally correct fp32 routing)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import assert_layer_close, check_routing, logit_error_bound, need_gpu, say
+from mxfp4_expert_weight_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(torch, ls):
+    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer
+    wl = ls.wl
+    d = DeviceLayerSet.from_host(ls)
+    b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
+    run_layer(d, b)
+    torch.cuda.synchronize()
+    out = dict(y=b.y.cpu().numpy(), ids=b.ids.cpu().numpy(), w=b.weights.cpu().numpy(),
+               logits=b.logits.cpu().numpy(), hdr=b.header(),
+               num_active=int(b.num_active.item()))
+    return out, d, b
+
+
+def _check_full(torch, ls, what):
+    wl = ls.wl
+    say(f"layer {what}: M={wl.M} H={wl.H} I={wl.I} E={wl.E} k={wl.k} shared={wl.shared} {wl.routing}")
+    g, _, _ = _run(torch, ls)
+    r = oracle.moe_layer(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s,
+                         wl.k, wl.shared)
+    xf = oracle.bf16_bits_to_f64(ls.x_bits)
+    bound = logit_error_bound(xf, ls.w_router, ls.bias, wl.H)
+    amb = check_routing(g["ids"], g["w"], g["logits"], r["logits"], bound, wl.k, what)
+    keep = np.setdiff1d(np.arange(wl.M), amb)
+    rms = float(np.sqrt(np.mean(r["y"] ** 2)))
+    assert_layer_close(g["y"][keep], r["y"][keep], rms, what)
+    if not amb:
+        assert g["num_active"] == r["num_active"]
+        assert g["hdr"]["gemv_experts"] == r["num_active"] + int(wl.shared)
+    assert len(amb) <= max(1, wl.M // 50), f"{what}: {len(amb)} ambiguous tokens"
+    return g, r
+
+
+def test_tiny_config_every_element():
+    torch = need_gpu()
+    _check_full(torch, synth.layer_set("tiny"), "tiny")
+
+
+@pytest.mark.parametrize("M,H,I,E,k,shared,routing", [
+    (7, 96, 64, 5, 3, True, "plain"),        # ragged: lanes idle in both GEMVs, M*k > E
+    (3, 2592, 800, 9, 2, True, "plain"),     # K tails: a second K pass in gate/up and down
+    (1, 32, 32, 1, 1, False, "plain"),       # smallest layer, no shared expert
+    (5, 256, 128, 6, 6, False, "overlap"),   # k = E: every expert active
+    (64, 128, 96, 16, 4, True, "zipf"),      # many tokens per expert
+    (2, 8192, 64, 3, 2, True, "plain"),      # largest hidden size
+    (2, 64, 4096, 3, 1, True, "plain"),      # largest intermediate size
+])
+def test_edge_shapes_every_element(M, H, I, E, k, shared, routing):
+    torch = need_gpu()
+    wl = synth.custom(f"edge{M}x{H}x{I}", M, H, I, E, k, shared, routing, seed=M + H + I)
+    _check_full(torch, synth.layer_set(wl), wl.name)
+
+
+@pytest.mark.parametrize("name,sets", [("ling_m1", [0, 17]), ("ling_m4_mtp", [0, 39])])
+def test_ling_decode_full_size(name, sets):
+    torch = need_gpu()
+    for l in sets:
+        _check_full(torch, synth.layer_set(name, l), f"{name}/set{l}")
+
+
+@pytest.mark.parametrize("name,tokens", [("ling_m32_zipf", [0, 5, 17, 31]),
+                                         ("ling_m512_prefill", [0, 101, 333, 511])])
+def test_ling_batch_sampled_tokens(name, tokens):
+    """Full-size batch on the GPU; the oracle recomputes sampled tokens one by
+    one (tokens do not interact).  rms(ref) is estimated on the sample."""
+    torch = need_gpu()
+    ls = synth.layer_set(name, 0)
+    wl = ls.wl
+    say(f"layer {name}: M={wl.M} sampled {tokens}")
+    g, _, _ = _run(torch, ls)
+    r = oracle.moe_layer_tokens(tokens, ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s,
+                                ls.w2_q, ls.w2_s, wl.k, wl.shared)
+    xf = oracle.bf16_bits_to_f64(ls.x_bits[tokens])
+    b = ls.bias if ls.bias is None or ls.bias.ndim == 1 else ls.bias[tokens]
+    bound = logit_error_bound(xf, ls.w_router, b, wl.H)
+    amb = check_routing(g["ids"][tokens], g["w"][tokens], g["logits"][tokens], r["logits"], bound,
+                        wl.k, name)
+    keep = [i for i in range(len(tokens)) if i not in amb]
+    rms = float(np.sqrt(np.mean(r["y"] ** 2)))
+    assert_layer_close(g["y"][tokens][keep], r["y"][keep], rms, name)
+    # every token's output is finite and the dedup covers every routed pair
+    assert np.all(np.isfinite(g["y"]))
+    D = len(np.unique(g["ids"]))
+    assert g["num_active"] == D and g["hdr"]["gemv_experts"] == D + 1
+
+
+def test_token_independence_m4_vs_m1():
+    """y_t of a 4-token batch equals y_t of token t run alone (dedup changes nothing)."""
+    torch = need_gpu()
+    ls = synth.layer_set("ling_m4_mtp", 3)
+    say("token independence ling_m4_mtp/set3")
+    g4, _, _ = _run(torch, ls)
+    for t in range(4):
+        wl1 = synth.Workload("one", 1, ls.wl.H, ls.wl.I, ls.wl.E, ls.wl.k, True, "overlap", 1, 0)
+        one = synth.LayerSet(wl1, ls.x_bits[t:t + 1], ls.w_router, ls.bias[t:t + 1], ls.w13_q,
+                             ls.w13_s, ls.w2_q, ls.w2_s)
+        g1, _, _ = _run(torch, one)
+        assert np.array_equal(g1["ids"][0], g4["ids"][t])
+        rms = float(np.sqrt(np.mean(g4["y"] ** 2)))
+        assert np.all(np.abs(g1["y"][0] - g4["y"][t]) <= 1e-5 * (np.abs(g4["y"][t]) + rms))
+
+
+def test_down_scale_doubling_doubles_output():
+    """+1 on every down-projection scale byte doubles y (power-of-two scaling
+    commutes with fp32 rounding; only the order of the atomic adds differs)."""
+    torch = need_gpu()
+    ls = synth.layer_set("ling_m4_mtp", 5)
+    say("scale doubling ling_m4_mtp/set5")
+    g, _, _ = _run(torch, ls)
+    ls2 = synth.LayerSet(ls.wl, ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q,
+                         ls.w2_s + np.uint8(1))
+    g2, _, _ = _run(torch, ls2)
+    rms = float(np.sqrt(np.mean(g["y"] ** 2)))
+    assert np.all(np.abs(g2["y"] - 2 * g["y"]) <= 1e-5 * (np.abs(2 * g["y"]) + 2 * rms))
