@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the MXFP4 MoE decode layer on one MI355X.
 
-A step is one whole layer -- moe_route, moe_sort_by_expert, moe_mxfp4_forward
-(router GEMV + top-k, the sort by expert, every active expert's fused dequant
-GEMVs and the weighted combine plus the shared expert) -- on the next of
+A step is one whole layer -- one moe_layer call (router GEMV + top-k, the sort
+by expert, every active expert's fused dequant GEMVs and the weighted combine
+plus the shared expert; --three-calls times moe_route, moe_sort_by_expert and
+moe_mxfp4_forward instead) -- on the next of
 `--sets` distinct layer weight sets, so consecutive steps never reuse expert
 weights and the 256 MB Infinity Cache cannot serve them.  Steps are replayed
 from a HIP graph of one pass over all sets; inputs are resident in HBM before
@@ -12,9 +13,9 @@ the timed region starts.
 Prints one JSON line:
   value        layer GB/s: algorithmic bytes of a layer / time per layer
   ms_per_step  time per layer
-  roofline     the forward's kernels (expert weights, the dominant bytes):
-               expert bytes per launch / mean launch span, measured with HIP
-               events that take the kernels' own begin/end timestamps
+  roofline     the dominant kernel (gate/up: two thirds of the expert bytes):
+               its weight bytes per launch / mean launch duration, from HIP
+               events bound to that kernel's own begin/end timestamps
   cpu_baseline the float64 oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -40,6 +41,10 @@ def log(*a):
 
 def expert_bytes_per_expert(H, I):
     return 2 * I * (H // 2 + H // 32) + H * (I // 2 + I // 32)
+
+
+def gateup_bytes_per_expert(H, I):
+    return 2 * I * (H // 2 + H // 32)
 
 
 def layer_bytes(wl, D):
@@ -149,6 +154,8 @@ def main():
     ap.add_argument("--workload", default="ling_m1")
     ap.add_argument("--sets", type=int, default=None, help="layer sets rotated (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--three-calls", action="store_true",
+                    help="time moe_route + moe_sort_by_expert + moe_mxfp4_forward instead of moe_layer")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (reference for rocprof byte counters)")
     args = ap.parse_args()
@@ -196,11 +203,11 @@ def main():
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for i in range(n):
-                run_layer(sets[i % nsets], buf, weights[i % nsets])
+                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls)
         torch.cuda.current_stream().wait_stream(s)
         with torch.cuda.graph(g):
             for i in range(n):
-                run_layer(sets[i % nsets], buf, weights[i % nsets])
+                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls)
         return g
 
     g_full = capture(nsets)
@@ -232,8 +239,9 @@ def main():
     log(f"[bench] {args.steps} steps in {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms): "
         f"{ms_per_step * 1e3:.2f} us/layer, {layer_gbs:.0f} GB/s")
 
-    # Roofline of the forward's kernels: per-launch spans from HIP events bound to
-    # the kernels' own begin/end timestamps, over the same K steps (eager).
+    # Roofline of the dominant kernel (gate/up: 2/3 of the expert bytes): per-launch
+    # durations from HIP events bound to that kernel's own begin/end timestamps,
+    # over the same K steps run eagerly on the stream the kernels use.
     hev = HipEvents()
     n_ev = min(args.steps, 4000)
     starts = [hev.create() for _ in range(n_ev)]
@@ -242,22 +250,19 @@ def main():
     torch.cuda.synchronize()
     for i in range(n_ev):
         d, w = sets[step_sets[i]], weights[step_sets[i]]
-        binding.moe_route(d.x, d.w_router, d.bias, d.bias_row_stride, d.M, d.H, d.E, d.k, buf.logits,
-                          buf.ids, buf.weights, stream)
-        binding.moe_sort_by_expert(buf.ids, d.M, d.k, d.E, buf.offsets, buf.pairs, buf.active,
-                                   buf.num_active, stream)
-        binding.moe_mxfp4_forward_timed(d.x, w, d.M, d.k, buf.weights, buf.offsets, buf.pairs, buf.active,
-                                        buf.num_active, buf.y, buf.ws, buf.ws_bytes, starts[i], stops[i],
-                                        stream)
+        binding.moe_layer_timed(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits,
+                                buf.ids, buf.weights, buf.offsets, buf.pairs, buf.active, buf.num_active,
+                                buf.y, buf.ws, buf.ws_bytes, starts[i], stops[i], stream)
     torch.cuda.synchronize()
     spans = [hev.elapsed_ms(starts[i], stops[i]) for i in range(n_ev)]
     for e in starts + stops:
         hev.destroy(e)
-    fwd_ms = sum(spans) / n_ev
-    fwd_bytes = sum(exp_b[:n_ev]) / n_ev
-    achieved = fwd_bytes / (fwd_ms * 1e-3) / 1e9
-    log(f"[bench] forward kernels: {fwd_ms * 1e3:.2f} us per launch, {fwd_bytes / 1e6:.2f} MB expert "
-        f"weights, {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+    gu_ms = sum(spans) / n_ev
+    gu_bytes = sum((D[step_sets[i]] + int(wl.shared)) * gateup_bytes_per_expert(wl.H, wl.I)
+                   for i in range(n_ev)) / n_ev
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    log(f"[bench] gate/up kernel: {gu_ms * 1e3:.2f} us per launch, {gu_bytes / 1e6:.2f} MB, "
+        f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
     out = {
         "metric": METRIC,
@@ -272,7 +277,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "M": wl.M, "hidden": wl.H, "inter": wl.I, "experts": wl.E,
+        "config": {"workload": wl.name, "entry": "three calls" if args.three_calls else "moe_layer", "M": wl.M, "hidden": wl.H, "inter": wl.I, "experts": wl.E,
                    "top_k": wl.k, "shared_expert": wl.shared, "routing": wl.routing,
                    "layer_sets_rotated": nsets, "weights": "MXFP4 (E2M1 + E8M0/32)",
                    "activations": "bf16"},
@@ -280,10 +285,10 @@ def main():
         "layer_bytes": sum(lay_b) / len(lay_b),
         "layer_frac_of_hbm_peak": layer_gbs / HBM_PEAK_GBS,
         "mean_distinct_experts": sum(D[l] for l in step_sets) / len(step_sets),
-        "roofline": {"bound": "hbm", "kernel": "moe_mxfp4_forward (gateup_kernel + down_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "gateup_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "us_per_launch": fwd_ms * 1e3, "bytes_per_launch": fwd_bytes},
+                     "us_per_launch": gu_ms * 1e3, "bytes_per_launch": gu_bytes},
     }
     if not args.no_cpu_baseline:
         del sets

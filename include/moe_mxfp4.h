@@ -138,17 +138,32 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int3
                              const int32_t* num_active, float* y, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* moe_mxfp4_forward, plus timing: `start_event` / `stop_event` (hipEvent_t, may be
- * NULL) take the begin timestamp of the forward's first kernel and the end
- * timestamp of its last kernel (hipExtLaunchKernelGGL), so hipEventElapsedTime
- * gives the kernels' own execution span without queueing gaps before it.
- * For measurement; results are those of moe_mxfp4_forward. */
-moe_status moe_mxfp4_forward_timed(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
-                                   int32_t top_k, const float* topk_weights,
-                                   const int32_t* expert_offsets, const int32_t* sorted_pairs,
-                                   const int32_t* active_experts, const int32_t* num_active, float* y,
-                                   void* workspace, size_t workspace_bytes, void* start_event,
-                                   void* stop_event, void* stream);
+/* The whole layer in one call: moe_route, moe_sort_by_expert and
+ * moe_mxfp4_forward with the same arguments and outputs, fused into fewer
+ * launches.  For M <= 4 (decode, speculative verify) there are three: the
+ * router logits, then a gate/up kernel each of whose workgroups takes the
+ * top-k and the expert sort itself from the logits, then down.  For M <= 8 the
+ * top-k and the sort share one workgroup; above, they are separate launches.
+ * Every intermediate output (logits, ids, weights, sort outputs) is still
+ * written, with the values the separate calls give.
+ * Limits: those of the three calls; x, w_router and the bank 16-byte aligned,
+ * workspace 256-byte aligned. */
+moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logit_bias,
+                     int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                     float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                     int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_layer, plus timing of its dominant kernel: `start_event` / `stop_event`
+ * (hipEvent_t, may be NULL) take the begin and end timestamps of the gate/up
+ * kernel (hipExtLaunchKernelGGL; for M <= 4 it includes the in-block routing),
+ * so hipEventElapsedTime gives that kernel's own execution time.  For measurement; results are those of moe_layer. */
+moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float* logit_bias,
+                           int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                           void* workspace, size_t workspace_bytes, void* start_event, void* stop_event,
+                           void* stream);
 
 /* Dequantise an MXFP4 tensor [rows][cols] (layout above) to fp32 with the same
  * device routine the expert kernels use (exposes it for exact checks).

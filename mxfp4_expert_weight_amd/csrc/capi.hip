@@ -47,7 +47,7 @@ size_t moe_workspace_bytes(int32_t M, int32_t top_k, int32_t E, int32_t H, int32
   if (check_route_sizes(M, E, top_k) != MOE_OK || check_hidden(H) != MOE_OK ||
       check_inter(I) != MOE_OK)
     return 0;
-  return workspace_bytes(M, top_k, I);
+  return workspace_bytes(M, top_k, E, I);
 }
 
 moe_status moe_route(const uint16_t* x, const float* w_router, const float* logit_bias,
@@ -85,12 +85,11 @@ moe_status moe_sort_by_expert(const int32_t* topk_ids, int32_t M, int32_t top_k,
                                           active_experts, num_active, (hipStream_t)stream));
 }
 
-moe_status moe_mxfp4_forward_timed(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
-                                   int32_t top_k, const float* topk_weights,
-                                   const int32_t* expert_offsets, const int32_t* sorted_pairs,
-                                   const int32_t* active_experts, const int32_t* num_active, float* y,
-                                   void* workspace, size_t workspace_bytes_, void* start_event,
-                                   void* stop_event, void* stream) {
+moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                             const float* topk_weights, const int32_t* expert_offsets,
+                             const int32_t* sorted_pairs, const int32_t* active_experts,
+                             const int32_t* num_active, float* y, void* workspace,
+                             size_t workspace_bytes_, void* stream) {
   if (!x || !w || !topk_weights || !expert_offsets || !sorted_pairs || !active_experts ||
       !num_active || !y || !workspace)
     return MOE_ERR_NULL;
@@ -103,7 +102,7 @@ moe_status moe_mxfp4_forward_timed(const uint16_t* x, const moe_mxfp4_weights* w
   if (!aligned16(x) || !aligned16(w->w13_q) || !aligned16(w->w13_s) || !aligned16(w->w2_q) ||
       !aligned16(w->w2_s) || ((uintptr_t)workspace & 255u))
     return MOE_ERR_ALIGN;
-  if (workspace_bytes_ < workspace_bytes(M, top_k, w->inter)) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes_ < workspace_bytes(M, top_k, w->num_experts, w->inter)) return MOE_ERR_WORKSPACE;
 
   ForwardArgs a;
   a.x = x;
@@ -113,21 +112,95 @@ moe_status moe_mxfp4_forward_timed(const uint16_t* x, const moe_mxfp4_weights* w
   a.active = active_experts; a.num_active = num_active;
   a.y = y;
   a.hdr = reinterpret_cast<WorkspaceHeader*>(workspace);
-  a.h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) + workspace_h_offset());
+  a.h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) +
+                                    workspace_h_offset(M, top_k, w->num_experts));
+  a.rec = nullptr;
   a.M = M; a.k = top_k; a.E = w->num_experts; a.H = w->hidden; a.I = w->inter;
   a.has_shared = w->has_shared;
-  return hip_status(launch_forward(a, (hipStream_t)stream, (hipEvent_t)start_event,
-                                   (hipEvent_t)stop_event));
+  return hip_status(launch_forward(a, (hipStream_t)stream));
 }
 
-moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
-                             const float* topk_weights, const int32_t* expert_offsets,
-                             const int32_t* sorted_pairs, const int32_t* active_experts,
-                             const int32_t* num_active, float* y, void* workspace,
-                             size_t workspace_bytes_, void* stream) {
-  return moe_mxfp4_forward_timed(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs,
-                                 active_experts, num_active, y, workspace, workspace_bytes_, nullptr,
-                                 nullptr, stream);
+namespace {
+
+ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                       const float* topk_weights, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                       const int32_t* active_experts, const int32_t* num_active, float* y, void* workspace) {
+  ForwardArgs a;
+  a.x = x;
+  a.w13_q = w->w13_q; a.w13_s = w->w13_s; a.w2_q = w->w2_q; a.w2_s = w->w2_s;
+  a.topk_weights = topk_weights;
+  a.offsets = expert_offsets; a.sorted_pairs = sorted_pairs;
+  a.active = active_experts; a.num_active = num_active;
+  a.y = y;
+  a.hdr = reinterpret_cast<WorkspaceHeader*>(workspace);
+  a.rec = reinterpret_cast<const SlotRec*>(reinterpret_cast<char*>(workspace) + workspace_rec_offset());
+  a.h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) +
+                                    workspace_h_offset(M, top_k, w->num_experts));
+  a.M = M; a.k = top_k; a.E = w->num_experts; a.H = w->hidden; a.I = w->inter;
+  a.has_shared = w->has_shared;
+  return a;
+}
+
+}  // namespace
+
+moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float* logit_bias,
+                           int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                           void* workspace, size_t workspace_bytes_, void* start_event, void* stop_event,
+                           void* stream) {
+  if (!x || !w_router || !w || !logits || !topk_ids || !topk_weights || !expert_offsets ||
+      !sorted_pairs || !active_experts || !num_active || !y || !workspace)
+    return MOE_ERR_NULL;
+  if (!w->w13_q || !w->w13_s || !w->w2_q || !w->w2_s) return MOE_ERR_NULL;
+  const int32_t E = w->num_experts, H = w->hidden;
+  moe_status st = check_route_sizes(M, E, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_hidden(H)) != MOE_OK) return st;
+  if ((st = check_inter(w->inter)) != MOE_OK) return st;
+  if (w->has_shared != 0 && w->has_shared != 1) return MOE_ERR_SHAPE;
+  if (logit_bias && bias_row_stride != 0 && bias_row_stride != E) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w->w13_q) || !aligned16(w->w13_s) ||
+      !aligned16(w->w2_q) || !aligned16(w->w2_s) || ((uintptr_t)workspace & 255u))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes_ < workspace_bytes(M, top_k, w->num_experts, w->inter)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_router_logits(x, w_router, logit_bias, logit_bias ? bias_row_stride : 0, M, H, E, logits,
+                           s) != hipSuccess)
+    return MOE_ERR_HIP;
+  ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
+                             num_active, y, workspace);
+  SlotRec* rec = reinterpret_cast<SlotRec*>(reinterpret_cast<char*>(workspace) + workspace_rec_offset());
+  hipEvent_t start = (hipEvent_t)start_event, stop = (hipEvent_t)stop_event;
+  if (M <= kRoutedMaxTokens) {
+    // decode: every gate/up block routes itself from the logits
+    const RouteOut r{logits, topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts,
+                     num_active, rec, expert_bits(E)};
+    return hip_status(launch_forward_routed(a, r, s, start, stop));
+  }
+  const RecOut ro{rec, topk_weights, M, top_k, w->has_shared};
+  hipError_t e;
+  if (topk_sort_fits_one_block(M)) {
+    e = launch_topk_sort_small(logits, M, E, top_k, topk_ids, topk_weights, expert_offsets,
+                               sorted_pairs, active_experts, num_active, s, ro);
+  } else {
+    e = launch_topk_softmax(logits, M, E, top_k, topk_ids, topk_weights, s);
+    if (e == hipSuccess)
+      e = launch_sort_by_expert(topk_ids, M * top_k, E, expert_offsets, sorted_pairs, active_experts,
+                                num_active, s, ro);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_forward(a, s, start, stop));
+}
+
+moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logit_bias,
+                     int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                     float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                     int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                     void* workspace, size_t workspace_bytes_, void* stream) {
+  return moe_layer_timed(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids,
+                         topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
+                         workspace, workspace_bytes_, nullptr, nullptr, stream);
 }
 
 moe_status moe_mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,

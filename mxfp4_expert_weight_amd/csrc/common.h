@@ -53,33 +53,64 @@ __device__ __forceinline__ float silu(float g) {
   return g * sig;
 }
 
-// -------------------------------------------------------- DPP reductions --
-// Sums across aligned groups of N lanes (N = 2, 4, 8, 16) with DPP moves that
-// stay inside a 16-lane row: quad_perm swaps, then half-row and row mirrors.
-__device__ __forceinline__ float dpp_add_quad_xor1(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+// ------------------------------------------------------- wave reductions --
+// Cross-lane steps without LDS: DPP moves inside a 16-lane row (quad_perm
+// swaps, half-row and row mirrors), then the CDNA4 row swaps
+// v_permlane16_swap (rows 0<->1, 2<->3) and v_permlane32_swap (halves).
+// Every lane of the reduced group ends up holding the result.
+__device__ __forceinline__ uint32_t dpp_quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float dpp_add_quad_xor2(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float dpp_add_half_mirror(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_half_mirror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float dpp_add_row_mirror(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_row_mirror(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
+}
+// The partner row's value (lanes l and l^16) / partner half's value (l and l^32):
+// a swap leaves one copy of each operand in the two results.
+struct Pair { uint32_t a, b; };
+__device__ __forceinline__ Pair swap16(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return {r[0], r[1]};
+}
+__device__ __forceinline__ Pair swap32(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return {r[0], r[1]};
 }
 
-// Sum over each aligned group of N lanes; every lane of the group gets the sum.
+// Sum over each aligned group of N lanes (N = 1..64, power of two).
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
-  if constexpr (N >= 2) v = dpp_add_quad_xor1(v);
-  if constexpr (N >= 4) v = dpp_add_quad_xor2(v);
-  if constexpr (N >= 8) v = dpp_add_half_mirror(v);
-  if constexpr (N >= 16) v = dpp_add_row_mirror(v);
-  if constexpr (N >= 32) v += __shfl_xor(v, 16);
-  if constexpr (N >= 64) v += __shfl_xor(v, 32);
+  if constexpr (N >= 2) v += __uint_as_float(dpp_quad_xor1(__float_as_uint(v)));
+  if constexpr (N >= 4) v += __uint_as_float(dpp_quad_xor2(__float_as_uint(v)));
+  if constexpr (N >= 8) v += __uint_as_float(dpp_half_mirror(__float_as_uint(v)));
+  if constexpr (N >= 16) v += __uint_as_float(dpp_row_mirror(__float_as_uint(v)));
+  if constexpr (N >= 32) { Pair p = swap16(__float_as_uint(v)); v = __uint_as_float(p.a) + __uint_as_float(p.b); }
+  if constexpr (N >= 64) { Pair p = swap32(__float_as_uint(v)); v = __uint_as_float(p.a) + __uint_as_float(p.b); }
   return v;
+}
+
+// Unsigned max / min over the whole wave; every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_quad_xor1(v));
+  v = max(v, dpp_quad_xor2(v));
+  v = max(v, dpp_half_mirror(v));
+  v = max(v, dpp_row_mirror(v));
+  Pair p = swap16(v); v = max(p.a, p.b);
+  p = swap32(v); return max(p.a, p.b);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_quad_xor1(v));
+  v = min(v, dpp_quad_xor2(v));
+  v = min(v, dpp_half_mirror(v));
+  v = min(v, dpp_row_mirror(v));
+  Pair p = swap16(v); v = min(p.a, p.b);
+  p = swap32(v); return min(p.a, p.b);
 }
 
 // ------------------------------------------------------------- workspace --

@@ -4,15 +4,18 @@
 // paragraph on sparse activation and expert routing); it stays in fp32 because
 // the softmax is sensitive to quantisation error (MoE-SpeQ article, 2.1).
 #include "kernels.h"
+#include "sort_dev.h"
+#include "topk_dev.h"
 
 namespace moe {
 
 // ------------------------------------------------------------- logits --
 // One wave per expert row.  Lane l holds float4 number (l + 64 i) of the
 // fp32 router row in registers (coalesced 16-byte loads, 1 KiB per wave
-// instruction) and reuses it for every token: logits[t][e] = x_t . W_r[e]
-// with exact bf16 * fp32 products accumulated in fp32, then a wave sum.
-template <int VMAX>
+// instruction) and reuses it for every token; up to TB tokens are processed
+// per pass with all their activation loads issued together.
+// logits[t][e] = x_t . W_r[e] (+ bias): exact bf16 * fp32 products, fp32 sums.
+template <int VMAX, int TB>
 __global__ __launch_bounds__(128) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ w_router,
                                                             const float* __restrict__ bias,
@@ -25,106 +28,94 @@ __global__ __launch_bounds__(128) void router_logits_kernel(const uint16_t* __re
   const float4* wrow = reinterpret_cast<const float4*>(w_router + (size_t)e * H);
   float4 w[VMAX];
 #pragma unroll
-  for (int i = 0; i < VMAX; ++i) {
+  for (int i = 0; i < VMAX; ++i) {       // clamped loads, zeroed past the row (no branches)
     const int v = lane + kWave * i;
-    w[i] = (v < nvec) ? wrow[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 t = wrow[min(v, nvec - 1)];
+    w[i] = (v < nvec) ? t : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int t = 0; t < M; ++t) {
-    const uint2* xrow = reinterpret_cast<const uint2*>(x + (size_t)t * H);
-    float acc = 0.f;
+  for (int t0 = 0; t0 < M; t0 += TB) {
+    uint2 xv[TB][VMAX];
 #pragma unroll
-    for (int i = 0; i < VMAX; ++i) {
-      const int v = lane + kWave * i;
-      if (v < nvec) {
-        const uint2 xv = xrow[v];
-        acc = fmaf(bf16_bits_to_f32(xv.x & 0xFFFFu), w[i].x, acc);
-        acc = fmaf(bf16_bits_to_f32(xv.x >> 16), w[i].y, acc);
-        acc = fmaf(bf16_bits_to_f32(xv.y & 0xFFFFu), w[i].z, acc);
-        acc = fmaf(bf16_bits_to_f32(xv.y >> 16), w[i].w, acc);
+    for (int q = 0; q < TB; ++q) {
+      const uint2* xrow = reinterpret_cast<const uint2*>(x + (size_t)min(t0 + q, M - 1) * H);
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i) {
+        const int v = lane + kWave * i;
+        const uint2 t = xrow[min(v, nvec - 1)];
+        xv[q][i] = (v < nvec) ? t : make_uint2(0, 0);
       }
     }
-    acc = group_sum<kWave>(acc);
-    if (lane == 0) {
-      if (bias) acc += bias[(size_t)t * bias_stride + e];
-      logits[(size_t)t * E + e] = acc;
+#pragma unroll
+    for (int q = 0; q < TB; ++q) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i) {
+        acc = fmaf(bf16_bits_to_f32(xv[q][i].x & 0xFFFFu), w[i].x, acc);
+        acc = fmaf(bf16_bits_to_f32(xv[q][i].x >> 16), w[i].y, acc);
+        acc = fmaf(bf16_bits_to_f32(xv[q][i].y & 0xFFFFu), w[i].z, acc);
+        acc = fmaf(bf16_bits_to_f32(xv[q][i].y >> 16), w[i].w, acc);
+      }
+      acc = group_sum<kWave>(acc);
+      const int t = t0 + q;
+      if (lane == 0 && t < M) {
+        if (bias) acc += bias[(size_t)t * bias_stride + e];
+        logits[(size_t)t * E + e] = acc;
+      }
     }
   }
 }
 
-// ------------------------------------------------------------- top-k --
-// Order-preserving map of an fp32 onto uint32 (-0 is folded onto +0 first so
-// equal values tie on the index, as the definition asks).
-__device__ __forceinline__ uint32_t f32_orderable(float f) {
-  uint32_t u = __float_as_uint(f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float f32_from_orderable(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
-// Key: orderable logit in the high word, (2^32-1 - expert) in the low word,
-// so one unsigned max picks the largest logit and, among equal logits, the
-// lower expert index.  0 never occurs for a real entry.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-  return ((uint64_t)f32_orderable(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)k, off);
-    uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    k = (o > k) ? o : k;
-  }
-  return k;
-}
-
-// One wave per token; lane l owns experts l, l+64, ... (at most 16 of them).
-// k rounds of "wave max, owner drops it"; round i's winner lands in lane i,
-// which then forms its weight exp(l_i - l_0) / sum over the kept experts.
+// One wave per token.
+template <int C>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int M, int E,
                                                            int k, int* __restrict__ topk_ids,
                                                            float* __restrict__ topk_weights) {
-  constexpr int kPer = MOE_MAX_EXPERTS / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= M) return;
-  const float* row = logits + (size_t)t * E;
-  uint64_t key[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + kWave * j;
-    key[j] = (e < E) ? topk_key(row[e], e) : 0ull;
-  }
-  uint64_t best = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) best = key[j] > best ? key[j] : best;
-
-  int my_id = 0;
-  float my_val = 0.f;
-  float top_val = 0.f;
-  for (int i = 0; i < k; ++i) {
-    const uint64_t win = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)win);
-    const float v = f32_from_orderable((uint32_t)(win >> 32));
-    if (i == 0) top_val = v;
-    if (lane == i) { my_id = e; my_val = v; }
-    if ((e & (kWave - 1)) == lane) {       // owner drops the winner, rescans
-      best = 0;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if (key[j] == win) key[j] = 0ull;
-        best = key[j] > best ? key[j] : best;
-      }
-    }
-  }
-  const float ex = (lane < k) ? expf(my_val - top_val) : 0.f;
-  const float sum = group_sum<kWave>(ex);
+  int id; float w;
+  wave_topk_softmax<C>(logits + (size_t)t * E, E, k, id, w);
   if (lane < k) {
-    topk_ids[(size_t)t * k + lane] = my_id;
-    topk_weights[(size_t)t * k + lane] = ex / sum;
+    topk_ids[(size_t)t * k + lane] = id;
+    topk_weights[(size_t)t * k + lane] = w;
   }
+}
+
+// Small batches: one workgroup of M waves takes every token's top-k into LDS
+// (and the outputs), then wave 0 sorts the M*k pairs by expert in LDS and the
+// block writes the sort outputs and the slot records.
+template <int C>
+__global__ __launch_bounds__(64 * kTopkSortMaxTokens) void topk_sort_small_kernel(
+    const float* __restrict__ logits, int M, int E, int k, int ebits, int* __restrict__ topk_ids,
+    float* __restrict__ topk_weights, int* __restrict__ offsets, int* __restrict__ sorted_pairs,
+    int* __restrict__ active, int* __restrict__ num_active, RecOut ro) {
+  constexpr int kMaxPairs = kTopkSortMaxTokens * MOE_MAX_TOPK;
+  __shared__ int ids_lds[kMaxPairs];
+  __shared__ float w_lds[kMaxPairs];
+  __shared__ int sp_lds[kMaxPairs];
+  __shared__ int act_lds[kMaxPairs];
+  __shared__ int sort_lds[wave_sort_lds_ints(C)];
+  __shared__ int na_lds;
+  const int N = M * k;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = threadIdx.x / kWave;
+  int id; float w;
+  wave_topk_softmax<C>(logits + (size_t)t * E, E, k, id, w);
+  if (lane < k) {
+    ids_lds[t * k + lane] = id;
+    w_lds[t * k + lane] = w;
+    topk_ids[(size_t)t * k + lane] = id;
+    topk_weights[(size_t)t * k + lane] = w;
+  }
+  __syncthreads();
+  int* off = sort_lds + kWave * C + 1;
+  if (t == 0) wave_sort_small<C>(ids_lds, N, E, ebits, sort_lds, off, sp_lds, act_lds, &na_lds);
+  __syncthreads();
+  const int D = na_lds;
+  block_store_sort(E, off, sp_lds, act_lds, D, offsets, sorted_pairs, active, num_active);
+  if (ro.rec)
+    for (int slot = threadIdx.x; slot < max_slots(M, k, E); slot += blockDim.x)
+      ro.rec[slot] = make_slot_record(slot, D, off, sp_lds, act_lds, w_lds, M, k, E, ro.has_shared);
 }
 
 hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias,
@@ -132,10 +123,16 @@ hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const 
                                 hipStream_t s) {
   const int waves_per_block = 2;
   dim3 grid((E + waves_per_block - 1) / waves_per_block), block(waves_per_block * kWave);
-  if (H <= 2560)
-    router_logits_kernel<10><<<grid, block, 0, s>>>(x, w_router, bias, bias_stride, M, H, E, logits);
-  else
-    router_logits_kernel<32><<<grid, block, 0, s>>>(x, w_router, bias, bias_stride, M, H, E, logits);
+  if (H <= 2560) {
+    if (M == 1)
+      router_logits_kernel<10, 1><<<grid, block, 0, s>>>(x, w_router, bias, bias_stride, M, H, E, logits);
+    else if (M <= 4)
+      router_logits_kernel<10, 4><<<grid, block, 0, s>>>(x, w_router, bias, bias_stride, M, H, E, logits);
+    else
+      router_logits_kernel<10, 8><<<grid, block, 0, s>>>(x, w_router, bias, bias_stride, M, H, E, logits);
+  } else {
+    router_logits_kernel<32, 1><<<grid, block, 0, s>>>(x, w_router, bias, bias_stride, M, H, E, logits);
+  }
   return hipGetLastError();
 }
 
@@ -143,7 +140,21 @@ hipError_t launch_topk_softmax(const float* logits, int M, int E, int k, int* id
                                hipStream_t s) {
   const int waves_per_block = 4;
   dim3 grid((M + waves_per_block - 1) / waves_per_block), block(waves_per_block * kWave);
-  topk_softmax_kernel<<<grid, block, 0, s>>>(logits, M, E, k, ids, weights);
+  if (topk_lane_experts(E) == 8)
+    topk_softmax_kernel<8><<<grid, block, 0, s>>>(logits, M, E, k, ids, weights);
+  else
+    topk_softmax_kernel<16><<<grid, block, 0, s>>>(logits, M, E, k, ids, weights);
+  return hipGetLastError();
+}
+
+bool topk_sort_fits_one_block(int M) { return M <= kTopkSortMaxTokens; }
+
+hipError_t launch_topk_sort_small(const float* logits, int M, int E, int k, int* ids, float* weights,
+                                  int* offsets, int* sorted_pairs, int* active, int* num_active,
+                                  hipStream_t s, RecOut ro) {
+  auto kern = topk_lane_experts(E) == 8 ? topk_sort_small_kernel<8> : topk_sort_small_kernel<16>;
+  kern<<<1, M * kWave, 0, s>>>(logits, M, E, k, expert_bits(E), ids, weights, offsets, sorted_pairs, active,
+                               num_active, ro);
   return hipGetLastError();
 }
 

@@ -1,0 +1,260 @@
+// Stable counting sort of the (token, slot) pairs by expert (MoE-SpeQ article,
+// section 4.2: gather every token's expert assignments, order them by expert
+// id and run each expert once over its tokens).  One workgroup does it all in
+// LDS: per-wave histograms, an exclusive scan over experts, then each wave
+// places its own segment of pairs in order.  Stability comes from three
+// facts: waves own consecutive segments, a wave walks its segment in order in
+// 64-pair steps, and inside a step a pair's rank is the number of lower lanes
+// holding the same expert (found with one ballot per expert-id bit).
+#pragma once
+
+#include "kernels.h"
+
+namespace moe {
+
+// Inclusive prefix sum over the wave: Hillis-Steele inside each 16-lane row
+// with DPP row shifts (lanes whose source falls outside the row add 0), then
+// the row totals carried across rows with readlane.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  if (lane >= 16) v += r0;
+  if (lane >= 32) v += r1;
+  if (lane >= 48) v += r2;
+  return v;
+}
+
+// Ints of LDS block_sort_pairs needs with nw waves and E experts.
+__host__ __device__ inline size_t sort_lds_ints(int nw, int E) { return (size_t)nw * E + E + 2 * nw; }
+
+// Sort `N` pairs whose expert ids are ids[0..N) (global or LDS).  Uses
+// sort_lds_ints(nw, E) ints of LDS at `lds`; every thread of the block calls it.
+// With sp_lds / act_lds / na_lds non-null it also keeps sorted_pairs, the
+// active list and D in LDS (for an epilogue in the same block); the exclusive
+// offsets stay at lds + nw*E after the call.
+__device__ inline void block_sort_pairs(const int* ids, int N, int E, int ebits, int* lds,
+                                 int* __restrict__ offsets, int* __restrict__ sorted_pairs,
+                                 int* __restrict__ active, int* __restrict__ num_active,
+                                 int* sp_lds = nullptr, int* act_lds = nullptr, int* na_lds = nullptr) {
+  const int nw = blockDim.x / kWave;
+  const int w = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int bd = blockDim.x;
+  int* cnt = lds;                 // [nw][E]: per-wave counts, then per-wave running bases
+  int* off = cnt + nw * E;        // [E]: exclusive offsets of each expert
+  int* wtot = off + E;            // [2 * nw]: per-wave scan totals
+
+  for (int i = threadIdx.x; i < nw * E; i += bd) cnt[i] = 0;
+  __syncthreads();
+
+  const int seg = (N + nw - 1) / nw;
+  const int beg = min(N, w * seg), end = min(N, beg + seg);
+  for (int p = beg + lane; p < end; p += kWave) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[w * E + e], 1);   // invalid ids are dropped
+  }
+  __syncthreads();
+
+  // Each thread owns a contiguous span of experts: total count per expert and
+  // the exclusive prefix over waves (stored back in place as wave bases).
+  const int per = (E + bd - 1) / bd;
+  const int e0 = min(E, threadIdx.x * per), e1 = min(E, e0 + per);
+  int csum = 0, asum = 0;
+  for (int e = e0; e < e1; ++e) {
+    int run = 0;
+    for (int v = 0; v < nw; ++v) {
+      const int c = cnt[v * E + e];
+      cnt[v * E + e] = run;
+      run += c;
+    }
+    off[e] = run;                  // total, turned into an offset below
+    csum += run;
+    asum += run > 0;
+  }
+  // Block-wide exclusive scan of (count, active flag) over the thread spans.
+  const int cinc = wave_inclusive_scan(csum);
+  const int ainc = wave_inclusive_scan(asum);
+  if (lane == kWave - 1) { wtot[w] = cinc; wtot[nw + w] = ainc; }
+  __syncthreads();
+  int cbase = cinc - csum, abase = ainc - asum;
+  for (int v = 0; v < w; ++v) { cbase += wtot[v]; abase += wtot[nw + v]; }
+  for (int e = e0; e < e1; ++e) {
+    const int c = off[e];
+    off[e] = cbase;
+    offsets[e] = cbase;
+    if (c > 0) {
+      if (act_lds) act_lds[abase] = e;
+      active[abase++] = e;
+    }
+    cbase += c;
+  }
+  if (threadIdx.x == bd - 1) {
+    offsets[E] = cbase;            // == number of valid pairs
+    *num_active = abase;
+    if (na_lds) *na_lds = abase;
+  }
+  __syncthreads();
+
+  // Placement: wave w walks its segment in order, 64 pairs per step.
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int base = beg; base < end; base += kWave) {
+    const int p = base + lane;
+    int e = (p < end) ? ids[p] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    if (!valid) e = 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(valid && bit);
+      match &= bit ? bal : ~bal;
+    }
+    if (valid) {
+      const int rank = __popcll(match & lt_mask);
+      const int pos = off[e] + cnt[w * E + e] + rank;
+      sorted_pairs[pos] = p;
+      if (sp_lds) sp_lds[pos] = p;
+      __builtin_amdgcn_wave_barrier();
+      if (rank == 0) cnt[w * E + e] += __popcll(match);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Slot record of `slot` from a finished sort: slots [0, D) are the active
+// experts in increasing order, slot D the shared expert (if any), later slots
+// have no work (e = -1).  off = exclusive offsets (E+1 entries), sp = sorted
+// pairs, act = active list, w = routing weights of the pairs (LDS or global).
+__device__ __forceinline__ SlotRec make_slot_record(int slot, int D, const int* off, const int* sp,
+                                                    const int* act, const float* w, int M, int k, int E,
+                                                    int has_shared) {
+  SlotRec r;
+  r.pad[0] = r.pad[1] = r.pad[2] = r.pad[3] = 0;
+  if (slot < D) {
+    r.e = act[slot];
+    r.pbeg = off[r.e];
+    r.n = off[r.e + 1] - r.pbeg;
+    r.hrow0 = r.pbeg;
+#pragma unroll
+    for (int q = 0; q < kRecTokens; ++q) {
+      const int pair = (q < r.n) ? sp[r.pbeg + q] : 0;
+      r.tok[q] = (q < r.n) ? pair / k : 0;
+      r.w[q] = (q < r.n) ? w[pair] : 0.f;
+    }
+  } else if (slot == D && has_shared) {
+    r.e = E; r.pbeg = -1; r.n = M; r.hrow0 = M * k;
+#pragma unroll
+    for (int q = 0; q < kRecTokens; ++q) { r.tok[q] = q < M ? q : 0; r.w[q] = 1.f; }
+  } else {
+    r.e = -1; r.pbeg = -1; r.n = 0; r.hrow0 = 0;
+#pragma unroll
+    for (int q = 0; q < kRecTokens; ++q) { r.tok[q] = 0; r.w[q] = 0.f; }
+  }
+  return r;
+}
+
+// Slot records from the finished sort in global memory (this block wrote it
+// and a barrier made it visible): one thread per possible slot.
+__device__ inline void block_write_slot_records(const RecOut& ro, int E, int nslots,
+                                                const int* __restrict__ offsets,
+                                                const int* __restrict__ sorted_pairs,
+                                                const int* __restrict__ active,
+                                                const int* __restrict__ num_active) {
+  const int D = *num_active;
+  for (int slot = threadIdx.x; slot < nslots; slot += blockDim.x)
+    ro.rec[slot] = make_slot_record(slot, D, offsets, sorted_pairs, active, ro.topk_weights, ro.M, ro.k, E,
+                                    ro.has_shared);
+}
+
+// LDS of wave_sort_small<C>: two arrays of 64*C + 1 ints.
+__host__ __device__ constexpr int wave_sort_lds_ints(int C) { return 2 * (kWave * C + 1); }
+
+// Stable counting sort of N pairs (expert ids in LDS) by one wave, for the
+// small batches of decode (E <= 64*C).  Lane l owns experts [l*C, l*C + C):
+// histogram with LDS atomics, per-lane scan of its counts, one wave scan of
+// the lane totals; then pairs are placed 64 at a time in order, a pair's rank
+// among equal experts of its step coming from one ballot per expert-id bit.
+// Leaves in LDS: off[0..E] exclusive offsets (off[E] = valid pairs), sp =
+// sorted pairs, act = active experts in increasing order, *na = their number.
+// `lds` holds wave_sort_lds_ints(C) ints; off points into it.
+template <int C>
+__device__ inline void wave_sort_small(const int* ids, int N, int E, int ebits, int* lds, int*& off, int* sp,
+                                       int* act, int* na) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int* cur = lds;                       // histogram, then running positions
+  off = lds + kWave * C + 1;
+#pragma unroll
+  for (int i = 0; i < C; ++i) cur[lane * C + i] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (int p = lane; p < N; p += kWave) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cur[e], 1);     // invalid ids are dropped
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int c[C], tot = 0, pres = 0;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    c[i] = cur[lane * C + i];
+    tot += c[i];
+    pres += c[i] > 0;
+  }
+  const int tinc = wave_inclusive_scan(tot), pinc = wave_inclusive_scan(pres);
+  int run = tinc - tot, slot = pinc - pres;
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int x = lane * C + i;
+    if (x < E) {
+      off[x] = run;
+      cur[x] = run;
+      if (c[i] > 0) act[slot++] = x;
+    }
+    run += c[i];
+  }
+  if (lane == kWave - 1) {
+    off[E] = tinc;                      // valid pairs
+    *na = pinc;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int base = 0; base < N; base += kWave) {
+    const int p = base + lane;
+    int e = (p < N) ? ids[p] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    if (!valid) e = 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(valid && bit);
+      match &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(match & lt_mask);
+    if (valid) sp[cur[e] + rank] = p;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == 0) cur[e] += __popcll(match);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Copy a sort kept in LDS to the caller's arrays (every thread of the block;
+// after a barrier that follows wave_sort_small).
+__device__ inline void block_store_sort(int E, const int* off, const int* sp, const int* act, int D,
+                                        int* __restrict__ offsets, int* __restrict__ sorted_pairs,
+                                        int* __restrict__ active, int* __restrict__ num_active) {
+  const int nvalid = off[E];
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) offsets[i] = off[i];
+  for (int i = threadIdx.x; i < nvalid; i += blockDim.x) sorted_pairs[i] = sp[i];
+  for (int i = threadIdx.x; i < D; i += blockDim.x) active[i] = act[i];
+  if (threadIdx.x == 0) *num_active = D;
+}
+
+}  // namespace moe

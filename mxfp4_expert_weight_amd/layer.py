@@ -79,10 +79,16 @@ class LayerBuffers:
 
 
 def run_layer(d: DeviceLayerSet, b: LayerBuffers, w: Optional[binding.moe_mxfp4_weights] = None,
-              stream=None):
-    """route -> sort -> forward for one layer set (three C calls, stream-ordered)."""
+              stream=None, fused: bool = True):
+    """One layer: moe_layer (fused=True) or moe_route -> moe_sort_by_expert ->
+    moe_mxfp4_forward (fused=False); same outputs, stream-ordered."""
     if w is None:
         w = d.weights()
+    if fused:
+        binding.moe_layer(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, b.logits, b.ids,
+                          b.weights, b.offsets, b.pairs, b.active, b.num_active, b.y, b.ws, b.ws_bytes,
+                          stream)
+        return
     binding.moe_route(d.x, d.w_router, d.bias, d.bias_row_stride, d.M, d.H, d.E, d.k, b.logits, b.ids,
                       b.weights, stream)
     binding.moe_sort_by_expert(b.ids, d.M, d.k, d.E, b.offsets, b.pairs, b.active, b.num_active, stream)

@@ -126,10 +126,10 @@ def _overlap_bias(rng: np.random.Generator, M: int, E: int, k: int) -> np.ndarra
         mine: list[int] = []
         for _ in range(k):
             reuse_pool = [e for e in union if e not in mine]
-            if t > 0 and reuse_pool and rng.random() < OVERLAP_PROB:
+            fresh = np.setdiff1d(np.arange(E), np.array(union + mine, dtype=np.int64))
+            if t > 0 and reuse_pool and (rng.random() < OVERLAP_PROB or fresh.size == 0):
                 mine.append(reuse_pool[rng.integers(len(reuse_pool))])
             else:
-                fresh = np.setdiff1d(np.arange(E), np.array(union + mine, dtype=np.int64))
                 mine.append(int(fresh[rng.integers(len(fresh))]))
         bias[t, mine] = OVERLAP_BIAS
         for e in mine:

@@ -96,6 +96,19 @@ def test_forward_host_checks(lib):
     assert _status(f, *(args[:11] + [ws - 1, 0])) == B.MOE_ERR_WORKSPACE
 
 
+def test_layer_host_checks(lib):
+    w = B.make_weights(A, A, A, A, 512, 2560, 768, 1)
+    ws = B.moe_workspace_bytes(1, 8, 512, 2560, 768)
+    f = B.moe_layer
+    args = [A, A, None, 0, w, 1, 8, A, A, A, A, A, A, A, A, A, ws, 0]
+    assert _status(f, *([None] + args[1:])) == B.MOE_ERR_NULL
+    assert _status(f, *(args[:4] + [None] + args[5:])) == B.MOE_ERR_NULL
+    assert _status(f, *(args[:5] + [0] + args[6:])) == B.MOE_ERR_SHAPE
+    assert _status(f, *(args[:2] + [A, 3] + args[4:])) == B.MOE_ERR_SHAPE         # bias stride
+    assert _status(f, *(args[:1] + [MIS] + args[2:])) == B.MOE_ERR_ALIGN
+    assert _status(f, *(args[:16] + [ws - 1, 0])) == B.MOE_ERR_WORKSPACE
+
+
 def test_dequant_host_checks(lib):
     d = B.moe_mxfp4_dequantize
     assert _status(d, None, A, 4, 64, A, 0) == B.MOE_ERR_NULL

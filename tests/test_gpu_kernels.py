@@ -61,7 +61,7 @@ def _topk_gpu(torch, logits, k):
 
 @pytest.mark.parametrize("E,k,M,kind", [
     (16, 2, 64, "ties"), (512, 8, 300, "normal"), (512, 8, 200, "ties"), (1024, 32, 50, "ties"),
-    (100, 7, 33, "normal"), (1, 1, 5, "normal"), (64, 64, 3, "ties"), (1000, 1, 17, "signed_zero"),
+    (100, 7, 33, "normal"), (1, 1, 5, "normal"), (32, 32, 3, "ties"), (1000, 1, 17, "signed_zero"),
     (512, 8, 4096, "normal"),
 ])
 def test_topk_softmax_exact_ids(E, k, M, kind):

@@ -1,5 +1,6 @@
-"""GPU parity of the whole layer (route -> sort -> forward through the C ABI,
-the launch sequence bench.py times) against the float64 oracle.
+"""GPU parity of the whole layer against the float64 oracle, through both
+C-ABI paths: moe_layer (the call bench.py times) and moe_route ->
+moe_sort_by_expert -> moe_mxfp4_forward.
 
 Output bar: |gpu - ref| <= 1e-2 (|ref| + rms(ref)) per element.  Routing: ids
 exact except where the oracle's order is decided by less than the fp32 error
@@ -15,12 +16,12 @@ from mxfp4_expert_weight_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-def _run(torch, ls):
+def _run(torch, ls, fused=True):
     from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer
     wl = ls.wl
     d = DeviceLayerSet.from_host(ls)
     b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
-    run_layer(d, b)
+    run_layer(d, b, fused=fused)
     torch.cuda.synchronize()
     out = dict(y=b.y.cpu().numpy(), ids=b.ids.cpu().numpy(), w=b.weights.cpu().numpy(),
                logits=b.logits.cpu().numpy(), hdr=b.header(),
@@ -28,10 +29,11 @@ def _run(torch, ls):
     return out, d, b
 
 
-def _check_full(torch, ls, what):
+def _check_full(torch, ls, what, fused=True):
     wl = ls.wl
-    say(f"layer {what}: M={wl.M} H={wl.H} I={wl.I} E={wl.E} k={wl.k} shared={wl.shared} {wl.routing}")
-    g, _, _ = _run(torch, ls)
+    say(f"layer {what}: M={wl.M} H={wl.H} I={wl.I} E={wl.E} k={wl.k} shared={wl.shared} {wl.routing} "
+        f"{'moe_layer' if fused else 'three calls'}")
+    g, _, _ = _run(torch, ls, fused)
     r = oracle.moe_layer(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s,
                          wl.k, wl.shared)
     xf = oracle.bf16_bits_to_f64(ls.x_bits)
@@ -47,9 +49,10 @@ def _check_full(torch, ls, what):
     return g, r
 
 
-def test_tiny_config_every_element():
+@pytest.mark.parametrize("fused", [True, False])
+def test_tiny_config_every_element(fused):
     torch = need_gpu()
-    _check_full(torch, synth.layer_set("tiny"), "tiny")
+    _check_full(torch, synth.layer_set("tiny"), "tiny", fused)
 
 
 @pytest.mark.parametrize("M,H,I,E,k,shared,routing", [
@@ -60,18 +63,24 @@ def test_tiny_config_every_element():
     (64, 128, 96, 16, 4, True, "zipf"),      # many tokens per expert
     (2, 8192, 64, 3, 2, True, "plain"),      # largest hidden size
     (2, 64, 4096, 3, 1, True, "plain"),      # largest intermediate size
+    (8, 64, 32, 40, 8, True, "overlap"),     # 64 pairs: largest one-wave sort in the fused route
+    (8, 64, 32, 600, 9, False, "plain"),     # 72 pairs: block sort; E > 512 top-k
+    (2, 64, 32, 1024, 32, True, "plain"),    # largest E and k
+    (4, 64, 32, 1024, 32, True, "plain"),    # 128 pairs routed inside the gate/up blocks
 ])
 def test_edge_shapes_every_element(M, H, I, E, k, shared, routing):
     torch = need_gpu()
     wl = synth.custom(f"edge{M}x{H}x{I}", M, H, I, E, k, shared, routing, seed=M + H + I)
-    _check_full(torch, synth.layer_set(wl), wl.name)
+    ls = synth.layer_set(wl)
+    _check_full(torch, ls, wl.name, fused=True)
+    _check_full(torch, ls, wl.name, fused=False)
 
 
 @pytest.mark.parametrize("name,sets", [("ling_m1", [0, 17]), ("ling_m4_mtp", [0, 39])])
 def test_ling_decode_full_size(name, sets):
     torch = need_gpu()
-    for l in sets:
-        _check_full(torch, synth.layer_set(name, l), f"{name}/set{l}")
+    for i, l in enumerate(sets):
+        _check_full(torch, synth.layer_set(name, l), f"{name}/set{l}", fused=(i == 0))
 
 
 @pytest.mark.parametrize("name,tokens", [("ling_m32_zipf", [0, 5, 17, 31]),
