@@ -23,48 +23,103 @@ constexpr int DN_LDS_PER_WAVE = 4 * DN_NR * (MOE_MAX_INTER / 32);
 constexpr int GU_SHORT_H = 32 * GU_HC * 16;         // longest row the single-pass path holds (2560)
 constexpr int DN_SHORT_I = 16 * DN_HC * 16;         // (768)
 
-// Routing inside a gate/up block (decode batches, M <= kRoutedMaxTokens):
-// wave t takes token t's top-k from the logits, wave 0 sorts the pairs by
-// expert in LDS, and the block reads its own slot (blockIdx.y) from the result.
-// Every block computes the same routing from the same logits; block (0, 0)
-// writes the routing outputs and block (0, slot) the slot record the down
-// kernel reads.  Returns false when the slot has no work.
+// Routing inside a gate/up block (decode batches, M <= kRoutedMaxTokens, so
+// at most 128 pairs: two per lane).  Every workgroup first takes the top-k of
+// token t in wave t, into LDS.  Then:
+//  - the workgroup at x = 0 of the extra last grid row is the writer: wave 0
+//    sorts the pairs and the block writes the routing outputs and the header;
+//  - every other workgroup needs only its own slot s = blockIdx.y: each wave
+//    marks the chosen experts in its own LDS bitmap, counts the active experts
+//    with a popcount scan over the bitmap words, takes the s-th set bit as its
+//    expert and finds that expert's pairs with ballots (no barrier, no sort);
+//    block (0, s) writes the slot record the down kernel reads.
+// Every workgroup computes the same top-k from the same logits.  Returns
+// false when the workgroup has no gate/up work.
 template <int C>
-__device__ __forceinline__ bool route_in_block(const ForwardArgs& a, const RouteOut& r, ExpertSlot& s,
-                                               int& n_act) {
-  __shared__ int ids_lds[kRoutedMaxPairs];
-  __shared__ float w_lds[kRoutedMaxPairs];
-  __shared__ int sp_lds[kRoutedMaxPairs];
-  __shared__ int act_lds[kRoutedMaxPairs];
-  __shared__ int sort_lds[wave_sort_lds_ints(C)];
-  __shared__ int na_lds;
+__device__ __forceinline__ bool route_in_block(const ForwardArgs& a, const RouteOut& r, ExpertSlot& s) {
+  constexpr int kWords = MOE_MAX_EXPERTS / 32;           // bitmap words; index kWords is a sink
+  __shared__ SmallSortLds<C, kRoutedMaxPairs> L;
+  __shared__ uint32_t bits[GU_WPB][kWords + 1];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int nw = blockDim.x / kWave;
-  const int N = a.M * a.k;
+  const int N = a.M * a.k, E = a.E;
+  const bool writer = blockIdx.y == gridDim.y - 1;
+  if (writer && blockIdx.x != 0) return false;
+  if (lane <= kWords) bits[wave][lane] = 0u;
   for (int t = wave; t < a.M; t += nw) {
     int id; float w;
-    wave_topk_softmax<C>(r.logits + (size_t)t * a.E, a.E, a.k, id, w);
+    wave_topk_softmax<C>(r.logits + (size_t)t * E, E, a.k, id, w);
     if (lane < a.k) {
-      ids_lds[t * a.k + lane] = id;
-      w_lds[t * a.k + lane] = w;
+      L.ids[t * a.k + lane] = id;
+      L.w[t * a.k + lane] = w;
+      L.tok[t * a.k + lane] = t;
     }
   }
   __syncthreads();
-  int* off = sort_lds + kWave * C + 1;
-  if (wave == 0) wave_sort_small<C>(ids_lds, N, a.E, r.ebits, sort_lds, off, sp_lds, act_lds, &na_lds);
-  __syncthreads();
-  const int D = na_lds;
-  n_act = D;
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    block_store_sort(a.E, off, sp_lds, act_lds, D, r.offsets, r.sorted_pairs, r.active, r.num_active);
-    for (int i = threadIdx.x; i < N; i += blockDim.x) {
-      r.topk_ids[i] = ids_lds[i];
-      r.topk_weights[i] = w_lds[i];
+  if (writer) {
+    if (wave == 0) wave_sort_small(L, N, E, r.ebits);
+    __syncthreads();
+    block_store_small_sort(L, N, E, r.topk_ids, r.topk_weights, r.offsets, r.sorted_pairs, r.active,
+                           r.num_active);
+    if (threadIdx.x == 0) {
+      a.hdr->gemv_experts = L.na + a.has_shared;        // every expert runs on this path
+      a.hdr->mfma_experts = 0;
     }
+    return false;
   }
-  const SlotRec rec = make_slot_record(blockIdx.y, D, off, sp_lds, act_lds, w_lds, a.M, a.k, a.E,
-                                       a.has_shared);
-  if (blockIdx.x == 0 && threadIdx.x == 0) r.rec[blockIdx.y] = rec;
+  // this wave's copy of the pairs: pair `lane` (A) and pair `lane + 64` (B)
+  const int pA = min(lane, N - 1), pB = min(lane + kWave, N - 1);
+  const int eA = L.ids[pA], eB = L.ids[pB];
+  const int tA = L.tok[pA], tB = L.tok[pB];
+  const float wA = L.w[pA], wB = L.w[pB];
+  const bool vA = lane < N && (unsigned)eA < (unsigned)E;
+  const bool vB = lane + kWave < N && (unsigned)eB < (unsigned)E;
+  uint32_t* mb = bits[wave];
+  atomicOr(&mb[vA ? (eA >> 5) : kWords], 1u << (eA & 31));
+  atomicOr(&mb[vB ? (eB >> 5) : kWords], 1u << (eB & 31));
+  wave_lds_fence();
+  const int nwords = (E + 31) >> 5;
+  const uint32_t word = (lane < nwords) ? mb[min(lane, kWords - 1)] : 0u;
+  const int inc = wave_inclusive_scan(__popc(word));
+  const int D = __builtin_amdgcn_readlane(inc, kWave - 1);
+  const int slot = blockIdx.y;
+  SlotRec rec;
+  rec.pad[0] = rec.pad[1] = rec.pad[2] = rec.pad[3] = 0;
+#pragma unroll
+  for (int q = 0; q < kRecTokens; ++q) { rec.tok[q] = 0; rec.w[q] = 0.f; }
+  if (slot < D) {
+    const int wsel = (int)__builtin_ctzll(__ballot(inc > slot));          // word holding the expert
+    uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)word, wsel);
+    int nth = slot - (__builtin_amdgcn_readlane(inc, wsel) - __popc(wb));
+    for (; nth > 0; --nth) wb &= wb - 1u;
+    const int e = wsel * 32 + __builtin_ctz(wb);
+    uint64_t mA = __ballot(vA && eA == e), mB = __ballot(vB && eB == e);
+    rec.e = e;
+    rec.n = __popcll(mA) + __popcll(mB);
+    rec.pbeg = __popcll(__ballot(vA && eA < e)) + __popcll(__ballot(vB && eB < e));
+    rec.hrow0 = rec.pbeg;
+#pragma unroll
+    for (int q = 0; q < kRecTokens; ++q) {             // the expert's pairs in order
+      if (mA) {
+        const int p = (int)__builtin_ctzll(mA);
+        rec.tok[q] = __builtin_amdgcn_readlane(tA, p);
+        rec.w[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wA), p));
+        mA &= mA - 1;
+      } else if (mB) {
+        const int p = (int)__builtin_ctzll(mB);
+        rec.tok[q] = __builtin_amdgcn_readlane(tB, p);
+        rec.w[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wB), p));
+        mB &= mB - 1;
+      }
+    }
+  } else if (slot == D && a.has_shared) {
+    rec.e = E; rec.n = a.M; rec.pbeg = -1; rec.hrow0 = N;
+#pragma unroll
+    for (int q = 0; q < kRecTokens; ++q) { rec.tok[q] = q < a.M ? q : 0; rec.w[q] = 1.f; }
+  } else {
+    rec.e = -1; rec.n = 0; rec.pbeg = -1; rec.hrow0 = 0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) r.rec[slot] = rec;
   s.e = rec.e; s.n = rec.n; s.pbeg = rec.pbeg; s.hrow0 = rec.hrow0;
 #pragma unroll
   for (int q = 0; q < kRecTokens; ++q) { s.tok[q] = rec.tok[q]; s.w[q] = rec.w[q]; }
@@ -84,16 +139,14 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
     for (size_t i = b * blockDim.x + threadIdx.x; i < total; i += nblk * blockDim.x) a.y[i] = 0.f;
   }
   ExpertSlot s;
-  int n_act = 0;
   if constexpr (C > 0) {
-    if (!route_in_block<C>(a, r, s, n_act)) return;     // uniform over the block
+    if (!route_in_block<C>(a, r, s)) return;             // uniform over the block
   } else {
     if (!resolve_slot(blockIdx.y, a, s)) return;
-  }
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    if constexpr (C == 0) n_act = *a.num_active;
-    a.hdr->gemv_experts = n_act + a.has_shared;          // every expert runs on this path
-    a.hdr->mfma_experts = 0;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+      a.hdr->gemv_experts = *a.num_active + a.has_shared;  // every expert runs on this path
+      a.hdr->mfma_experts = 0;
+    }
   }
   __shared__ uint8_t s_lds[GU_WPB][GU_LDS_PER_WAVE];
   const int wave = threadIdx.x / kWave;
@@ -140,10 +193,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 namespace {
 
+// routed: the gate/up grid has one more row (the routing writer).
 hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, const RouteOut& r,
-                       hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+                       bool routed, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
-  dim3 ggu((a.I + GU_PAIRS_PER_BLOCK - 1) / GU_PAIRS_PER_BLOCK, slots), bgu(GU_WPB * kWave);
+  dim3 ggu((a.I + GU_PAIRS_PER_BLOCK - 1) / GU_PAIRS_PER_BLOCK, slots + (routed ? 1 : 0));
+  dim3 bgu(GU_WPB * kWave);
   dim3 gdn((a.H + DN_ROWS_PER_BLOCK - 1) / DN_ROWS_PER_BLOCK, slots), bdn(DN_WPB * kWave);
   auto dn = (a.I <= DN_SHORT_I) ? down_kernel<true> : down_kernel<false>;
   // with events, they take the gate/up kernel's own begin/end timestamps
@@ -158,8 +213,8 @@ hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, 
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const RouteOut none{};
-  return launch_pair(a.H <= GU_SHORT_H ? gateup_kernel<true, 0> : gateup_kernel<false, 0>, a, none, s, start,
-                     stop);
+  return launch_pair(a.H <= GU_SHORT_H ? gateup_kernel<true, 0> : gateup_kernel<false, 0>, a, none, false, s,
+                     start, stop);
 }
 
 hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s, hipEvent_t start,
@@ -170,7 +225,7 @@ hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStr
     gu = short_h ? gateup_kernel<true, 8> : gateup_kernel<false, 8>;
   else
     gu = short_h ? gateup_kernel<true, 16> : gateup_kernel<false, 16>;
-  return launch_pair(gu, a, r, s, start, stop);
+  return launch_pair(gu, a, r, true, s, start, stop);
 }
 
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols, float* out,

@@ -89,33 +89,24 @@ __global__ __launch_bounds__(64 * kTopkSortMaxTokens) void topk_sort_small_kerne
     const float* __restrict__ logits, int M, int E, int k, int ebits, int* __restrict__ topk_ids,
     float* __restrict__ topk_weights, int* __restrict__ offsets, int* __restrict__ sorted_pairs,
     int* __restrict__ active, int* __restrict__ num_active, RecOut ro) {
-  constexpr int kMaxPairs = kTopkSortMaxTokens * MOE_MAX_TOPK;
-  __shared__ int ids_lds[kMaxPairs];
-  __shared__ float w_lds[kMaxPairs];
-  __shared__ int sp_lds[kMaxPairs];
-  __shared__ int act_lds[kMaxPairs];
-  __shared__ int sort_lds[wave_sort_lds_ints(C)];
-  __shared__ int na_lds;
+  __shared__ SmallSortLds<C, kTopkSortMaxTokens * MOE_MAX_TOPK> L;
   const int N = M * k;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = threadIdx.x / kWave;
   int id; float w;
   wave_topk_softmax<C>(logits + (size_t)t * E, E, k, id, w);
   if (lane < k) {
-    ids_lds[t * k + lane] = id;
-    w_lds[t * k + lane] = w;
-    topk_ids[(size_t)t * k + lane] = id;
-    topk_weights[(size_t)t * k + lane] = w;
+    L.ids[t * k + lane] = id;
+    L.w[t * k + lane] = w;
+    L.tok[t * k + lane] = t;
   }
   __syncthreads();
-  int* off = sort_lds + kWave * C + 1;
-  if (t == 0) wave_sort_small<C>(ids_lds, N, E, ebits, sort_lds, off, sp_lds, act_lds, &na_lds);
+  if (t == 0) wave_sort_small(L, N, E, ebits);
   __syncthreads();
-  const int D = na_lds;
-  block_store_sort(E, off, sp_lds, act_lds, D, offsets, sorted_pairs, active, num_active);
+  block_store_small_sort(L, N, E, topk_ids, topk_weights, offsets, sorted_pairs, active, num_active);
   if (ro.rec)
     for (int slot = threadIdx.x; slot < max_slots(M, k, E); slot += blockDim.x)
-      ro.rec[slot] = make_slot_record(slot, D, off, sp_lds, act_lds, w_lds, M, k, E, ro.has_shared);
+      ro.rec[slot] = small_slot_record(L, slot, M, k, E, ro.has_shared);
 }
 
 hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias,

@@ -171,64 +171,100 @@ __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nsl
                                     ro.has_shared);
 }
 
-// LDS of wave_sort_small<C>: two arrays of 64*C + 1 ints.
-__host__ __device__ constexpr int wave_sort_lds_ints(int C) { return 2 * (kWave * C + 1); }
+// LDS state of the small sort (decode batches): MAXP pairs at most, E <= 64*C.
+// Lane l owns experts [l*C, l*C + C) of the per-expert arrays and moves them
+// with 16-byte accesses (a 4-byte access at a stride of C words would hit a
+// few banks only).  Index kSink of the per-pair arrays absorbs the writes of
+// lanes with nothing to write.
+template <int C, int MAXP>
+struct SmallSortLds {
+  static constexpr int kExp = kWave * C;   // experts covered (>= E)
+  static constexpr int kSink = MAXP;
+  __align__(16) int cur[kExp + 4];          // histogram, then running positions; [kExp] = sink
+  __align__(16) int off[kExp + 4];          // exclusive offsets; off[E] = valid pairs
+  __align__(16) int pslot[kExp + 4];        // active experts below each expert
+  int ids[MAXP];                            // input: expert of each pair
+  float w[MAXP];                            // input: routing weight of each pair
+  int tok[MAXP];                            // input: token of each pair
+  int sp[MAXP + 1];                         // sorted pairs
+  int stok[MAXP + 1];                       // their tokens
+  float sw[MAXP + 1];                       // their weights
+  int act[MAXP];                            // active experts in increasing order
+  int act_beg[MAXP];                        // first sorted position of each
+  int act_n[MAXP];                          // pairs of each
+  int na;                                   // active experts
+  int nvalid;                               // pairs with a valid expert
+};
 
-// Stable counting sort of N pairs (expert ids in LDS) by one wave, for the
-// small batches of decode (E <= 64*C).  Lane l owns experts [l*C, l*C + C):
-// histogram with LDS atomics, per-lane scan of its counts, one wave scan of
-// the lane totals; then pairs are placed 64 at a time in order, a pair's rank
-// among equal experts of its step coming from one ballot per expert-id bit.
-// Leaves in LDS: off[0..E] exclusive offsets (off[E] = valid pairs), sp =
-// sorted pairs, act = active experts in increasing order, *na = their number.
-// `lds` holds wave_sort_lds_ints(C) ints; off points into it.
-template <int C>
-__device__ inline void wave_sort_small(const int* ids, int N, int E, int ebits, int* lds, int*& off, int* sp,
-                                       int* act, int* na) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int* cur = lds;                       // histogram, then running positions
-  off = lds + kWave * C + 1;
-#pragma unroll
-  for (int i = 0; i < C; ++i) cur[lane * C + i] = 0;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  for (int p = lane; p < N; p += kWave) {
-    const int e = ids[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cur[e], 1);     // invalid ids are dropped
-  }
+__device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Stable counting sort of the N pairs in L.ids by one wave (N <= MAXP).  Lane
+// l owns experts [l*C, l*C + C): histogram with LDS atomics, a per-lane scan
+// of its counts, one wave scan of (count, present) packed in one int; pairs
+// are then placed 64 at a time in order, a pair's rank among equal experts of
+// its step coming from one ballot per expert-id bit, and the first pair of
+// each expert writes its active-list entry.  Fills every other field of L.
+template <int C, int MAXP>
+__device__ inline void wave_sort_small(SmallSortLds<C, MAXP>& L, int N, int E, int ebits) {
+  using S = SmallSortLds<C, MAXP>;
+  static_assert(C % 4 == 0 && MAXP < 65536 && S::kExp < 65536, "packed scan");
+  const int lane = threadIdx.x & (kWave - 1);
+  int4* cur4 = reinterpret_cast<int4*>(&L.cur[lane * C]);
+#pragma unroll
+  for (int i = 0; i < C / 4; ++i) cur4[i] = make_int4(0, 0, 0, 0);
+  wave_lds_fence();
+  for (int base = 0; base < N; base += kWave) {
+    const int p = base + lane;
+    const int e = L.ids[min(p, N - 1)];
+    const bool valid = p < N && (unsigned)e < (unsigned)E;        // invalid ids are dropped
+    atomicAdd(&L.cur[valid ? e : S::kExp], 1);
+  }
+  wave_lds_fence();
   int c[C], tot = 0, pres = 0;
 #pragma unroll
-  for (int i = 0; i < C; ++i) {
-    c[i] = cur[lane * C + i];
-    tot += c[i];
-    pres += c[i] > 0;
+  for (int i = 0; i < C / 4; ++i) {
+    const int4 v = cur4[i];
+    c[4 * i] = v.x; c[4 * i + 1] = v.y; c[4 * i + 2] = v.z; c[4 * i + 3] = v.w;
   }
-  const int tinc = wave_inclusive_scan(tot), pinc = wave_inclusive_scan(pres);
-  int run = tinc - tot, slot = pinc - pres;
 #pragma unroll
-  for (int i = 0; i < C; ++i) {
-    const int x = lane * C + i;
-    if (x < E) {
-      off[x] = run;
-      cur[x] = run;
-      if (c[i] > 0) act[slot++] = x;
-    }
+  for (int i = 0; i < C; ++i) { tot += c[i]; pres += c[i] > 0; }
+  const int packed = tot | (pres << 16);
+  const int inc = wave_inclusive_scan(packed);
+  const int all = __builtin_amdgcn_readlane(inc, kWave - 1);
+  int run = (inc - packed) & 0xFFFF, slot = (inc - packed) >> 16;
+  int o[C], ps[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {     // experts past E have no pairs: their offset is the total
+    o[i] = run;
+    ps[i] = slot;
     run += c[i];
+    slot += c[i] > 0;
   }
-  if (lane == kWave - 1) {
-    off[E] = tinc;                      // valid pairs
-    *na = pinc;
+  int4* off4 = reinterpret_cast<int4*>(&L.off[lane * C]);
+  int4* ps4 = reinterpret_cast<int4*>(&L.pslot[lane * C]);
+#pragma unroll
+  for (int i = 0; i < C / 4; ++i) {
+    const int4 v = make_int4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
+    off4[i] = v;
+    cur4[i] = v;
+    ps4[i] = make_int4(ps[4 * i], ps[4 * i + 1], ps[4 * i + 2], ps[4 * i + 3]);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+  if (lane == 0) {
+    L.off[S::kExp] = all & 0xFFFF;  // covers E == kExp
+    L.na = all >> 16;
+    L.nvalid = all & 0xFFFF;
+  }
+  wave_lds_fence();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   for (int base = 0; base < N; base += kWave) {
     const int p = base + lane;
-    int e = (p < N) ? ids[p] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    if (!valid) e = 0;
+    const int pc = min(p, N - 1);
+    const int e0 = L.ids[pc];
+    const bool valid = p < N && (unsigned)e0 < (unsigned)E;
+    const int e = valid ? e0 : 0;
     uint64_t match = __ballot(valid);
     for (int b = 0; b < ebits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -236,24 +272,71 @@ __device__ inline void wave_sort_small(const int* ids, int N, int E, int ebits, 
       match &= bit ? bal : ~bal;
     }
     const int rank = __popcll(match & lt_mask);
-    if (valid) sp[cur[e] + rank] = p;
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (valid && rank == 0) cur[e] += __popcll(match);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    const int pos = L.cur[e] + rank;
+    const int d = valid ? pos : S::kSink;
+    L.sp[d] = p;
+    L.stok[d] = L.tok[pc];
+    L.sw[d] = L.w[pc];
+    if (valid && pos == L.off[e]) {   // first pair of its expert
+      const int sl = L.pslot[e];
+      L.act[sl] = e;
+      L.act_beg[sl] = pos;
+      L.act_n[sl] = L.off[e + 1] - pos;
+    }
+    if (base + kWave < N) {         // later steps start after this step's pairs
+      wave_lds_fence();
+      const bool lead = valid && rank == 0;
+      atomicAdd(&L.cur[lead ? e : S::kExp], lead ? __popcll(match) : 0);
+      wave_lds_fence();
+    }
   }
 }
 
-// Copy a sort kept in LDS to the caller's arrays (every thread of the block;
-// after a barrier that follows wave_sort_small).
-__device__ inline void block_store_sort(int E, const int* off, const int* sp, const int* act, int D,
-                                        int* __restrict__ offsets, int* __restrict__ sorted_pairs,
-                                        int* __restrict__ active, int* __restrict__ num_active) {
-  const int nvalid = off[E];
-  for (int i = threadIdx.x; i <= E; i += blockDim.x) offsets[i] = off[i];
-  for (int i = threadIdx.x; i < nvalid; i += blockDim.x) sorted_pairs[i] = sp[i];
-  for (int i = threadIdx.x; i < D; i += blockDim.x) active[i] = act[i];
+// Slot record of `slot` from a small sort (after the barrier that follows it).
+template <int C, int MAXP>
+__device__ __forceinline__ SlotRec small_slot_record(const SmallSortLds<C, MAXP>& L, int slot, int M, int k, int E,
+                                                     int has_shared) {
+  SlotRec r;
+  r.pad[0] = r.pad[1] = r.pad[2] = r.pad[3] = 0;
+  const int D = L.na;
+  if (slot < D) {
+    r.e = L.act[slot];
+    r.pbeg = L.act_beg[slot];
+    r.n = L.act_n[slot];
+    r.hrow0 = r.pbeg;
+#pragma unroll
+    for (int q = 0; q < kRecTokens; ++q) {
+      const int at = r.pbeg + min(q, r.n - 1);
+      r.tok[q] = (q < r.n) ? L.stok[at] : 0;
+      r.w[q] = (q < r.n) ? L.sw[at] : 0.f;
+    }
+  } else if (slot == D && has_shared) {
+    r.e = E; r.pbeg = -1; r.n = M; r.hrow0 = M * k;
+#pragma unroll
+    for (int q = 0; q < kRecTokens; ++q) { r.tok[q] = q < M ? q : 0; r.w[q] = 1.f; }
+  } else {
+    r.e = -1; r.pbeg = -1; r.n = 0; r.hrow0 = 0;
+#pragma unroll
+    for (int q = 0; q < kRecTokens; ++q) { r.tok[q] = 0; r.w[q] = 0.f; }
+  }
+  return r;
+}
+
+// Copy a small sort and the top-k it sorted to the caller's arrays (every
+// thread of the block, after the barrier that follows the sort).
+template <int C, int MAXP>
+__device__ inline void block_store_small_sort(const SmallSortLds<C, MAXP>& L, int N, int E,
+                                              int* __restrict__ topk_ids, float* __restrict__ topk_weights,
+                                              int* __restrict__ offsets, int* __restrict__ sorted_pairs,
+                                              int* __restrict__ active, int* __restrict__ num_active) {
+  const int nvalid = L.nvalid, D = L.na;
+  for (int i = threadIdx.x; i < N; i += blockDim.x) {
+    if (topk_ids) topk_ids[i] = L.ids[i];
+    if (topk_weights) topk_weights[i] = L.w[i];
+  }
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) offsets[i] = L.off[i];
+  for (int i = threadIdx.x; i < nvalid; i += blockDim.x) sorted_pairs[i] = L.sp[i];
+  for (int i = threadIdx.x; i < D; i += blockDim.x) active[i] = L.act[i];
   if (threadIdx.x == 0) *num_active = D;
 }
 

@@ -45,43 +45,65 @@ __device__ __forceinline__ void load_logit_keys(const float* row, int E, uint32_
   }
 }
 
+// Best and second-best key of a lane's entries (first index among equals),
+// skipping entries whose bit is set in `taken`.
+template <int kPer>
+__device__ __forceinline__ void lane_top2(const uint32_t (&val)[kPer], uint32_t taken, uint32_t& b1, int& j1,
+                                          uint32_t& b2, int& j2) {
+  b1 = 0u; b2 = 0u; j1 = 0; j2 = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t v = ((taken >> j) & 1u) ? 0u : val[j];
+    const bool gt1 = v > b1, gt2 = v > b2;
+    b2 = gt1 ? b1 : (gt2 ? v : b2);
+    j2 = gt1 ? j1 : (gt2 ? j : j2);
+    b1 = gt1 ? v : b1;
+    j1 = gt1 ? j : j1;
+  }
+}
+
 // Top-k of one token's logits by one full wave (all 64 lanes active, E <=
 // 64*kPer).  Each round takes the wave maximum of the lanes' best keys; the
 // lowest lane holding it owns the lowest expert index with that value (a
 // lane's experts are contiguous and precede the next lane's, and inside a lane
 // the first of equal keys is kept), so ties go to the lower index with one
-// ballot instead of a second reduction.  The owner drops that entry.  Round
-// i's winner lands in lane i, which returns its expert and the weight
-// exp(l_i - l_0) / sum over the kept experts; other lanes return weight 0.
+// ballot instead of a second reduction.  A lane keeps its two best keys, so
+// the winner just promotes its second; only a lane that wins twice rescans its
+// entries.  Round i's winner lands in lane i, which returns its expert and the
+// weight exp(l_i - l_0) / sum over the kept experts; other lanes return 0.
 template <int kPer>
 __device__ __forceinline__ void wave_topk_softmax(const float* row, int E, int k, int& out_id,
                                                   float& out_w) {
-  static_assert(kPer % 4 == 0, "kPer");
+  static_assert(kPer % 4 == 0 && kPer <= 32, "kPer");
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t val[kPer];
   load_logit_keys<kPer>(row, E, val);
-  uint32_t bv = 0u;
-  int bj = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (val[j] > bv) { bv = val[j]; bj = j; }     // strict: lowest j among equals
+  uint32_t b1, b2, taken = 0u;
+  int j1, j2;
+  lane_top2<kPer>(val, 0u, b1, j1, b2, j2);
+  bool second = true;                 // b2 is still this lane's next-best entry
 
   int my_id = 0;
   uint32_t my_val = 0u, top_val = 0u;
   for (int i = 0; i < k; ++i) {
-    const uint32_t vmax = wave_max_u32(bv);
-    const uint64_t holders = __ballot(bv == vmax);
+    const uint32_t vmax = wave_max_u32(b1);
+    const uint64_t holders = __ballot(b1 == vmax);
     const int wl = (int)__builtin_ctzll(holders);                    // wave-uniform
-    const int wj = __builtin_amdgcn_readlane(bj, wl);
+    const int wj = __builtin_amdgcn_readlane(j1, wl);
     if (i == 0) top_val = vmax;
-    if (lane == i) { my_id = wl * kPer + wj; my_val = vmax; }
-    if (lane == wl) {
-      bv = 0u; bj = 0;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if (j == wj) val[j] = 0u;
-        if (val[j] > bv) { bv = val[j]; bj = j; }
+    my_id = (lane == i) ? wl * kPer + wj : my_id;
+    my_val = (lane == i) ? vmax : my_val;
+    const bool hit = lane == wl;
+    taken |= hit ? (1u << j1) : 0u;
+    if (__ballot(hit && !second)) {   // the winner already used its second: rescan
+      if (hit) {
+        lane_top2<kPer>(val, taken, b1, j1, b2, j2);
+        second = true;
       }
+    } else {
+      b1 = hit ? b2 : b1;
+      j1 = hit ? j2 : j1;
+      second = hit ? false : second;
     }
   }
   const float ex = (lane < k) ? expf(f32_from_orderable(my_val) - f32_from_orderable(top_val)) : 0.f;
