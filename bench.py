@@ -104,6 +104,68 @@ def device_sets(torch, wl, nsets):
     return out
 
 
+def kernel_source_hash():
+    """sha256 over the HIP sources and the header: a traffic figure measured on
+    other sources is stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mxfp4_expert_weight_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "moe_mxfp4.h"), "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary, or None
+    when there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"gateup_kernel_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "|")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def profile_summary(dirs, kernel):
+    """Summarise rocprofv3 csv output directories (kernel stats and per-dispatch
+    counters) as text."""
+    import csv
+    import glob
+    import statistics
+    lines = []
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+            lines.append(f"kernel stats ({os.path.relpath(f, d)}):")
+            lines.append(f"  {'kernel':64s} {'calls':>7s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'%':>6s}")
+            for r in csv.DictReader(open(f)):
+                lines.append(f"  {r['Name'][:64]:64s} {r['Calls']:>7s} {float(r['AverageNs']) / 1e3:9.2f} "
+                             f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                             f"{float(r['Percentage']):6.1f}")
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            per = {}
+            for r in csv.DictReader(open(f)):
+                key = (r["Kernel_Name"], r["Counter_Name"])
+                per.setdefault(key, []).append(float(r["Counter_Value"]))
+            lines.append(f"counters per dispatch ({os.path.relpath(f, d)}):")
+            for (kn, cn), vals in sorted(per.items()):
+                if kernel and kernel not in kn and "elementwise" not in kn and "copy" not in kn.lower():
+                    continue
+                lines.append(f"  {kn[:64]:64s} {cn:12s} n={len(vals):6d} mean={statistics.mean(vals):14.1f} "
+                             f"median={statistics.median(vals):14.1f}")
+    print("\n".join(lines))
+
+
 def cpu_baseline(wl, seconds_budget=20.0):
     """The oracle as it stands, on host-generated sets of the same workload."""
     import numpy as np
@@ -158,7 +220,17 @@ def main():
                     help="time moe_route + moe_sort_by_expert + moe_mxfp4_forward instead of moe_layer")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (reference for rocprof byte counters)")
+    ap.add_argument("--profile-summary", nargs="+", metavar="DIR",
+                    help="print a text summary of rocprofv3 csv output directories and exit")
+    ap.add_argument("--kernel", default="gateup_kernel", help="kernel kept in --profile-summary counters")
+    ap.add_argument("--source-hash", action="store_true", help="print the kernel sources' sha256 and exit")
     args = ap.parse_args()
+    if args.profile_summary:
+        profile_summary(args.profile_summary, args.kernel)
+        return
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -275,7 +347,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "entry": "three calls" if args.three_calls else "moe_layer", "M": wl.M, "hidden": wl.H, "inter": wl.I, "experts": wl.E,
                    "top_k": wl.k, "shared_expert": wl.shared, "routing": wl.routing,
@@ -287,7 +359,7 @@ def main():
         "mean_distinct_experts": sum(D[l] for l in step_sets) / len(step_sets),
         "roofline": {"bound": "hbm", "kernel": "gateup_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(wl.name),
                      "us_per_launch": gu_ms * 1e3, "bytes_per_launch": gu_bytes},
     }
     if not args.no_cpu_baseline:
