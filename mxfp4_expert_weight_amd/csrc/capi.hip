@@ -1,5 +1,7 @@
 // C ABI of the MXFP4 MoE layer: host-side argument checks, then launches.
 // Nothing here allocates, synchronises or keeps state.
+#include <climits>
+
 #include "kernels.h"
 
 using namespace moe;
@@ -27,6 +29,61 @@ moe_status check_inter(int32_t I) {
   return MOE_OK;
 }
 
+// Arguments of the expert stage; the slot records live in the workspace.  The
+// MFMA fields are set when the path is on for these sizes.
+ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                       const float* topk_weights, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                       const int32_t* active_experts, const int32_t* num_active, float* y, void* workspace) {
+  const WorkspaceLayout L = workspace_layout(M, top_k, w->num_experts, w->hidden, w->inter);
+  char* ws = reinterpret_cast<char*>(workspace);
+  ForwardArgs a{};
+  a.x = x;
+  a.w13_q = w->w13_q; a.w13_s = w->w13_s; a.w2_q = w->w2_q; a.w2_s = w->w2_s;
+  a.topk_weights = topk_weights;
+  a.offsets = expert_offsets; a.sorted_pairs = sorted_pairs;
+  a.active = active_experts; a.num_active = num_active;
+  a.y = y;
+  a.hdr = reinterpret_cast<WorkspaceHeader*>(workspace);
+  a.rec = reinterpret_cast<const SlotRec*>(ws + L.rec);
+  a.h = reinterpret_cast<uint16_t*>(ws + L.h);
+  a.M = M; a.k = top_k; a.E = w->num_experts; a.H = w->hidden; a.I = w->inter;
+  a.has_shared = w->has_shared;
+  const bool on = mfma_path(M, a.H, a.I);
+  a.mfma_min = on ? kMfmaMinTokens : INT_MAX;
+  if (on) {
+    a.xq_hi = reinterpret_cast<uint8_t*>(ws + L.xq_hi);
+    a.xq_lo = reinterpret_cast<uint8_t*>(ws + L.xq_lo);
+    a.xq_shi = reinterpret_cast<uint8_t*>(ws + L.xq_shi);
+    a.xq_slo = reinterpret_cast<uint8_t*>(ws + L.xq_slo);
+    a.hq_hi = reinterpret_cast<uint8_t*>(ws + L.hq_hi);
+    a.hq_lo = reinterpret_cast<uint8_t*>(ws + L.hq_lo);
+    a.hq_shi = reinterpret_cast<uint8_t*>(ws + L.hq_shi);
+    a.hq_slo = reinterpret_cast<uint8_t*>(ws + L.hq_slo);
+    a.items = reinterpret_cast<const int2*>(ws + L.items);
+  }
+  return a;
+}
+
+RecOut layer_recout(const ForwardArgs& a, void* workspace) {
+  return RecOut{const_cast<SlotRec*>(a.rec), a.topk_weights, a.M, a.k, a.has_shared, a.mfma_min,
+                const_cast<int2*>(a.items), reinterpret_cast<WorkspaceHeader*>(workspace)};
+}
+
+// The expert stage: GEMV gate/up (zeroes y) and down for the experts with few
+// tokens; with the MFMA path on, x is quantised first and the dense kernels
+// take the experts listed in the work items.
+hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+  const bool mfma = a.mfma_min == kMfmaMinTokens;
+  hipError_t e = hipSuccess;
+  if (mfma && (e = launch_forward_mfma_front(a, s)) != hipSuccess) return e;
+  if ((e = launch_forward(a, s, start, stop)) != hipSuccess) return e;
+  if (mfma) {
+    if ((e = launch_gateup_mfma(a, s)) != hipSuccess) return e;
+    if ((e = launch_down_mfma(a, s)) != hipSuccess) return e;
+  }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -47,7 +104,7 @@ size_t moe_workspace_bytes(int32_t M, int32_t top_k, int32_t E, int32_t H, int32
   if (check_route_sizes(M, E, top_k) != MOE_OK || check_hidden(H) != MOE_OK ||
       check_inter(I) != MOE_OK)
     return 0;
-  return workspace_bytes(M, top_k, E, I);
+  return workspace_layout(M, top_k, E, H, I).total;
 }
 
 moe_status moe_route(const uint16_t* x, const float* w_router, const float* logit_bias,
@@ -102,46 +159,21 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int3
   if (!aligned16(x) || !aligned16(w->w13_q) || !aligned16(w->w13_s) || !aligned16(w->w2_q) ||
       !aligned16(w->w2_s) || ((uintptr_t)workspace & 255u))
     return MOE_ERR_ALIGN;
-  if (workspace_bytes_ < workspace_bytes(M, top_k, w->num_experts, w->inter)) return MOE_ERR_WORKSPACE;
-
-  ForwardArgs a;
-  a.x = x;
-  a.w13_q = w->w13_q; a.w13_s = w->w13_s; a.w2_q = w->w2_q; a.w2_s = w->w2_s;
-  a.topk_weights = topk_weights;
-  a.offsets = expert_offsets; a.sorted_pairs = sorted_pairs;
-  a.active = active_experts; a.num_active = num_active;
-  a.y = y;
-  a.hdr = reinterpret_cast<WorkspaceHeader*>(workspace);
-  a.h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) +
-                                    workspace_h_offset(M, top_k, w->num_experts));
-  a.rec = nullptr;
-  a.M = M; a.k = top_k; a.E = w->num_experts; a.H = w->hidden; a.I = w->inter;
-  a.has_shared = w->has_shared;
-  return hip_status(launch_forward(a, (hipStream_t)stream));
+  if (workspace_bytes_ < workspace_layout(M, top_k, w->num_experts, w->hidden, w->inter).total)
+    return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
+                             num_active, y, workspace);
+  if (a.mfma_min == kMfmaMinTokens) {
+    // the path choice needs per-expert token counts: records (and MFMA items) first
+    const RecOut ro = layer_recout(a, workspace);
+    if (launch_records(expert_offsets, sorted_pairs, active_experts, num_active, a.E, ro, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else {
+    a.rec = nullptr;                 // few tokens: resolved from the sort outputs directly
+  }
+  return hip_status(launch_experts(a, s, nullptr, nullptr));
 }
-
-namespace {
-
-ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
-                       const float* topk_weights, const int32_t* expert_offsets, const int32_t* sorted_pairs,
-                       const int32_t* active_experts, const int32_t* num_active, float* y, void* workspace) {
-  ForwardArgs a;
-  a.x = x;
-  a.w13_q = w->w13_q; a.w13_s = w->w13_s; a.w2_q = w->w2_q; a.w2_s = w->w2_s;
-  a.topk_weights = topk_weights;
-  a.offsets = expert_offsets; a.sorted_pairs = sorted_pairs;
-  a.active = active_experts; a.num_active = num_active;
-  a.y = y;
-  a.hdr = reinterpret_cast<WorkspaceHeader*>(workspace);
-  a.rec = reinterpret_cast<const SlotRec*>(reinterpret_cast<char*>(workspace) + workspace_rec_offset());
-  a.h = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(workspace) +
-                                    workspace_h_offset(M, top_k, w->num_experts));
-  a.M = M; a.k = top_k; a.E = w->num_experts; a.H = w->hidden; a.I = w->inter;
-  a.has_shared = w->has_shared;
-  return a;
-}
-
-}  // namespace
 
 moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float* logit_bias,
                            int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
@@ -163,14 +195,14 @@ moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(w->w13_q) || !aligned16(w->w13_s) ||
       !aligned16(w->w2_q) || !aligned16(w->w2_s) || ((uintptr_t)workspace & 255u))
     return MOE_ERR_ALIGN;
-  if (workspace_bytes_ < workspace_bytes(M, top_k, w->num_experts, w->inter)) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes_ < workspace_layout(M, top_k, E, H, w->inter).total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (launch_router_logits(x, w_router, logit_bias, logit_bias ? bias_row_stride : 0, M, H, E, logits,
                            s) != hipSuccess)
     return MOE_ERR_HIP;
   ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
                              num_active, y, workspace);
-  SlotRec* rec = reinterpret_cast<SlotRec*>(reinterpret_cast<char*>(workspace) + workspace_rec_offset());
+  SlotRec* rec = const_cast<SlotRec*>(a.rec);
   hipEvent_t start = (hipEvent_t)start_event, stop = (hipEvent_t)stop_event;
   if (M <= kRoutedMaxTokens) {
     // decode: every gate/up block routes itself from the logits
@@ -178,7 +210,7 @@ moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float
                      num_active, rec, expert_bits(E)};
     return hip_status(launch_forward_routed(a, r, s, start, stop));
   }
-  const RecOut ro{rec, topk_weights, M, top_k, w->has_shared};
+  const RecOut ro = layer_recout(a, workspace);
   hipError_t e;
   if (topk_sort_fits_one_block(M)) {
     e = launch_topk_sort_small(logits, M, E, top_k, topk_ids, topk_weights, expert_offsets,
@@ -190,7 +222,7 @@ moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float
                                 num_active, s, ro);
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(launch_forward(a, s, start, stop));
+  return hip_status(launch_experts(a, s, start, stop));
 }
 
 moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logit_bias,

@@ -119,7 +119,8 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 struct WorkspaceHeader {
   int32_t gemv_experts;   // expert passes on the VALU GEMV path in the last call
   int32_t mfma_experts;   // expert passes on the MFMA path in the last call
-  int32_t reserved[62];
+  int32_t mfma_items;     // (expert slot, token tile) work items of the MFMA kernels
+  int32_t reserved[61];
 };
 static_assert(sizeof(WorkspaceHeader) == 256, "header size");
 

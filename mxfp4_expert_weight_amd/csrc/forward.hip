@@ -64,6 +64,7 @@ __device__ __forceinline__ bool route_in_block(const ForwardArgs& a, const Route
     if (threadIdx.x == 0) {
       a.hdr->gemv_experts = L.na + a.has_shared;        // every expert runs on this path
       a.hdr->mfma_experts = 0;
+      a.hdr->mfma_items = 0;
     }
     return false;
   }
@@ -142,11 +143,12 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
   if constexpr (C > 0) {
     if (!route_in_block<C>(a, r, s)) return;             // uniform over the block
   } else {
-    if (!resolve_slot(blockIdx.y, a, s)) return;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-      a.hdr->gemv_experts = *a.num_active + a.has_shared;  // every expert runs on this path
+    if (!a.rec && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+      a.hdr->gemv_experts = *a.num_active + a.has_shared;  // without records: every expert on this path
       a.hdr->mfma_experts = 0;
+      a.hdr->mfma_items = 0;
     }
+    if (!resolve_slot(blockIdx.y, a, s)) return;
   }
   __shared__ uint8_t s_lds[GU_WPB][GU_LDS_PER_WAVE];
   const int wave = threadIdx.x / kWave;

@@ -36,23 +36,68 @@ struct ForwardArgs {
   WorkspaceHeader* hdr;       // workspace header
   const SlotRec* rec;         // slot records, or null (then resolved from the sort outputs)
   int M, k, E, H, I, has_shared;
+  // MFMA path (experts with >= mfma_min tokens; mfma_min = INT_MAX when off)
+  int mfma_min;
+  uint8_t *xq_hi, *xq_lo;     // [M][H] two-term MXFP8 (E4M3) codes of x
+  uint8_t *xq_shi, *xq_slo;   // [M][H/32] their E8M0 scales
+  uint8_t *hq_hi, *hq_lo;     // [M*k + M][I] two-term MXFP8 codes of h (MFMA experts' rows)
+  uint8_t *hq_shi, *hq_slo;   // [M*k + M][I/32]
+  const int2* items;          // MFMA work items (slot, 64-token tile); count in hdr->mfma_items
 };
 
-// Workspace: header | slot records (one per possible active expert + shared) | h.
-__host__ __device__ inline int max_slots(int M, int k, int E) { return (E < M * k ? E : M * k) + 1; }
-inline size_t workspace_rec_offset() { return sizeof(WorkspaceHeader); }
-inline size_t workspace_h_offset(int M, int k, int E) {
-  return workspace_rec_offset() + align_up((size_t)max_slots(M, k, E) * sizeof(SlotRec), 256);
+// The MFMA path: experts with at least kMfmaMinTokens tokens run as dense
+// products on the scaled MXFP4 matrix cores when M reaches that many tokens
+// and both reduction lengths are multiples of the instruction's K.
+constexpr int kMfmaMinTokens = 16;
+constexpr int kMfmaTileTokens = 64;     // tokens per work item
+constexpr int kMfmaK = 128;             // K of one v_mfma_scale_f32_16x16x128_f8f6f4
+inline bool mfma_path(int M, int H, int I) {
+  return M >= kMfmaMinTokens && H % kMfmaK == 0 && I % kMfmaK == 0;
 }
-inline size_t workspace_bytes(int M, int k, int E, int I) {
-  return workspace_h_offset(M, k, E) + align_up((size_t)(M * (size_t)k + M) * I * sizeof(uint16_t), 256);
+// Work items of the MFMA kernels are (slot, tile) pairs: at most
+// ceil(pairs/64) + (number of MFMA experts <= pairs/16) of them.
+__host__ __device__ inline int mfma_max_items(int M, int k) {
+  const int pairs = M * k + M;
+  return (pairs + kMfmaTileTokens - 1) / kMfmaTileTokens + pairs / kMfmaMinTokens + 1;
 }
 
-// Optional epilogue of the sort: slot records for the forward kernels.
+// Workspace: header | slot records (one per possible active expert + shared) |
+// h | (MFMA path only) two-term MXFP8 x, two-term MXFP8 h, MFMA work items.
+__host__ __device__ inline int max_slots(int M, int k, int E) { return (E < M * k ? E : M * k) + 1; }
+struct WorkspaceLayout {
+  size_t rec, h, xq_hi, xq_lo, xq_shi, xq_slo, hq_hi, hq_lo, hq_shi, hq_slo, items, total;
+};
+inline WorkspaceLayout workspace_layout(int M, int k, int E, int H, int I) {
+  WorkspaceLayout w{};
+  const size_t pairs = (size_t)M * k + M;
+  size_t o = sizeof(WorkspaceHeader);
+  auto take = [&o](size_t bytes) { const size_t at = o; o += align_up(bytes, 256); return at; };
+  w.rec = take((size_t)max_slots(M, k, E) * sizeof(SlotRec));
+  w.h = take(pairs * I * sizeof(uint16_t));
+  if (mfma_path(M, H, I)) {
+    w.xq_hi = take((size_t)M * H);
+    w.xq_lo = take((size_t)M * H);
+    w.xq_shi = take((size_t)M * H / 32);
+    w.xq_slo = take((size_t)M * H / 32);
+    w.hq_hi = take(pairs * I);
+    w.hq_lo = take(pairs * I);
+    w.hq_shi = take(pairs * I / 32);
+    w.hq_slo = take(pairs * I / 32);
+    w.items = take((size_t)mfma_max_items(M, k) * sizeof(int2));
+  }
+  w.total = o;
+  return w;
+}
+
+// Optional epilogue of the sort: slot records for the forward kernels, the
+// MFMA work items, and the path counters in the workspace header.
 struct RecOut {
   SlotRec* rec;               // null: no records
   const float* topk_weights;  // [M][k]
   int M, k, has_shared;
+  int mfma_min;               // experts with at least this many tokens go to MFMA
+  int2* items;                // MFMA work items (null when the path is off)
+  WorkspaceHeader* hdr;
 };
 
 // Routing done inside the gate/up kernel (decode batches): where the logits
@@ -86,13 +131,21 @@ hipError_t launch_topk_softmax(const float* logits, int M, int E, int k, int* id
                                hipStream_t s);
 hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int* sorted_pairs,
                                  int* active, int* num_active, hipStream_t s,
-                                 RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0});
+                                 RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0, 0, nullptr, nullptr});
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start = nullptr,
                           hipEvent_t stop = nullptr);
 // Gate/up with the top-k and the expert sort done in every block from the
 // logits (M <= kRoutedMaxTokens), then down.
 hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s,
                                  hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// MFMA path (mfma.hip): two-term MXFP8 quantisation of x, the dense gate/up
+// and down products of the experts listed in the work items.
+hipError_t launch_forward_mfma_front(const ForwardArgs& a, hipStream_t s);   // x quantisation
+hipError_t launch_gateup_mfma(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_down_mfma(const ForwardArgs& a, hipStream_t s);
+// Slot records and MFMA items from the sort outputs (one workgroup).
+hipError_t launch_records(const int* offsets, const int* sorted_pairs, const int* active, const int* num_active,
+                          int E, RecOut ro, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols, float* out,
                           hipStream_t st);
 

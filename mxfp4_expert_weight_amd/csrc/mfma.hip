@@ -1,0 +1,371 @@
+// Dense path for experts with many tokens: the expert products run on the
+// gfx950 scaled matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4) with the
+// MXFP4 weights as the FP4 operand, read straight from their row-major layout
+// with their own E8M0 block scales.  The choice of kernel by problem shape
+// follows the MoE-SpeQ article, section 3.3 (many tokens per expert make the
+// work a dense contraction).
+//
+// The other operand must be FP8/FP6/FP4, so activations are carried as two
+// MXFP8 (E4M3) terms per 32-element block: v ~ hi * 2^sh + lo * 2^sl, where lo
+// encodes the residual of hi.  Each term keeps 4 significant bits, so the
+// pair keeps about 8, and the two products accumulate into one fp32 tile.
+//
+// Operand layout of the instruction (16 x 16 output tile, K = 128), lane l:
+//   FP4 A:   row l%16, K = 32*(l/16) + p for nibble p of 16 bytes (low nibble first)
+//   FP8 B:   column l%16, K = 64*(p/16) + 16*(l/16) + p%16 for byte p of 32 bytes
+//   scales:  byte 0 of lane l's scale register covers row/column l%16 and the
+//            K block [32*(l/16), +32), for both operands
+//   output:  register r of lane l is D[4*(l/16) + r][l%16]
+#include "kernels.h"
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int MF_TT = kMfmaTileTokens;   // tokens per work item (4 sub-tiles of 16)
+constexpr int MF_J = 32;                 // intermediate indices per gate/up workgroup
+constexpr int MF_R = 64;                 // output rows per down workgroup
+constexpr int MF_PITCH = 144;            // LDS bytes per staged 128-element row (+16 spreads banks)
+constexpr int MF_WAVES = 4;
+
+// ------------------------------------------------------- two-term MXFP8 --
+// E8M0 exponent e with amax * 2^-e in [128, 256): the block's largest value
+// uses the top normal binades of E4M3 (max 448) and never saturates.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  return (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 7;
+}
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// Encode 32 fp32 values.  Blocks whose largest value is below 2^-100 encode
+// as zero (scale byte 0).
+__device__ __forceinline__ void encode_two_term(const float (&v)[32], uint32_t (&hi)[8], uint32_t (&lo)[8],
+                                                uint32_t& shi, uint32_t& slo) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  if (!(amax >= 0x1p-100f)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) { hi[q] = 0u; lo[q] = 0u; }
+    shi = slo = 0u;
+    return;
+  }
+  const int e1 = mx_exponent(amax);
+  const float inv1 = pow2f(-e1), sc1 = pow2f(e1);
+  float r[32];
+  float ramax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q] * inv1, v[4 * q + 1] * inv1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * q + 2] * inv1, v[4 * q + 3] * inv1, w, true);
+    hi[q] = (uint32_t)w;
+    // the residual is exact in fp32 (hi * 2^e1 is within a factor 2^-4 of v)
+    r[4 * q + 0] = v[4 * q + 0] - __builtin_amdgcn_cvt_f32_fp8(w, 0) * sc1;
+    r[4 * q + 1] = v[4 * q + 1] - __builtin_amdgcn_cvt_f32_fp8(w, 1) * sc1;
+    r[4 * q + 2] = v[4 * q + 2] - __builtin_amdgcn_cvt_f32_fp8(w, 2) * sc1;
+    r[4 * q + 3] = v[4 * q + 3] - __builtin_amdgcn_cvt_f32_fp8(w, 3) * sc1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ramax = fmaxf(ramax, fabsf(r[4 * q + i]));
+  }
+  shi = (uint32_t)(e1 + 127);
+  if (!(ramax >= 0x1p-100f)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) lo[q] = 0u;
+    slo = 0u;
+    return;
+  }
+  const int e2 = mx_exponent(ramax);
+  const float inv2 = pow2f(-e2);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * q] * inv2, r[4 * q + 1] * inv2, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(r[4 * q + 2] * inv2, r[4 * q + 3] * inv2, w, true);
+    lo[q] = (uint32_t)w;
+  }
+  slo = (uint32_t)(e2 + 127);
+}
+
+// One thread per 32-element block of x [M][H] (bf16).
+__global__ __launch_bounds__(256) void quantize_x_kernel(const uint16_t* __restrict__ x, int M, int H,
+                                                         uint8_t* __restrict__ hi, uint8_t* __restrict__ lo,
+                                                         uint8_t* __restrict__ shi, uint8_t* __restrict__ slo) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nb = (int64_t)M * (H / 32);
+  if (b >= nb) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + b * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = src[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+      v[8 * i + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+    }
+  }
+  uint32_t h[8], l[8], sh, sl;
+  encode_two_term(v, h, l, sh, sl);
+  uint4* dh = reinterpret_cast<uint4*>(hi + b * 32);
+  uint4* dl = reinterpret_cast<uint4*>(lo + b * 32);
+  dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
+  dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
+  dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
+  dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+  shi[b] = (uint8_t)sh;
+  slo[b] = (uint8_t)sl;
+}
+
+// ------------------------------------------------------ staging in LDS --
+// A work item's 64 token rows of one 128-element chunk, both terms, are staged
+// by the 256 threads of the workgroup: thread (row c, quarter q) moves bytes
+// [32q, 32q + 32) of each term and the scale byte of block q.  Rows past the
+// item's tokens are zero.
+struct StageRegs {
+  uint4 h0, h1, l0, l1;
+  uint32_t sh, sl;
+};
+
+__device__ __forceinline__ void stage_load(StageRegs& st, const uint8_t* qhi, const uint8_t* qlo,
+                                           const uint8_t* shi, const uint8_t* slo, int64_t row, bool valid,
+                                           int K, int kc, int q) {
+  const int64_t rr = valid ? row : 0;               // clamped, masked after the load
+  const uint4* ph = reinterpret_cast<const uint4*>(qhi + rr * K + kc * kMfmaK + 32 * q);
+  const uint4* pl = reinterpret_cast<const uint4*>(qlo + rr * K + kc * kMfmaK + 32 * q);
+  const uint4 h0 = ph[0], h1 = ph[1], l0 = pl[0], l1 = pl[1];
+  const uint32_t sh = shi[rr * (K / 32) + kc * 4 + q], sl = slo[rr * (K / 32) + kc * 4 + q];
+  // mask word by word (a select of whole vectors goes through scratch memory)
+  const uint32_t m = valid ? 0xFFFFFFFFu : 0u;
+  st.h0 = make_uint4(h0.x & m, h0.y & m, h0.z & m, h0.w & m);
+  st.h1 = make_uint4(h1.x & m, h1.y & m, h1.z & m, h1.w & m);
+  st.l0 = make_uint4(l0.x & m, l0.y & m, l0.z & m, l0.w & m);
+  st.l1 = make_uint4(l1.x & m, l1.y & m, l1.z & m, l1.w & m);
+  st.sh = sh & m;
+  st.sl = sl & m;
+}
+
+struct __align__(16) StageBuf {
+  uint8_t hi[MF_TT * MF_PITCH];
+  uint8_t lo[MF_TT * MF_PITCH];
+  uint8_t shi[MF_TT * 4];
+  uint8_t slo[MF_TT * 4];
+};
+
+__device__ __forceinline__ void stage_store(StageBuf& b, const StageRegs& st, int c, int q) {
+  uint4* dh = reinterpret_cast<uint4*>(b.hi + c * MF_PITCH + 32 * q);
+  uint4* dl = reinterpret_cast<uint4*>(b.lo + c * MF_PITCH + 32 * q);
+  dh[0] = st.h0; dh[1] = st.h1;
+  dl[0] = st.l0; dl[1] = st.l1;
+  b.shi[c * 4 + q] = (uint8_t)st.sh;
+  b.slo[c * 4 + q] = (uint8_t)st.sl;
+}
+
+// B operand of token sub-tile s for lane (g, j): bytes [16g, +16) and
+// [64 + 16g, +16) of row 16s + j, and the scale of block g of that row.
+__device__ __forceinline__ v8i frag_b(const uint8_t* rows, int s, int g, int j) {
+  const uint8_t* r = rows + (16 * s + j) * MF_PITCH;
+  const uint4 a = *reinterpret_cast<const uint4*>(r + 16 * g);
+  const uint4 b = *reinterpret_cast<const uint4*>(r + 64 + 16 * g);
+  v8i v;
+  v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
+  v[4] = (int)b.x; v[5] = (int)b.y; v[6] = (int)b.z; v[7] = (int)b.w;
+  return v;
+}
+
+// A operand: 16 code bytes of one weight row at K offset 128*kc + 32g.
+__device__ __forceinline__ v8i frag_a(const uint8_t* row_q, int kc, int g) {
+  const uint4 a = *reinterpret_cast<const uint4*>(row_q + kc * (kMfmaK / 2) + 16 * g);
+  v8i v;
+  v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
+  v[4] = 0; v[5] = 0; v[6] = 0; v[7] = 0;
+  return v;
+}
+
+// Expert `rec`, token tile t0..t0+nt: one 16-row x 64-token product per wave
+// over K, both activation terms into the same accumulators.
+__device__ __forceinline__ void mfma_tile(v4f (&acc)[4], const uint8_t* row_q, const uint8_t* row_s,
+                                          const uint8_t* qhi, const uint8_t* qlo, const uint8_t* shi,
+                                          const uint8_t* slo, const int64_t stage_row, bool stage_valid, int K,
+                                          StageBuf (&buf)[2]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane >> 4, j = lane & 15;
+  const int c = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const int nk = K / kMfmaK;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
+  StageRegs st;
+  stage_load(st, qhi, qlo, shi, slo, stage_row, stage_valid, K, 0, q);
+  stage_store(buf[0], st, c, q);
+  v8i a = frag_a(row_q, 0, g);
+  uint32_t sa = row_s[4 * 0 + g];
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int cur = kc & 1;
+    const bool more = kc + 1 < nk;
+    v8i a_next = a;
+    uint32_t sa_next = sa;
+    if (more) {                                    // next chunk in flight during this one's products
+      stage_load(st, qhi, qlo, shi, slo, stage_row, stage_valid, K, kc + 1, q);
+      a_next = frag_a(row_q, kc + 1, g);
+      sa_next = row_s[4 * (kc + 1) + g];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const v8i bh = frag_b(buf[cur].hi, s, g, j);
+      const v8i bl = frag_b(buf[cur].lo, s, g, j);
+      const int sbh = buf[cur].shi[(16 * s + j) * 4 + g];
+      const int sbl = buf[cur].slo[(16 * s + j) * 4 + g];
+      acc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bh, acc[s], 4, 0, 0, (int)sa, 0, sbh);
+      acc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bl, acc[s], 4, 0, 0, (int)sa, 0, sbl);
+    }
+    if (more) stage_store(buf[cur ^ 1], st, c, q);
+    __syncthreads();
+    a = a_next;
+    sa = sa_next;
+  }
+}
+
+// Token index of the expert's token number tt (sorted order).
+__device__ __forceinline__ int item_token(const ForwardArgs& a, const SlotRec& r, int tt) {
+  return r.pbeg >= 0 ? a.sorted_pairs[r.pbeg + tt] / a.k : tt;
+}
+
+// ------------------------------------------------------------- gate/up --
+// Workgroup (32 intermediate indices, items): waves 0-1 take the 32 gate
+// rows, waves 2-3 the 32 up rows, each over the item's 64 tokens.  Epilogue:
+// h = SiLU(g) * u through LDS, then one thread per token encodes its 32
+// h values (one MXFP8 block along the down projection's K) in two terms.
+__global__ __launch_bounds__(MF_WAVES * kWave) void gateup_mfma_kernel(ForwardArgs a) {
+  __shared__ StageBuf buf[2];
+  __shared__ float ul[MF_TT][MF_J + 1];
+  const int n_items = a.hdr->mfma_items;
+  const int j0 = blockIdx.x * MF_J;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int g = lane >> 4, j = lane & 15;
+  const int half = wave & 1, is_up = wave >> 1;
+  const int c = threadIdx.x >> 2;
+  for (int it = blockIdx.y; it < n_items; it += gridDim.y) {
+    const int2 item = a.items[it];
+    const SlotRec rec = a.rec[item.x];
+    const int t0 = item.y * MF_TT;
+    const int nt = min(MF_TT, rec.n - t0);
+    const int64_t row = (int64_t)rec.e * 2 * a.I + (is_up ? a.I : 0) + j0 + 16 * half + j;
+    const uint8_t* row_q = a.w13_q + row * (a.H / 2);
+    const uint8_t* row_s = a.w13_s + row * (a.H / 32);
+    const bool sv = c < nt;
+    const int64_t srow = sv ? item_token(a, rec, t0 + c) : 0;
+    v4f acc[4];
+    mfma_tile(acc, row_q, row_s, a.xq_hi, a.xq_lo, a.xq_shi, a.xq_slo, srow, sv, a.H, buf);
+    // acc[s][r] = (gate or up) row 16*half + 4g + r, token 16s + j
+    if (is_up) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ul[16 * s + j][16 * half + 4 * g + r] = acc[s][r];
+    }
+    __syncthreads();
+    if (!is_up) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jl = 16 * half + 4 * g + r, tc = 16 * s + j;
+          ul[tc][jl] = silu(acc[s][r]) * ul[tc][jl];
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) {
+      const int tc = threadIdx.x;
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = ul[tc][i];
+      uint32_t h[8], l[8], sh, sl;
+      encode_two_term(v, h, l, sh, sl);
+      const int64_t hrow = rec.hrow0 + t0 + tc;
+      uint4* dh = reinterpret_cast<uint4*>(a.hq_hi + hrow * a.I + j0);
+      uint4* dl = reinterpret_cast<uint4*>(a.hq_lo + hrow * a.I + j0);
+      dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
+      dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
+      dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
+      dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+      a.hq_shi[hrow * (a.I / 32) + j0 / 32] = (uint8_t)sh;
+      a.hq_slo[hrow * (a.I / 32) + j0 / 32] = (uint8_t)sl;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- down --
+// Workgroup (64 output rows, items): wave w takes rows 16w..16w+15 over the
+// item's 64 tokens; the epilogue adds w_token * result into y (fp32 atomics,
+// as the GEMV path's combine).
+__global__ __launch_bounds__(MF_WAVES * kWave) void down_mfma_kernel(ForwardArgs a) {
+  __shared__ StageBuf buf[2];
+  const int n_items = a.hdr->mfma_items;
+  const int r0 = blockIdx.x * MF_R;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int g = lane >> 4, j = lane & 15;
+  const int c = threadIdx.x >> 2;
+  for (int it = blockIdx.y; it < n_items; it += gridDim.y) {
+    const int2 item = a.items[it];
+    const SlotRec rec = a.rec[item.x];
+    const int t0 = item.y * MF_TT;
+    const int nt = min(MF_TT, rec.n - t0);
+    const int64_t row = (int64_t)rec.e * a.H + r0 + 16 * wave + j;
+    const uint8_t* row_q = a.w2_q + row * (a.I / 2);
+    const uint8_t* row_s = a.w2_s + row * (a.I / 32);
+    const bool sv = c < nt;
+    const int64_t srow = sv ? (int64_t)rec.hrow0 + t0 + c : 0;
+    v4f acc[4];
+    mfma_tile(acc, row_q, row_s, a.hq_hi, a.hq_lo, a.hq_shi, a.hq_slo, srow, sv, a.I, buf);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int tc = 16 * s + j;
+      if (tc < nt) {
+        int t;
+        float w;
+        if (rec.pbeg >= 0) {
+          const int pair = a.sorted_pairs[rec.pbeg + t0 + tc];
+          t = pair / a.k;
+          w = a.topk_weights[pair];
+        } else {
+          t = t0 + tc;
+          w = 1.f;
+        }
+        float* yr = a.y + (int64_t)t * a.H + r0 + 16 * wave + 4 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unsafeAtomicAdd(yr + r, w * acc[s][r]);
+      }
+    }
+  }
+}
+
+namespace {
+// Rows of persistent workgroups: enough to fill the chip a few times over.
+unsigned item_rows(int row_tiles, int M, int k) {
+  const int want = (4 * 256 + row_tiles - 1) / row_tiles;
+  const int cap = mfma_max_items(M, k);
+  return (unsigned)(want < cap ? (want > 0 ? want : 1) : cap);
+}
+}  // namespace
+
+hipError_t launch_forward_mfma_front(const ForwardArgs& a, hipStream_t s) {
+  const int64_t nb = (int64_t)a.M * (a.H / 32);
+  quantize_x_kernel<<<dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s>>>(a.x, a.M, a.H, a.xq_hi, a.xq_lo,
+                                                                            a.xq_shi, a.xq_slo);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_mfma(const ForwardArgs& a, hipStream_t s) {
+  const int tiles = a.I / MF_J;
+  gateup_mfma_kernel<<<dim3(tiles, item_rows(tiles, a.M, a.k)), dim3(MF_WAVES * kWave), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_mfma(const ForwardArgs& a, hipStream_t s) {
+  const int tiles = a.H / MF_R;
+  down_mfma_kernel<<<dim3(tiles, item_rows(tiles, a.M, a.k)), dim3(MF_WAVES * kWave), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -107,6 +107,11 @@ __global__ __launch_bounds__(64 * kTopkSortMaxTokens) void topk_sort_small_kerne
   if (ro.rec)
     for (int slot = threadIdx.x; slot < max_slots(M, k, E); slot += blockDim.x)
       ro.rec[slot] = small_slot_record(L, slot, M, k, E, ro.has_shared);
+  if (ro.hdr && threadIdx.x == 0) {     // at most 8 tokens per expert: all on the GEMV path
+    ro.hdr->gemv_experts = L.na + ro.has_shared;
+    ro.hdr->mfma_experts = 0;
+    ro.hdr->mfma_items = 0;
+  }
 }
 
 hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias,

@@ -15,8 +15,18 @@ __global__ __launch_bounds__(512) void sort_by_expert_kernel(const int* __restri
   if (ro.rec) {
     __threadfence_block();
     __syncthreads();
-    block_write_slot_records(ro, E, max_slots(ro.M, ro.k, E), offsets, sorted_pairs, active, num_active);
+    block_write_slot_records(ro, E, max_slots(ro.M, ro.k, E), offsets, sorted_pairs, active, num_active, lds);
   }
+}
+
+// Slot records (and MFMA items) from sort outputs already in memory: the
+// expert stage of moe_mxfp4_forward when the MFMA path is on.
+__global__ __launch_bounds__(512) void records_kernel(const int* __restrict__ offsets,
+                                                      const int* __restrict__ sorted_pairs,
+                                                      const int* __restrict__ active,
+                                                      const int* __restrict__ num_active, int E, RecOut ro) {
+  __shared__ int lds[2 * (512 / kWave + 1)];
+  block_write_slot_records(ro, E, max_slots(ro.M, ro.k, E), offsets, sorted_pairs, active, num_active, lds);
 }
 
 int expert_bits(int E) {
@@ -32,6 +42,12 @@ hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int
   const size_t shmem = sizeof(int) * sort_lds_ints(nw, E);
   sort_by_expert_kernel<<<1, nw * kWave, shmem, s>>>(ids, N, E, expert_bits(E), offsets, sorted_pairs,
                                                      active, num_active, ro);
+  return hipGetLastError();
+}
+
+hipError_t launch_records(const int* offsets, const int* sorted_pairs, const int* active, const int* num_active,
+                          int E, RecOut ro, hipStream_t s) {
+  records_kernel<<<1, 512, 0, s>>>(offsets, sorted_pairs, active, num_active, E, ro);
   return hipGetLastError();
 }
 

@@ -159,16 +159,57 @@ __device__ __forceinline__ SlotRec make_slot_record(int slot, int D, const int* 
 }
 
 // Slot records from the finished sort in global memory (this block wrote it
-// and a barrier made it visible): one thread per possible slot.
+// and a barrier made it visible): one thread per possible slot.  Then the
+// path counters in the header and, with the MFMA path on, its work items:
+// (slot, 64-token tile) for every slot with at least ro.mfma_min tokens, in
+// slot order.  `lds` holds 2 * (waves + 1) ints.
 __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nslots,
                                                 const int* __restrict__ offsets,
                                                 const int* __restrict__ sorted_pairs,
                                                 const int* __restrict__ active,
-                                                const int* __restrict__ num_active) {
+                                                const int* __restrict__ num_active, int* lds) {
   const int D = *num_active;
-  for (int slot = threadIdx.x; slot < nslots; slot += blockDim.x)
-    ro.rec[slot] = make_slot_record(slot, D, offsets, sorted_pairs, active, ro.topk_weights, ro.M, ro.k, E,
-                                    ro.has_shared);
+  const int bd = blockDim.x, tid = threadIdx.x;
+  const int per = (nslots + bd - 1) / bd;
+  const int s0 = min(nslots, tid * per), s1 = min(nslots, s0 + per);
+  int tiles = 0, n_mfma = 0, n_gemv = 0;
+  for (int slot = s0; slot < s1; ++slot) {
+    const SlotRec r = make_slot_record(slot, D, offsets, sorted_pairs, active, ro.topk_weights, ro.M, ro.k, E,
+                                       ro.has_shared);
+    ro.rec[slot] = r;
+    if (r.e < 0) continue;
+    if (r.n >= ro.mfma_min) {
+      ++n_mfma;
+      tiles += (r.n + kMfmaTileTokens - 1) / kMfmaTileTokens;
+    } else {
+      ++n_gemv;
+    }
+  }
+  if (!ro.hdr) return;
+  // block-wide exclusive scan of the tile counts (thread spans are in slot order)
+  const int lane = tid & (kWave - 1), w = tid / kWave, nw = bd / kWave;
+  const int packed_c = n_mfma | (n_gemv << 16);
+  const int inc = wave_inclusive_scan(tiles);
+  const int cinc = wave_inclusive_scan(packed_c);
+  if (lane == kWave - 1) { lds[w] = inc; lds[nw + 1 + w] = cinc; }
+  __syncthreads();
+  int base = inc - tiles, call = 0;
+  for (int v = 0; v < nw; ++v) {
+    if (v < w) base += lds[v];
+    call += lds[nw + 1 + v];
+  }
+  if (ro.items) {
+    for (int slot = s0; slot < s1; ++slot) {
+      const SlotRec r = ro.rec[slot];
+      if (r.e < 0 || r.n < ro.mfma_min) continue;
+      for (int t = 0; t * kMfmaTileTokens < r.n; ++t) ro.items[base++] = make_int2(slot, t);
+    }
+  }
+  if (tid == bd - 1) {
+    ro.hdr->mfma_items = ro.items ? base : 0;
+    ro.hdr->mfma_experts = call & 0xFFFF;
+    ro.hdr->gemv_experts = call >> 16;
+  }
 }
 
 // LDS state of the small sort (decode batches): MAXP pairs at most, E <= 64*C.

@@ -29,6 +29,15 @@ def _run(torch, ls, fused=True):
     return out, d, b
 
 
+def expected_mfma_experts(wl, r):
+    """Experts with at least 16 tokens run on the matrix cores when M >= 16 and
+    H and I are multiples of 128 (the instruction's K)."""
+    if wl.M < 16 or wl.H % 128 or wl.I % 128:
+        return 0
+    counts = np.bincount(r["ids"].ravel(), minlength=wl.E)
+    return int(np.sum(counts >= 16)) + int(wl.shared and wl.M >= 16)
+
+
 def _check_full(torch, ls, what, fused=True):
     wl = ls.wl
     say(f"layer {what}: M={wl.M} H={wl.H} I={wl.I} E={wl.E} k={wl.k} shared={wl.shared} {wl.routing} "
@@ -44,7 +53,8 @@ def _check_full(torch, ls, what, fused=True):
     assert_layer_close(g["y"][keep], r["y"][keep], rms, what)
     if not amb:
         assert g["num_active"] == r["num_active"]
-        assert g["hdr"]["gemv_experts"] == r["num_active"] + int(wl.shared)
+        assert g["hdr"]["gemv_experts"] + g["hdr"]["mfma_experts"] == r["num_active"] + int(wl.shared)
+        assert g["hdr"]["mfma_experts"] == expected_mfma_experts(wl, r)
     assert len(amb) <= max(1, wl.M // 50), f"{what}: {len(amb)} ambiguous tokens"
     return g, r
 
@@ -67,6 +77,9 @@ def test_tiny_config_every_element(fused):
     (8, 64, 32, 600, 9, False, "plain"),     # 72 pairs: block sort; E > 512 top-k
     (2, 64, 32, 1024, 32, True, "plain"),    # largest E and k
     (4, 64, 32, 1024, 32, True, "plain"),    # 128 pairs routed inside the gate/up blocks
+    (40, 256, 128, 4, 2, True, "plain"),     # matrix-core path: every expert has >= 16 tokens
+    (130, 384, 256, 3, 2, True, "plain"),    # matrix-core path: ragged 64-token tiles
+    (24, 256, 128, 12, 2, True, "zipf"),     # both paths in one layer
 ])
 def test_edge_shapes_every_element(M, H, I, E, k, shared, routing):
     torch = need_gpu()
@@ -106,7 +119,9 @@ def test_ling_batch_sampled_tokens(name, tokens):
     # every token's output is finite and the dedup covers every routed pair
     assert np.all(np.isfinite(g["y"]))
     D = len(np.unique(g["ids"]))
-    assert g["num_active"] == D and g["hdr"]["gemv_experts"] == D + 1
+    counts = np.bincount(g["ids"].ravel(), minlength=wl.E)
+    assert g["num_active"] == D and g["hdr"]["gemv_experts"] + g["hdr"]["mfma_experts"] == D + 1
+    assert g["hdr"]["mfma_experts"] == int(np.sum(counts >= 16)) + 1     # + the shared expert (M >= 16)
 
 
 def test_token_independence_m4_vs_m1():
