@@ -65,6 +65,135 @@ __global__ __launch_bounds__(128) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// Batches: a tiled fp32 GEMM.  Workgroup = 32 tokens x TE experts, thread
+// (ty, tx) of 16 x 16 owns tokens {ty, ty + 16} and experts {tx + 16 j}.
+// K runs in 128-element chunks staged in LDS (x widened to fp32), double
+// buffered, so each memory round trip carries 4 KB per thread row group.
+// Each logit is summed in 16-product leaves, 16 leaves per group, then the
+// groups in order: the longest chain of fp32 roundings is
+// 16 + 16 + ceil(H/256) + 1 (bias), 43 at H = 2560 -- no longer than the
+// small-batch kernel's H/64 + 6 + 1.
+constexpr int RG_TT = 32, RG_KC = 128, RG_PITCH = RG_KC + 4;
+template <int TE>
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ w_router,
+                                                          const float* __restrict__ bias, int64_t bias_stride,
+                                                          int M, int H, int E, float* __restrict__ logits) {
+  constexpr int NE = TE / 16;
+  constexpr int WQ = TE * RG_KC / 4 / 256;      // float4s of W each thread stages per chunk
+  __shared__ __align__(16) float xs[2][RG_TT][RG_PITCH];
+  __shared__ __align__(16) float wsh[2][TE][RG_PITCH];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int t0 = blockIdx.y * RG_TT, e0 = blockIdx.x * TE;
+  // x staging: thread -> row tid/8, 16 bf16 at column (tid%8)*16
+  const int xr_row = tid >> 3, xr_col = (tid & 7) * 16;
+  const bool xv = t0 + xr_row < M;
+  const uint4* xsrc = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + xr_row, M - 1) * H + xr_col);
+  // W staging: float4 number q = tid + 256 i of the TE x 128 tile: row q/32, column (q%32)*4
+  const float4* wsrc[WQ];
+  bool wv[WQ];
+#pragma unroll
+  for (int i = 0; i < WQ; ++i) {
+    const int q = tid + 256 * i, row = q >> 5;
+    wv[i] = e0 + row < E;
+    wsrc[i] = reinterpret_cast<const float4*>(w_router + (size_t)min(e0 + row, E - 1) * H + (q & 31) * 4);
+  }
+  float tot[2][NE], grp[2][NE];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NE; ++j) { tot[i][j] = 0.f; grp[i][j] = 0.f; }
+  const int nk = H / RG_KC;
+  const int ktail = H - nk * RG_KC;              // < 128, multiple of 32: a last, partial chunk
+  const int nchunks = nk + (ktail ? 1 : 0);
+  uint4 xr0, xr1;
+  float4 wr[WQ];
+  auto load = [&](int kc) {
+    const int kbase = kc * RG_KC;
+    // columns past H read a clamped in-row address and are zeroed when staged
+    const int off = min(kbase + xr_col, H - 16);
+    xr0 = xsrc[(off - xr_col) / 8];
+    xr1 = xsrc[(off - xr_col) / 8 + 1];
+#pragma unroll
+    for (int i = 0; i < WQ; ++i) {
+      const int q = tid + 256 * i, col = (q & 31) * 4;
+      wr[i] = wsrc[i][(min(kbase + col, H - 4) - col) / 4];
+    }
+  };
+  auto store = [&](int buf, int kc) {
+    const int kbase = kc * RG_KC;
+    const bool in = xv && kbase + xr_col < H;
+    const uint32_t w8[8] = {xr0.x, xr0.y, xr0.z, xr0.w, xr1.x, xr1.y, xr1.z, xr1.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float4 f = in ? make_float4(bf16_bits_to_f32(w8[2 * h] & 0xFFFFu), bf16_bits_to_f32(w8[2 * h] >> 16),
+                                        bf16_bits_to_f32(w8[2 * h + 1] & 0xFFFFu),
+                                        bf16_bits_to_f32(w8[2 * h + 1] >> 16))
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(&xs[buf][xr_row][xr_col + 4 * h]) = f;
+    }
+#pragma unroll
+    for (int i = 0; i < WQ; ++i) {
+      const int q = tid + 256 * i, row = q >> 5, col = (q & 31) * 4;
+      *reinterpret_cast<float4*>(&wsh[buf][row][col]) =
+          (wv[i] && kbase + col < H) ? wr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load(0);
+  store(0, 0);
+  __syncthreads();
+  int leaves = 0;
+  for (int kc = 0; kc < nchunks; ++kc) {
+    const int cur = kc & 1;
+    if (kc + 1 < nchunks) load(kc + 1);
+    const int klen = (kc < nk) ? RG_KC : ktail;
+    for (int k0 = 0; k0 < klen; k0 += 16) {       // one 16-product leaf per step
+      float leaf[2][NE];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NE; ++j) leaf[i][j] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 16; kk += 4) {
+        const float4 a0 = *reinterpret_cast<const float4*>(&xs[cur][ty][k0 + kk]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&xs[cur][ty + 16][k0 + kk]);
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+          const float4 b = *reinterpret_cast<const float4*>(&wsh[cur][tx + 16 * j][k0 + kk]);
+          leaf[0][j] = fmaf(a0.x, b.x, leaf[0][j]); leaf[0][j] = fmaf(a0.y, b.y, leaf[0][j]);
+          leaf[0][j] = fmaf(a0.z, b.z, leaf[0][j]); leaf[0][j] = fmaf(a0.w, b.w, leaf[0][j]);
+          leaf[1][j] = fmaf(a1.x, b.x, leaf[1][j]); leaf[1][j] = fmaf(a1.y, b.y, leaf[1][j]);
+          leaf[1][j] = fmaf(a1.z, b.z, leaf[1][j]); leaf[1][j] = fmaf(a1.w, b.w, leaf[1][j]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NE; ++j) grp[i][j] += leaf[i][j];
+      if (++leaves == 16) {                        // a group is 16 leaves
+        leaves = 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < NE; ++j) { tot[i][j] += grp[i][j]; grp[i][j] = 0.f; }
+      }
+    }
+    if (kc + 1 < nchunks) store(cur ^ 1, kc + 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+      const int t = t0 + ty + 16 * i, e = e0 + tx + 16 * j;
+      if (t < M && e < E) {
+        float v = tot[i][j] + grp[i][j];
+        if (bias) v += bias[(size_t)t * bias_stride + e];
+        logits[(size_t)t * E + e] = v;
+      }
+    }
+}
+
 // One wave per token.
 template <int C>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int M, int E,
@@ -117,6 +246,17 @@ __global__ __launch_bounds__(64 * kTopkSortMaxTokens) void topk_sort_small_kerne
 hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias,
                                 int64_t bias_stride, int M, int H, int E, float* logits,
                                 hipStream_t s) {
+  if (M >= kRouterGemmMinTokens) {
+    const int tt = (M + RG_TT - 1) / RG_TT;
+    if (M >= 256) {
+      router_gemm_kernel<32><<<dim3((E + 31) / 32, tt), dim3(256), 0, s>>>(x, w_router, bias, bias_stride, M, H,
+                                                                           E, logits);
+    } else {
+      router_gemm_kernel<16><<<dim3((E + 15) / 16, tt), dim3(256), 0, s>>>(x, w_router, bias, bias_stride, M, H,
+                                                                           E, logits);
+    }
+    return hipGetLastError();
+  }
   const int waves_per_block = 2;
   dim3 grid((E + waves_per_block - 1) / waves_per_block), block(waves_per_block * kWave);
   if (H <= 2560) {

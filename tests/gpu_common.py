@@ -37,15 +37,25 @@ def assert_layer_close(y_gpu: np.ndarray, y_ref: np.ndarray, rms: float | None =
     return ratio
 
 
-def logit_error_bound(x_f64, w_router, bias, H):
-    """Bound on |fp32 router logit - exact logit|.  The kernel accumulates each
-    lane's ceil(H/256) float4s (4 fmas each) sequentially, then a 6-level wave
-    tree, then adds the bias: at most H/64 + 8 roundings of relative size u on
-    partial sums bounded by sum |x_i w_i| (+ |bias|)."""
+def router_rounding_chain(H, M):
+    """Longest chain of fp32 roundings in a router logit.  Batches below 64
+    tokens: each lane sums ceil(H/256) float4s (4 fmas each) in order, a
+    6-level wave tree follows, then the bias: H/64 + 8.  Larger batches (the
+    tiled GEMM): 16-product leaves, 16 leaves per group, the groups in order,
+    then the bias: 16 + 16 + ceil(H/256) + 2."""
+    if M < 64:
+        return H / 64 + 8
+    return 16 + 16 + -(-H // 256) + 2
+
+
+def logit_error_bound(x_f64, w_router, bias, H, M):
+    """Bound on |fp32 router logit - exact logit| for a launch over M tokens:
+    the rounding chain times u on partial sums bounded by sum |x_i w_i|
+    (+ |bias|)."""
     S = np.abs(x_f64) @ np.abs(np.asarray(w_router, np.float64)).T
     if bias is not None:
         S = S + np.abs(np.asarray(bias, np.float64))
-    return (H / 64 + 8) * U * S * 1.01
+    return router_rounding_chain(H, M) * U * S * 1.01
 
 
 def check_routing(ids_gpu, w_gpu, logits_gpu, ref_logits, bound, k, what=""):

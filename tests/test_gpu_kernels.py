@@ -1,11 +1,12 @@
 """GPU parity of the integer and exact steps, element by element against the
 oracle: MXFP4 dequantisation (bit-exact), top-k ids (exact) with their
-weights, and the stable sort by expert (exact)."""
+weights, the stable sort by expert (exact), and the router logits (within the
+fp32 error bound of each kernel's accumulation order)."""
 import numpy as np
 import pytest
 
 import oracle
-from gpu_common import U, need_gpu, say
+from gpu_common import U, check_routing, logit_error_bound, need_gpu, say
 from mxfp4_expert_weight_amd import binding as B, synth
 from mxfp4_expert_weight_amd.layer import to_device
 
@@ -122,3 +123,41 @@ def test_sort_by_expert_exact(M, k, E, dist):
     assert np.array_equal(pairs, r_pairs)
     assert np.array_equal(act[:D], r_act)
     assert np.all(act[D:] == -7)          # entries past D are left untouched
+
+
+# ----------------------------------------------------------------- router --
+
+@pytest.mark.parametrize("M,H,E,k,bias", [
+    (1, 2560, 512, 8, None),        # one wave per expert row, one token
+    (4, 2560, 512, 8, "rows"),      # up to 4 tokens per pass, per-token bias
+    (15, 224, 77, 3, None),         # ragged E
+    (63, 2560, 512, 8, "experts"),  # largest batch of the wave kernel
+    (64, 2560, 512, 8, "experts"),  # smallest batch of the tiled GEMM, 16-expert tiles
+    (65, 96, 40, 5, None),          # ragged token tile (65 = 2*32 + 1), one partial K chunk
+    (300, 8192, 1000, 8, None),     # 32-expert tiles, ragged E, longest H
+    (512, 2560, 512, 8, None),      # the chunked-prefill router
+])
+def test_router_logits_and_routing(M, H, E, k, bias):
+    torch = need_gpu()
+    say(f"router M={M} H={H} E={E} k={k} bias={bias}")
+    rng = np.random.default_rng(M * 7 + H)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    w = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    b = None
+    stride = 0
+    if bias == "rows":
+        b = rng.standard_normal((M, E)).astype(np.float32)
+        stride = E
+    elif bias == "experts":
+        b = rng.standard_normal(E).astype(np.float32)
+    logits = torch.empty((M, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((M, k), dtype=torch.float32, device="cuda")
+    B.moe_route(to_device(x), to_device(w), None if b is None else to_device(b), stride, M, H, E, k, logits,
+                ids, wts)
+    torch.cuda.synchronize()
+    xf = oracle.bf16_bits_to_f64(x)
+    ref = oracle.router_logits(xf, w, b)
+    bound = logit_error_bound(xf, w, b, H, M)
+    check_routing(ids.cpu().numpy(), wts.cpu().numpy(), logits.cpu().numpy(), ref, bound, k,
+                  f"router M={M}")

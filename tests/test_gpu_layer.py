@@ -46,7 +46,7 @@ def _check_full(torch, ls, what, fused=True):
     r = oracle.moe_layer(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s,
                          wl.k, wl.shared)
     xf = oracle.bf16_bits_to_f64(ls.x_bits)
-    bound = logit_error_bound(xf, ls.w_router, ls.bias, wl.H)
+    bound = logit_error_bound(xf, ls.w_router, ls.bias, wl.H, wl.M)
     amb = check_routing(g["ids"], g["w"], g["logits"], r["logits"], bound, wl.k, what)
     keep = np.setdiff1d(np.arange(wl.M), amb)
     rms = float(np.sqrt(np.mean(r["y"] ** 2)))
@@ -110,7 +110,7 @@ def test_ling_batch_sampled_tokens(name, tokens):
                                 ls.w2_q, ls.w2_s, wl.k, wl.shared)
     xf = oracle.bf16_bits_to_f64(ls.x_bits[tokens])
     b = ls.bias if ls.bias is None or ls.bias.ndim == 1 else ls.bias[tokens]
-    bound = logit_error_bound(xf, ls.w_router, b, wl.H)
+    bound = logit_error_bound(xf, ls.w_router, b, wl.H, wl.M)
     amb = check_routing(g["ids"][tokens], g["w"][tokens], g["logits"][tokens], r["logits"], bound,
                         wl.k, name)
     keep = [i for i in range(len(tokens)) if i not in amb]
