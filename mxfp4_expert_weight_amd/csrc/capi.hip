@@ -48,6 +48,9 @@ ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
   a.h = reinterpret_cast<uint16_t*>(ws + L.h);
   a.M = M; a.k = top_k; a.E = w->num_experts; a.H = w->hidden; a.I = w->inter;
   a.has_shared = w->has_shared;
+  const bool mt = mt_path(M, a.H, a.I);
+  a.mt_min = mt ? kMtMinTokens : INT_MAX;
+  a.mt_max = kMtMaxTokens;
   const bool on = mfma_path(M, a.H, a.I);
   a.mfma_min = on ? kMfmaMinTokens : INT_MAX;
   if (on) {
@@ -66,17 +69,23 @@ ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
 
 RecOut layer_recout(const ForwardArgs& a, void* workspace) {
   return RecOut{const_cast<SlotRec*>(a.rec), a.topk_weights, a.M, a.k, a.has_shared, a.mfma_min,
-                const_cast<int2*>(a.items), reinterpret_cast<WorkspaceHeader*>(workspace)};
+                const_cast<int2*>(a.items), reinterpret_cast<WorkspaceHeader*>(workspace), a.mt_min, a.mt_max};
 }
 
-// The expert stage: GEMV gate/up (zeroes y) and down for the experts with few
-// tokens; with the MFMA path on, x is quantised first and the dense kernels
-// take the experts listed in the work items.
+// The expert stage: GEMV gate/up (zeroes y) and down for the experts with
+// one or two tokens; with the few-token path on, its kernels take experts of
+// kMtMinTokens..kMtMaxTokens tokens; with the MFMA path on, x is quantised
+// first and the dense kernels take the experts listed in the work items.
 hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const bool mfma = a.mfma_min == kMfmaMinTokens;
+  const bool mt = a.mt_min == kMtMinTokens;
   hipError_t e = hipSuccess;
   if (mfma && (e = launch_forward_mfma_front(a, s)) != hipSuccess) return e;
   if ((e = launch_forward(a, s, start, stop)) != hipSuccess) return e;
+  if (mt) {
+    if ((e = launch_gateup_mt(a, s)) != hipSuccess) return e;
+    if ((e = launch_down_mt(a, s)) != hipSuccess) return e;
+  }
   if (mfma) {
     if ((e = launch_gateup_mfma(a, s)) != hipSuccess) return e;
     if ((e = launch_down_mfma(a, s)) != hipSuccess) return e;
@@ -164,7 +173,7 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int3
   hipStream_t s = (hipStream_t)stream;
   ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
                              num_active, y, workspace);
-  if (a.mfma_min == kMfmaMinTokens) {
+  if (a.mfma_min == kMfmaMinTokens || a.mt_min == kMtMinTokens) {
     // the path choice needs per-expert token counts: records (and MFMA items) first
     const RecOut ro = layer_recout(a, workspace);
     if (launch_records(expert_offsets, sorted_pairs, active_experts, num_active, a.E, ro, s) != hipSuccess)

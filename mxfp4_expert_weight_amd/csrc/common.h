@@ -120,7 +120,8 @@ struct WorkspaceHeader {
   int32_t gemv_experts;   // expert passes on the VALU GEMV path in the last call
   int32_t mfma_experts;   // expert passes on the MFMA path in the last call
   int32_t mfma_items;     // (expert slot, token tile) work items of the MFMA kernels
-  int32_t reserved[61];
+  int32_t mt_experts;     // expert passes on the few-token matrix-core path
+  int32_t reserved[60];
 };
 static_assert(sizeof(WorkspaceHeader) == 256, "header size");
 

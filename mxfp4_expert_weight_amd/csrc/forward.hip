@@ -65,6 +65,7 @@ __device__ __forceinline__ bool route_in_block(const ForwardArgs& a, const Route
       a.hdr->gemv_experts = L.na + a.has_shared;        // every expert runs on this path
       a.hdr->mfma_experts = 0;
       a.hdr->mfma_items = 0;
+      a.hdr->mt_experts = 0;
     }
     return false;
   }
@@ -147,6 +148,7 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
       a.hdr->gemv_experts = *a.num_active + a.has_shared;  // without records: every expert on this path
       a.hdr->mfma_experts = 0;
       a.hdr->mfma_items = 0;
+      a.hdr->mt_experts = 0;
     }
     if (!resolve_slot(blockIdx.y, a, s)) return;
   }

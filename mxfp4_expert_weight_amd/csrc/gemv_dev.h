@@ -31,14 +31,15 @@ struct ExpertSlot {
 
 // From the slot record when there is one (a single 64-byte load), else from
 // the sort outputs.
-// Experts with at least a.mfma_min tokens belong to the MFMA kernels.
+// Experts with at least a.mfma_min tokens belong to the MFMA kernels, those
+// with a.mt_min..a.mt_max tokens to the few-token matrix-core kernels.
 __device__ __forceinline__ bool resolve_slot(int slot, const ForwardArgs& a, ExpertSlot& s) {
   if (a.rec) {
     const SlotRec r = a.rec[slot];
     s.e = r.e; s.n = r.n; s.pbeg = r.pbeg; s.hrow0 = r.hrow0;
 #pragma unroll
     for (int q = 0; q < kRecTokens; ++q) { s.tok[q] = r.tok[q]; s.w[q] = r.w[q]; }
-    return r.e >= 0 && r.n < a.mfma_min;
+    return r.e >= 0 && r.n < a.mfma_min && !(r.n >= a.mt_min && r.n <= a.mt_max);
   }
   const int n_act = *a.num_active;
   if (slot < n_act) {

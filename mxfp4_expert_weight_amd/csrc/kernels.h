@@ -9,6 +9,9 @@ namespace moe {
 // load gives an expert kernel its expert, token count and first tokens, instead
 // of a chain of dependent loads through num_active, active, offsets and pairs.
 constexpr int kRecTokens = 4;
+// Largest batch whose routing runs inside every gate/up block: an expert then
+// has at most kRecTokens tokens, all of them in its slot record.
+constexpr int kRoutedMaxTokens = kRecTokens;
 struct SlotRec {
   int32_t e;                  // expert index in the bank (E = shared), -1 = no work
   int32_t n;                  // tokens of this expert
@@ -36,6 +39,9 @@ struct ForwardArgs {
   WorkspaceHeader* hdr;       // workspace header
   const SlotRec* rec;         // slot records, or null (then resolved from the sort outputs)
   int M, k, E, H, I, has_shared;
+  // few-token matrix-core path (experts with mt_min..mt_max tokens, below
+  // mfma_min; mt_min = INT_MAX when off)
+  int mt_min, mt_max;
   // MFMA path (experts with >= mfma_min tokens; mfma_min = INT_MAX when off)
   int mfma_min;
   uint8_t *xq_hi, *xq_lo;     // [M][H] two-term MXFP8 (E4M3) codes of x
@@ -44,6 +50,13 @@ struct ForwardArgs {
   uint8_t *hq_shi, *hq_slo;   // [M*k + M][I/32]
   const int2* items;          // MFMA work items (slot, 64-token tile); count in hdr->mfma_items
 };
+
+// The few-token matrix-core path (mt.hip): batches of more than
+// kRoutedMaxTokens tokens whose reduction lengths are multiples of its
+// 256-element chunk; experts with kMtMinTokens..kMtMaxTokens tokens.
+constexpr int kMtMinTokens = 3;
+constexpr int kMtMaxTokens = 16;
+constexpr int kMtChunk = 256;
 
 // The MFMA path: experts with at least kMfmaMinTokens tokens run as dense
 // products on the scaled MXFP4 matrix cores when M reaches that many tokens
@@ -54,6 +67,8 @@ constexpr int kMfmaK = 128;             // K of one v_mfma_scale_f32_16x16x128_f
 inline bool mfma_path(int M, int H, int I) {
   return M >= kMfmaMinTokens && H % kMfmaK == 0 && I % kMfmaK == 0;
 }
+inline bool mt_path(int M, int H, int I) { return M > kRoutedMaxTokens && H % kMtChunk == 0 && I % kMtChunk == 0; }
+
 // Work items of the MFMA kernels are (slot, tile) pairs: at most
 // ceil(pairs/64) + (number of MFMA experts <= pairs/16) of them.
 __host__ __device__ inline int mfma_max_items(int M, int k) {
@@ -98,6 +113,7 @@ struct RecOut {
   int mfma_min;               // experts with at least this many tokens go to MFMA
   int2* items;                // MFMA work items (null when the path is off)
   WorkspaceHeader* hdr;
+  int mt_min, mt_max;         // few-token matrix-core range (mt_min = INT_MAX: off)
 };
 
 // Routing done inside the gate/up kernel (decode batches): where the logits
@@ -113,9 +129,6 @@ struct RouteOut {
   SlotRec* rec;               // slot records for the down kernel
   int ebits;                  // bits of an expert id
 };
-// Largest batch whose routing runs inside every gate/up block: an expert then
-// has at most kRecTokens tokens, all of them in its slot record.
-constexpr int kRoutedMaxTokens = kRecTokens;
 constexpr int kRoutedMaxPairs = kRoutedMaxTokens * MOE_MAX_TOPK;
 
 // Batches of at least this many tokens take the tiled router GEMM.
@@ -133,7 +146,7 @@ hipError_t launch_topk_softmax(const float* logits, int M, int E, int k, int* id
                                hipStream_t s);
 hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int* sorted_pairs,
                                  int* active, int* num_active, hipStream_t s,
-                                 RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0, 0, nullptr, nullptr});
+                                 RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0, 0, nullptr, nullptr, 0, 0});
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start = nullptr,
                           hipEvent_t stop = nullptr);
 // Gate/up with the top-k and the expert sort done in every block from the
@@ -144,6 +157,9 @@ hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStr
 // and down products of the experts listed in the work items.
 hipError_t launch_forward_mfma_front(const ForwardArgs& a, hipStream_t s);   // x quantisation
 hipError_t launch_gateup_mfma(const ForwardArgs& a, hipStream_t s);
+// Few-token matrix-core path (mt.hip).
+hipError_t launch_gateup_mt(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_down_mt(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_down_mfma(const ForwardArgs& a, hipStream_t s);
 // Slot records and MFMA items from the sort outputs (one workgroup).
 hipError_t launch_records(const int* offsets, const int* sorted_pairs, const int* active, const int* num_active,

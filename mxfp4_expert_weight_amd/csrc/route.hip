@@ -233,11 +233,19 @@ __global__ __launch_bounds__(64 * kTopkSortMaxTokens) void topk_sort_small_kerne
   if (t == 0) wave_sort_small(L, N, E, ebits);
   __syncthreads();
   block_store_small_sort(L, N, E, topk_ids, topk_weights, offsets, sorted_pairs, active, num_active);
+  __shared__ int n_mt;
+  if (threadIdx.x == 0) n_mt = 0;
+  __syncthreads();
   if (ro.rec)
-    for (int slot = threadIdx.x; slot < max_slots(M, k, E); slot += blockDim.x)
-      ro.rec[slot] = small_slot_record(L, slot, M, k, E, ro.has_shared);
-  if (ro.hdr && threadIdx.x == 0) {     // at most 8 tokens per expert: all on the GEMV path
-    ro.hdr->gemv_experts = L.na + ro.has_shared;
+    for (int slot = threadIdx.x; slot < max_slots(M, k, E); slot += blockDim.x) {
+      const SlotRec r = small_slot_record(L, slot, M, k, E, ro.has_shared);
+      ro.rec[slot] = r;
+      if (r.e >= 0 && expert_path(r.n, ro.mt_min, ro.mt_max, ro.mfma_min) == 1) atomicAdd(&n_mt, 1);
+    }
+  __syncthreads();
+  if (ro.hdr && threadIdx.x == 0) {     // at most 8 tokens per expert: no dense MFMA
+    ro.hdr->gemv_experts = L.na + ro.has_shared - n_mt;
+    ro.hdr->mt_experts = n_mt;
     ro.hdr->mfma_experts = 0;
     ro.hdr->mfma_items = 0;
   }

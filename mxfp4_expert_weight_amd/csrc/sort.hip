@@ -25,7 +25,7 @@ __global__ __launch_bounds__(512) void records_kernel(const int* __restrict__ of
                                                       const int* __restrict__ sorted_pairs,
                                                       const int* __restrict__ active,
                                                       const int* __restrict__ num_active, int E, RecOut ro) {
-  __shared__ int lds[2 * (512 / kWave + 1)];
+  __shared__ int lds[4 * (512 / kWave) + 4];
   block_write_slot_records(ro, E, max_slots(ro.M, ro.k, E), offsets, sorted_pairs, active, num_active, lds);
 }
 

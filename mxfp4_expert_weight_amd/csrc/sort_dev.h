@@ -31,7 +31,11 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 }
 
 // Ints of LDS block_sort_pairs needs with nw waves and E experts.
-__host__ __device__ inline size_t sort_lds_ints(int nw, int E) { return (size_t)nw * E + E + 2 * nw; }
+// (at least what the records epilogue then reuses: 4 * nw + 4)
+__host__ __device__ inline size_t sort_lds_ints(int nw, int E) {
+  const size_t sort = (size_t)nw * E + E + 2 * nw, rec = 4 * (size_t)nw + 4;
+  return sort > rec ? sort : rec;
+}
 
 // Sort `N` pairs whose expert ids are ids[0..N) (global or LDS).  Uses
 // sort_lds_ints(nw, E) ints of LDS at `lds`; every thread of the block calls it.
@@ -158,11 +162,16 @@ __device__ __forceinline__ SlotRec make_slot_record(int slot, int D, const int* 
   return r;
 }
 
+// Path of an expert with n tokens: 0 GEMV, 1 few-token matrix cores, 2 MFMA.
+__device__ __forceinline__ int expert_path(int n, int mt_min, int mt_max, int mfma_min) {
+  return n >= mfma_min ? 2 : (n >= mt_min && n <= mt_max) ? 1 : 0;
+}
+
 // Slot records from the finished sort in global memory (this block wrote it
-// and a barrier made it visible): one thread per possible slot.  Then the
-// path counters in the header and, with the MFMA path on, its work items:
-// (slot, 64-token tile) for every slot with at least ro.mfma_min tokens, in
-// slot order.  `lds` holds 2 * (waves + 1) ints.
+// and a barrier made it visible).  Thread i handles a contiguous span of
+// slots.  Then the path counters in the header and, with the MFMA path on,
+// its work items: (slot, 64-token tile) for every slot with at least
+// ro.mfma_min tokens, in slot order.  `lds` holds 4 * waves + 4 ints.
 __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nslots,
                                                 const int* __restrict__ offsets,
                                                 const int* __restrict__ sorted_pairs,
@@ -172,31 +181,35 @@ __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nsl
   const int bd = blockDim.x, tid = threadIdx.x;
   const int per = (nslots + bd - 1) / bd;
   const int s0 = min(nslots, tid * per), s1 = min(nslots, s0 + per);
-  int tiles = 0, n_mfma = 0, n_gemv = 0;
+  int tiles = 0, cnt[3] = {0, 0, 0};
   for (int slot = s0; slot < s1; ++slot) {
     const SlotRec r = make_slot_record(slot, D, offsets, sorted_pairs, active, ro.topk_weights, ro.M, ro.k, E,
                                        ro.has_shared);
     ro.rec[slot] = r;
     if (r.e < 0) continue;
-    if (r.n >= ro.mfma_min) {
-      ++n_mfma;
-      tiles += (r.n + kMfmaTileTokens - 1) / kMfmaTileTokens;
-    } else {
-      ++n_gemv;
-    }
+    const int path = expert_path(r.n, ro.mt_min, ro.mt_max, ro.mfma_min);
+    ++cnt[path];
+    if (path == 2) tiles += (r.n + kMfmaTileTokens - 1) / kMfmaTileTokens;
   }
   if (!ro.hdr) return;
-  // block-wide exclusive scan of the tile counts (thread spans are in slot order)
+  // block-wide exclusive scan of the tile counts (thread spans are in slot
+  // order) and block sums of the path counts
   const int lane = tid & (kWave - 1), w = tid / kWave, nw = bd / kWave;
-  const int packed_c = n_mfma | (n_gemv << 16);
   const int inc = wave_inclusive_scan(tiles);
-  const int cinc = wave_inclusive_scan(packed_c);
-  if (lane == kWave - 1) { lds[w] = inc; lds[nw + 1 + w] = cinc; }
+  int csum[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) csum[p] = wave_inclusive_scan(cnt[p]);
+  if (lane == kWave - 1) {
+    lds[w] = inc;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) lds[nw * (p + 1) + w] = csum[p];
+  }
   __syncthreads();
-  int base = inc - tiles, call = 0;
+  int base = inc - tiles, tot[3] = {0, 0, 0};
   for (int v = 0; v < nw; ++v) {
     if (v < w) base += lds[v];
-    call += lds[nw + 1 + v];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) tot[p] += lds[nw * (p + 1) + v];
   }
   if (ro.items) {
     for (int slot = s0; slot < s1; ++slot) {
@@ -207,8 +220,9 @@ __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nsl
   }
   if (tid == bd - 1) {
     ro.hdr->mfma_items = ro.items ? base : 0;
-    ro.hdr->mfma_experts = call & 0xFFFF;
-    ro.hdr->gemv_experts = call >> 16;
+    ro.hdr->gemv_experts = tot[0];
+    ro.hdr->mt_experts = tot[1];
+    ro.hdr->mfma_experts = tot[2];
   }
 }
 

@@ -74,8 +74,8 @@ class LayerBuffers:
         self.ws = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=device)
 
     def header(self) -> dict:
-        h = self.ws[:8].view(torch.int32).cpu().tolist()
-        return dict(gemv_experts=h[0], mfma_experts=h[1])
+        h = self.ws[:16].view(torch.int32).cpu().tolist()
+        return dict(gemv_experts=h[0], mfma_experts=h[1], mfma_items=h[2], mt_experts=h[3])
 
 
 def run_layer(d: DeviceLayerSet, b: LayerBuffers, w: Optional[binding.moe_mxfp4_weights] = None,

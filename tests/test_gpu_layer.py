@@ -29,13 +29,29 @@ def _run(torch, ls, fused=True):
     return out, d, b
 
 
-def expected_mfma_experts(wl, r):
-    """Experts with at least 16 tokens run on the matrix cores when M >= 16 and
-    H and I are multiples of 128 (the instruction's K)."""
-    if wl.M < 16 or wl.H % 128 or wl.I % 128:
-        return 0
-    counts = np.bincount(r["ids"].ravel(), minlength=wl.E)
-    return int(np.sum(counts >= 16)) + int(wl.shared and wl.M >= 16)
+def expected_paths(wl, ids):
+    """(GEMV, few-token matrix-core, scaled-MFMA) expert counts of a layer.
+    Scaled MFMA: experts with >= 16 tokens when M >= 16 and H, I are multiples
+    of 128.  Few-token matrix cores: 3..16 tokens (below the MFMA range) when
+    M > 4 and H, I are multiples of 256.  The rest: GEMV."""
+    counts = np.bincount(np.asarray(ids).ravel(), minlength=wl.E)
+    n = [int(c) for c in counts if c > 0] + ([wl.M] if wl.shared else [])
+    mfma_on = wl.M >= 16 and wl.H % 128 == 0 and wl.I % 128 == 0
+    mt_on = wl.M > 4 and wl.H % 256 == 0 and wl.I % 256 == 0
+    paths = [0, 0, 0]
+    for c in n:
+        if mfma_on and c >= 16:
+            paths[2] += 1
+        elif mt_on and 3 <= c <= 16:
+            paths[1] += 1
+        else:
+            paths[0] += 1
+    return paths
+
+
+def assert_paths(hdr, wl, ids, what):
+    got = [hdr["gemv_experts"], hdr["mt_experts"], hdr["mfma_experts"]]
+    assert got == expected_paths(wl, ids), f"{what}: expert paths (gemv, mt, mfma) {got}"
 
 
 def _check_full(torch, ls, what, fused=True):
@@ -53,8 +69,7 @@ def _check_full(torch, ls, what, fused=True):
     assert_layer_close(g["y"][keep], r["y"][keep], rms, what)
     if not amb:
         assert g["num_active"] == r["num_active"]
-        assert g["hdr"]["gemv_experts"] + g["hdr"]["mfma_experts"] == r["num_active"] + int(wl.shared)
-        assert g["hdr"]["mfma_experts"] == expected_mfma_experts(wl, r)
+        assert_paths(g["hdr"], wl, r["ids"], what)
     assert len(amb) <= max(1, wl.M // 50), f"{what}: {len(amb)} ambiguous tokens"
     return g, r
 
@@ -80,6 +95,9 @@ def test_tiny_config_every_element(fused):
     (40, 256, 128, 4, 2, True, "plain"),     # matrix-core path: every expert has >= 16 tokens
     (130, 384, 256, 3, 2, True, "plain"),    # matrix-core path: ragged 64-token tiles
     (24, 256, 128, 12, 2, True, "zipf"),     # both paths in one layer
+    (6, 256, 256, 3, 2, False, "plain"),     # few-token matrix cores after the fused top-k + sort
+    (12, 256, 256, 6, 4, True, "plain"),     # few-token matrix cores, shared expert included
+    (24, 512, 512, 10, 3, True, "zipf"),     # GEMV, few-token and scaled-MFMA experts in one layer
 ])
 def test_edge_shapes_every_element(M, H, I, E, k, shared, routing):
     torch = need_gpu()
@@ -119,9 +137,8 @@ def test_ling_batch_sampled_tokens(name, tokens):
     # every token's output is finite and the dedup covers every routed pair
     assert np.all(np.isfinite(g["y"]))
     D = len(np.unique(g["ids"]))
-    counts = np.bincount(g["ids"].ravel(), minlength=wl.E)
-    assert g["num_active"] == D and g["hdr"]["gemv_experts"] + g["hdr"]["mfma_experts"] == D + 1
-    assert g["hdr"]["mfma_experts"] == int(np.sum(counts >= 16)) + 1     # + the shared expert (M >= 16)
+    assert g["num_active"] == D
+    assert_paths(g["hdr"], wl, g["ids"], name)
 
 
 def test_token_independence_m4_vs_m1():
