@@ -113,6 +113,15 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   p = swap32(v); return min(p.a, p.b);
 }
 
+// Workgroup barrier that orders LDS only: it does not wait for outstanding
+// global loads (gfx950 barriers do not imply a memory wait), so prefetched
+// weights stay in flight across it.  (__syncthreads waits for all of them.)
+__device__ __forceinline__ void block_barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------- workspace --
 // Header at the start of the forward workspace; device-written counters that
 // tell the caller which path ran (no global state in the library).

@@ -124,40 +124,6 @@ __device__ __forceinline__ void unpack8(const uint4& v, uint32_t* a) {
   a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
 }
 
-// Block barrier that orders LDS only: it does not wait for outstanding global
-// loads (gfx950 barriers do not imply a memory wait), so prefetched weights
-// stay in flight across it.
-__device__ __forceinline__ void block_barrier_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Activation rows (bf16, `row_u4` uint4 per row) of an expert's first `nl`
-// tokens into LDS, by the whole block, in two steps so the loads can be issued
-// early and their LDS writes placed after later loads: stage_issue loads this
-// thread's share into registers (clamped addresses, no branches), stage_commit
-// writes them.  `row_of(i)` gives the global row of token i.
-template <int PT, typename RowOf>
-__device__ __forceinline__ void stage_issue(const uint16_t* __restrict__ base, int row_u4, int nl,
-                                            RowOf row_of, uint4 (&v)[PT]) {
-  const int total = nl * row_u4;
-#pragma unroll
-  for (int k = 0; k < PT; ++k) {
-    const int idx = min((int)threadIdx.x + k * (int)blockDim.x, total - 1);
-    const int r = idx / row_u4, c = idx - r * row_u4;
-    v[k] = reinterpret_cast<const uint4*>(base + (size_t)row_of(r) * (row_u4 * 8))[c];
-  }
-}
-template <int PT>
-__device__ __forceinline__ void stage_commit(int row_u4, int nl, const uint4 (&v)[PT], uint4* lds) {
-  const int total = nl * row_u4;
-#pragma unroll
-  for (int k = 0; k < PT; ++k) {
-    const int idx = (int)threadIdx.x + k * (int)blockDim.x;
-    if (idx < total) lds[idx] = v[k];
-  }
-}
 
 // Activations of one token for one lane: half-chunk hc = 16 bf16 = two uint4.
 __device__ __forceinline__ void act_from(const uint4* row, int hc, uint32_t* a8) {

@@ -126,22 +126,17 @@ struct StageRegs {
   uint32_t sh, sl;
 };
 
+// Raw loads (clamped row); the mask for rows past the tile is applied when
+// the registers are written to LDS, so the load's wait is not forced early.
 __device__ __forceinline__ void stage_load(StageRegs& st, const uint8_t* qhi, const uint8_t* qlo,
-                                           const uint8_t* shi, const uint8_t* slo, int64_t row, bool valid,
-                                           int K, int kc, int q) {
-  const int64_t rr = valid ? row : 0;               // clamped, masked after the load
-  const uint4* ph = reinterpret_cast<const uint4*>(qhi + rr * K + kc * kMfmaK + 32 * q);
-  const uint4* pl = reinterpret_cast<const uint4*>(qlo + rr * K + kc * kMfmaK + 32 * q);
-  const uint4 h0 = ph[0], h1 = ph[1], l0 = pl[0], l1 = pl[1];
-  const uint32_t sh = shi[rr * (K / 32) + kc * 4 + q], sl = slo[rr * (K / 32) + kc * 4 + q];
-  // mask word by word (a select of whole vectors goes through scratch memory)
-  const uint32_t m = valid ? 0xFFFFFFFFu : 0u;
-  st.h0 = make_uint4(h0.x & m, h0.y & m, h0.z & m, h0.w & m);
-  st.h1 = make_uint4(h1.x & m, h1.y & m, h1.z & m, h1.w & m);
-  st.l0 = make_uint4(l0.x & m, l0.y & m, l0.z & m, l0.w & m);
-  st.l1 = make_uint4(l1.x & m, l1.y & m, l1.z & m, l1.w & m);
-  st.sh = sh & m;
-  st.sl = sl & m;
+                                           const uint8_t* shi, const uint8_t* slo, int64_t row, int K, int kc,
+                                           int q) {
+  const uint4* ph = reinterpret_cast<const uint4*>(qhi + row * K + kc * kMfmaK + 32 * q);
+  const uint4* pl = reinterpret_cast<const uint4*>(qlo + row * K + kc * kMfmaK + 32 * q);
+  st.h0 = ph[0]; st.h1 = ph[1];
+  st.l0 = pl[0]; st.l1 = pl[1];
+  st.sh = shi[row * (K / 32) + kc * 4 + q];
+  st.sl = slo[row * (K / 32) + kc * 4 + q];
 }
 
 struct __align__(16) StageBuf {
@@ -151,13 +146,17 @@ struct __align__(16) StageBuf {
   uint8_t slo[MF_TT * 4];
 };
 
-__device__ __forceinline__ void stage_store(StageBuf& b, const StageRegs& st, int c, int q) {
+__device__ __forceinline__ void stage_store(StageBuf& b, const StageRegs& st, int c, int q, bool valid) {
+  // mask word by word (a select of whole vectors goes through scratch memory)
+  const uint32_t m = valid ? 0xFFFFFFFFu : 0u;
   uint4* dh = reinterpret_cast<uint4*>(b.hi + c * MF_PITCH + 32 * q);
   uint4* dl = reinterpret_cast<uint4*>(b.lo + c * MF_PITCH + 32 * q);
-  dh[0] = st.h0; dh[1] = st.h1;
-  dl[0] = st.l0; dl[1] = st.l1;
-  b.shi[c * 4 + q] = (uint8_t)st.sh;
-  b.slo[c * 4 + q] = (uint8_t)st.sl;
+  dh[0] = make_uint4(st.h0.x & m, st.h0.y & m, st.h0.z & m, st.h0.w & m);
+  dh[1] = make_uint4(st.h1.x & m, st.h1.y & m, st.h1.z & m, st.h1.w & m);
+  dl[0] = make_uint4(st.l0.x & m, st.l0.y & m, st.l0.z & m, st.l0.w & m);
+  dl[1] = make_uint4(st.l1.x & m, st.l1.y & m, st.l1.z & m, st.l1.w & m);
+  b.shi[c * 4 + q] = (uint8_t)(st.sh & m);
+  b.slo[c * 4 + q] = (uint8_t)(st.sl & m);
 }
 
 // B operand of token sub-tile s for lane (g, j): bytes [16g, +16) and
@@ -172,17 +171,15 @@ __device__ __forceinline__ v8i frag_b(const uint8_t* rows, int s, int g, int j) 
   return v;
 }
 
-// A operand: 16 code bytes of one weight row at K offset 128*kc + 32g.
-__device__ __forceinline__ v8i frag_a(const uint8_t* row_q, int kc, int g) {
-  const uint4 a = *reinterpret_cast<const uint4*>(row_q + kc * (kMfmaK / 2) + 16 * g);
-  v8i v;
-  v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
-  v[4] = 0; v[5] = 0; v[6] = 0; v[7] = 0;
-  return v;
-}
 
 // Expert `rec`, token tile t0..t0+nt: one 16-row x 64-token product per wave
-// over K, both activation terms into the same accumulators.
+// over K, both activation terms into the same accumulators.  The weight
+// operand is prefetched MF_ADEPTH chunks ahead in a register ring (the HBM
+// round trip is several chunks of products long); the activation chunks go
+// through two LDS buffers one chunk ahead.  Barriers order LDS only, so the
+// prefetched weights stay in flight across them.
+constexpr int MF_ADEPTH = 8;
+static_assert(MF_ADEPTH % 2 == 0, "the staging registers alternate by chunk parity");
 __device__ __forceinline__ void mfma_tile(v4f (&acc)[4], const uint8_t* row_q, const uint8_t* row_s,
                                           const uint8_t* qhi, const uint8_t* qlo, const uint8_t* shi,
                                           const uint8_t* slo, const int64_t stage_row, bool stage_valid, int K,
@@ -193,35 +190,50 @@ __device__ __forceinline__ void mfma_tile(v4f (&acc)[4], const uint8_t* row_q, c
   const int nk = K / kMfmaK;
 #pragma unroll
   for (int s = 0; s < 4; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
-  StageRegs st;
-  stage_load(st, qhi, qlo, shi, slo, stage_row, stage_valid, K, 0, q);
-  stage_store(buf[0], st, c, q);
-  v8i a = frag_a(row_q, 0, g);
-  uint32_t sa = row_s[4 * 0 + g];
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    const int cur = kc & 1;
-    const bool more = kc + 1 < nk;
-    v8i a_next = a;
-    uint32_t sa_next = sa;
-    if (more) {                                    // next chunk in flight during this one's products
-      stage_load(st, qhi, qlo, shi, slo, stage_row, stage_valid, K, kc + 1, q);
-      a_next = frag_a(row_q, kc + 1, g);
-      sa_next = row_s[4 * (kc + 1) + g];
-    }
+  uint4 ar[MF_ADEPTH];
+  uint32_t sr[MF_ADEPTH];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const v8i bh = frag_b(buf[cur].hi, s, g, j);
-      const v8i bl = frag_b(buf[cur].lo, s, g, j);
-      const int sbh = buf[cur].shi[(16 * s + j) * 4 + g];
-      const int sbl = buf[cur].slo[(16 * s + j) * 4 + g];
-      acc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bh, acc[s], 4, 0, 0, (int)sa, 0, sbh);
-      acc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bl, acc[s], 4, 0, 0, (int)sa, 0, sbl);
+  for (int d = 0; d < MF_ADEPTH; ++d) {           // chunks past the end re-read the last (unused)
+    const int kc = min(d, nk - 1);
+    ar[d] = *reinterpret_cast<const uint4*>(row_q + kc * (kMfmaK / 2) + 16 * g);
+    sr[d] = row_s[4 * kc + g];
+  }
+  // activation chunks: loaded two chunks ahead into st[chunk & 1], written to
+  // LDS one chunk ahead (chunks past the end repeat the last: never read)
+  StageRegs st[2];
+  stage_load(st[0], qhi, qlo, shi, slo, stage_row, K, 0, q);
+  stage_store(buf[0], st[0], c, q, stage_valid);
+  stage_load(st[1], qhi, qlo, shi, slo, stage_row, K, min(1, nk - 1), q);
+  block_barrier_lds();
+  for (int kb = 0; kb < nk; kb += MF_ADEPTH) {
+#pragma unroll
+    for (int d = 0; d < MF_ADEPTH; ++d) {
+      const int kc = kb + d;
+      if (kc < nk) {                               // uniform
+        const int cur = kc & 1;                    // == d & 1 (MF_ADEPTH is even)
+        stage_load(st[d & 1], qhi, qlo, shi, slo, stage_row, K, min(kc + 2, nk - 1), q);
+        v8i a;
+        a[0] = (int)ar[d].x; a[1] = (int)ar[d].y; a[2] = (int)ar[d].z; a[3] = (int)ar[d].w;
+        a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
+        const int sa = (int)sr[d];
+        {                                          // refill this ring slot with chunk kc + MF_ADEPTH
+          const int kn = min(kc + MF_ADEPTH, nk - 1);
+          ar[d] = *reinterpret_cast<const uint4*>(row_q + kn * (kMfmaK / 2) + 16 * g);
+          sr[d] = row_s[4 * kn + g];
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const v8i bh = frag_b(buf[cur].hi, s, g, j);
+          const v8i bl = frag_b(buf[cur].lo, s, g, j);
+          const int sbh = buf[cur].shi[(16 * s + j) * 4 + g];
+          const int sbl = buf[cur].slo[(16 * s + j) * 4 + g];
+          acc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bh, acc[s], 4, 0, 0, sa, 0, sbh);
+          acc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bl, acc[s], 4, 0, 0, sa, 0, sbl);
+        }
+        stage_store(buf[cur ^ 1], st[(d + 1) & 1], c, q, stage_valid);
+        block_barrier_lds();
+      }
     }
-    if (more) stage_store(buf[cur ^ 1], st, c, q);
-    __syncthreads();
-    a = a_next;
-    sa = sa_next;
   }
 }
 
@@ -263,7 +275,7 @@ __global__ __launch_bounds__(MF_WAVES * kWave) void gateup_mfma_kernel(ForwardAr
 #pragma unroll
         for (int r = 0; r < 4; ++r) ul[16 * s + j][16 * half + 4 * g + r] = acc[s][r];
     }
-    __syncthreads();
+    block_barrier_lds();
     if (!is_up) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -273,7 +285,7 @@ __global__ __launch_bounds__(MF_WAVES * kWave) void gateup_mfma_kernel(ForwardAr
           ul[tc][jl] = silu(acc[s][r]) * ul[tc][jl];
         }
     }
-    __syncthreads();
+    block_barrier_lds();
     if (threadIdx.x < nt) {
       const int tc = threadIdx.x;
       float v[32];
@@ -291,7 +303,7 @@ __global__ __launch_bounds__(MF_WAVES * kWave) void gateup_mfma_kernel(ForwardAr
       a.hq_shi[hrow * (a.I / 32) + j0 / 32] = (uint8_t)sh;
       a.hq_slo[hrow * (a.I / 32) + j0 / 32] = (uint8_t)sl;
     }
-    __syncthreads();
+    block_barrier_lds();
   }
 }
 
