@@ -22,29 +22,38 @@ constexpr int GU_LDS_PER_WAVE = 2 * 2 * GU_NP * (MOE_MAX_HIDDEN / 32);
 constexpr int DN_LDS_PER_WAVE = 4 * DN_NR * (MOE_MAX_INTER / 32);
 constexpr int GU_SHORT_H = 32 * GU_HC * 16;         // longest row the single-pass path holds (2560)
 constexpr int DN_SHORT_I = 16 * DN_HC * 16;         // (768)
+// Gate/up workgroups resident per CU (3 waves per SIMD, 4 waves a workgroup).
+constexpr int kGateupBlocksPerCu = 3;
 
 // Routing inside a gate/up block (decode batches, M <= kRoutedMaxTokens, so
-// at most 128 pairs: two per lane).  Every workgroup first takes the top-k of
-// token t in wave t, into LDS.  Then:
-//  - the workgroup at x = 0 of the extra last grid row is the writer: wave 0
-//    sorts the pairs and the block writes the routing outputs and the header;
-//  - every other workgroup needs only its own slot s = blockIdx.y: each wave
-//    marks the chosen experts in its own LDS bitmap, counts the active experts
-//    with a popcount scan over the bitmap words, takes the s-th set bit as its
-//    expert and finds that expert's pairs with ballots (no barrier, no sort);
-//    block (0, s) writes the slot record the down kernel reads.
-// Every workgroup computes the same top-k from the same logits.  Returns
-// false when the workgroup has no gate/up work.
+// at most 128 pairs: two per lane).  route_prepare: every workgroup takes the
+// top-k of token t in wave t, into LDS.  The workgroup at x = 0 of the extra
+// last grid row is the writer: wave 0 sorts the pairs and the block writes the
+// routing outputs and the header.  Every other workgroup needs only the slots
+// it works on: each wave marks the chosen experts in its own LDS bitmap and
+// counts the active experts with a popcount scan over the bitmap words (no
+// barrier, no sort); route_slot then takes the slot-th set bit as the slot's
+// expert and finds its pairs with ballots.  Every workgroup computes the same
+// top-k from the same logits.
+struct RouteState {           // per-wave: this wave's copy of the pairs and the bitmap scan
+  int eA, eB, tA, tB;         // pair `lane` (A) and pair `lane + 64` (B): expert, token
+  float wA, wB;               // their routing weights
+  bool vA, vB;
+  uint32_t word;              // bitmap word `lane` of the active experts
+  int inc;                    // inclusive popcount scan over the words
+  int D;                      // active experts
+};
+
+// Returns false for the writer (after writing the routing outputs).
 template <int C>
-__device__ __forceinline__ bool route_in_block(const ForwardArgs& a, const RouteOut& r, ExpertSlot& s) {
+__device__ __forceinline__ bool route_prepare(const ForwardArgs& a, const RouteOut& r, RouteState& rs,
+                                              bool writer) {
   constexpr int kWords = MOE_MAX_EXPERTS / 32;           // bitmap words; index kWords is a sink
   __shared__ SmallSortLds<C, kRoutedMaxPairs> L;
   __shared__ uint32_t bits[GU_WPB][kWords + 1];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int nw = blockDim.x / kWave;
   const int N = a.M * a.k, E = a.E;
-  const bool writer = blockIdx.y == gridDim.y - 1;
-  if (writer && blockIdx.x != 0) return false;
   if (lane <= kWords) bits[wave][lane] = 0u;
   for (int t = wave; t < a.M; t += nw) {
     int id; float w;
@@ -69,63 +78,63 @@ __device__ __forceinline__ bool route_in_block(const ForwardArgs& a, const Route
     }
     return false;
   }
-  // this wave's copy of the pairs: pair `lane` (A) and pair `lane + 64` (B)
   const int pA = min(lane, N - 1), pB = min(lane + kWave, N - 1);
-  const int eA = L.ids[pA], eB = L.ids[pB];
-  const int tA = L.tok[pA], tB = L.tok[pB];
-  const float wA = L.w[pA], wB = L.w[pB];
-  const bool vA = lane < N && (unsigned)eA < (unsigned)E;
-  const bool vB = lane + kWave < N && (unsigned)eB < (unsigned)E;
+  rs.eA = L.ids[pA]; rs.eB = L.ids[pB];
+  rs.tA = L.tok[pA]; rs.tB = L.tok[pB];
+  rs.wA = L.w[pA]; rs.wB = L.w[pB];
+  rs.vA = lane < N && (unsigned)rs.eA < (unsigned)E;
+  rs.vB = lane + kWave < N && (unsigned)rs.eB < (unsigned)E;
   uint32_t* mb = bits[wave];
-  atomicOr(&mb[vA ? (eA >> 5) : kWords], 1u << (eA & 31));
-  atomicOr(&mb[vB ? (eB >> 5) : kWords], 1u << (eB & 31));
+  atomicOr(&mb[rs.vA ? (rs.eA >> 5) : kWords], 1u << (rs.eA & 31));
+  atomicOr(&mb[rs.vB ? (rs.eB >> 5) : kWords], 1u << (rs.eB & 31));
   wave_lds_fence();
   const int nwords = (E + 31) >> 5;
-  const uint32_t word = (lane < nwords) ? mb[min(lane, kWords - 1)] : 0u;
-  const int inc = wave_inclusive_scan(__popc(word));
-  const int D = __builtin_amdgcn_readlane(inc, kWave - 1);
-  const int slot = blockIdx.y;
+  rs.word = (lane < nwords) ? mb[min(lane, kWords - 1)] : 0u;
+  rs.inc = wave_inclusive_scan(__popc(rs.word));
+  rs.D = __builtin_amdgcn_readlane(rs.inc, kWave - 1);
+  return true;
+}
+
+// Slot record of `slot`: slots [0, D) are the active experts in increasing
+// order, slot D the shared expert, later slots have no work (e = -1).
+__device__ __forceinline__ SlotRec route_slot(const ForwardArgs& a, const RouteState& rs, int slot) {
   SlotRec rec;
   rec.pad[0] = rec.pad[1] = rec.pad[2] = rec.pad[3] = 0;
 #pragma unroll
   for (int q = 0; q < kRecTokens; ++q) { rec.tok[q] = 0; rec.w[q] = 0.f; }
-  if (slot < D) {
-    const int wsel = (int)__builtin_ctzll(__ballot(inc > slot));          // word holding the expert
-    uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)word, wsel);
-    int nth = slot - (__builtin_amdgcn_readlane(inc, wsel) - __popc(wb));
+  if (slot < rs.D) {
+    const int wsel = (int)__builtin_ctzll(__ballot(rs.inc > slot));      // word holding the expert
+    uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)rs.word, wsel);
+    int nth = slot - (__builtin_amdgcn_readlane(rs.inc, wsel) - __popc(wb));
     for (; nth > 0; --nth) wb &= wb - 1u;
     const int e = wsel * 32 + __builtin_ctz(wb);
-    uint64_t mA = __ballot(vA && eA == e), mB = __ballot(vB && eB == e);
+    uint64_t mA = __ballot(rs.vA && rs.eA == e), mB = __ballot(rs.vB && rs.eB == e);
     rec.e = e;
     rec.n = __popcll(mA) + __popcll(mB);
-    rec.pbeg = __popcll(__ballot(vA && eA < e)) + __popcll(__ballot(vB && eB < e));
+    rec.pbeg = __popcll(__ballot(rs.vA && rs.eA < e)) + __popcll(__ballot(rs.vB && rs.eB < e));
     rec.hrow0 = rec.pbeg;
 #pragma unroll
     for (int q = 0; q < kRecTokens; ++q) {             // the expert's pairs in order
       if (mA) {
         const int p = (int)__builtin_ctzll(mA);
-        rec.tok[q] = __builtin_amdgcn_readlane(tA, p);
-        rec.w[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wA), p));
+        rec.tok[q] = __builtin_amdgcn_readlane(rs.tA, p);
+        rec.w[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs.wA), p));
         mA &= mA - 1;
       } else if (mB) {
         const int p = (int)__builtin_ctzll(mB);
-        rec.tok[q] = __builtin_amdgcn_readlane(tB, p);
-        rec.w[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wB), p));
+        rec.tok[q] = __builtin_amdgcn_readlane(rs.tB, p);
+        rec.w[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs.wB), p));
         mB &= mB - 1;
       }
     }
-  } else if (slot == D && a.has_shared) {
-    rec.e = E; rec.n = a.M; rec.pbeg = -1; rec.hrow0 = N;
+  } else if (slot == rs.D && a.has_shared) {
+    rec.e = a.E; rec.n = a.M; rec.pbeg = -1; rec.hrow0 = a.M * a.k;
 #pragma unroll
     for (int q = 0; q < kRecTokens; ++q) { rec.tok[q] = q < a.M ? q : 0; rec.w[q] = 1.f; }
   } else {
     rec.e = -1; rec.n = 0; rec.pbeg = -1; rec.hrow0 = 0;
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) r.rec[slot] = rec;
-  s.e = rec.e; s.n = rec.n; s.pbeg = rec.pbeg; s.hrow0 = rec.hrow0;
-#pragma unroll
-  for (int q = 0; q < kRecTokens; ++q) { s.tok[q] = rec.tok[q]; s.w[q] = rec.w[q]; }
-  return rec.e >= 0;
+  return rec;
 }
 
 // at most 3 waves per SIMD: the codes, scales and staged activations of a wave
@@ -141,8 +150,47 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
     for (size_t i = b * blockDim.x + threadIdx.x; i < total; i += nblk * blockDim.x) a.y[i] = 0.f;
   }
   ExpertSlot s;
+  __shared__ uint8_t s_lds[GU_WPB][GU_LDS_PER_WAVE];
+  const int wave = threadIdx.x / kWave;
+  const int jp0 = (blockIdx.x * GU_WPB + wave) * 2 * GU_NP;
   if constexpr (C > 0) {
-    if (!route_in_block<C>(a, r, s)) return;             // uniform over the block
+    // routed: rows 0 .. gridDim.y-2 loop over the slots (each workgroup routes
+    // once, however many slots it takes); the last row is the writer
+    const bool writer = blockIdx.y == gridDim.y - 1;
+    if (writer && blockIdx.x != 0) return;
+    RouteState rs;
+    if (!route_prepare<C>(a, r, rs, writer)) return;     // uniform over the block
+    // this block's slots: blockIdx.y, + rows, + 2 rows, ...  Their records are
+    // looked up first (one wave per slot) and parked in LDS, so no routing
+    // state stays live in registers through the GEMVs.
+    __shared__ SlotRec s_rec[kRoutedMaxPairs + 1];
+    const int slots = max_slots(a.M, a.k, a.E) - 1 + a.has_shared;
+    const int rows = gridDim.y - 1;
+    const int mine = (slots - (int)blockIdx.y + rows - 1) / rows;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int i = wave; i < mine; i += GU_WPB) {
+      const int slot = blockIdx.y + i * rows;
+      const SlotRec rec = route_slot(a, rs, slot);
+      if (lane == 0) {
+        s_rec[i] = rec;
+        if (blockIdx.x == 0) r.rec[slot] = rec;
+      }
+    }
+    __syncthreads();
+    for (int i = 0; i < mine; ++i) {
+      const SlotRec& rec = s_rec[i];
+      if (rec.e < 0) break;                              // later slots are empty too
+      s.e = rec.e; s.n = rec.n; s.pbeg = rec.pbeg; s.hrow0 = rec.hrow0;
+#pragma unroll
+      for (int q = 0; q < kRecTokens; ++q) { s.tok[q] = rec.tok[q]; s.w[q] = rec.w[q]; }
+      if (jp0 < a.I) {
+        if constexpr (SHORT)
+          gateup_short<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
+        else
+          gateup_long<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
+      }
+    }
+    return;
   } else {
     if (!a.rec && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
       a.hdr->gemv_experts = *a.num_active + a.has_shared;  // without records: every expert on this path
@@ -152,9 +200,6 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
     }
     if (!resolve_slot(blockIdx.y, a, s)) return;
   }
-  __shared__ uint8_t s_lds[GU_WPB][GU_LDS_PER_WAVE];
-  const int wave = threadIdx.x / kWave;
-  const int jp0 = (blockIdx.x * GU_WPB + wave) * 2 * GU_NP;
   if (jp0 >= a.I) return;
   if constexpr (SHORT)
     gateup_short<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
@@ -197,11 +242,30 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 namespace {
 
+// Compute units of the current device (looked up once per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 // routed: the gate/up grid has one more row (the routing writer).
 hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, const RouteOut& r,
                        bool routed, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
-  dim3 ggu((a.I + GU_PAIRS_PER_BLOCK - 1) / GU_PAIRS_PER_BLOCK, slots + (routed ? 1 : 0));
+  const int gx = (a.I + GU_PAIRS_PER_BLOCK - 1) / GU_PAIRS_PER_BLOCK;
+  int gy = slots;
+  if (routed) {   // as many rows of slots as stay resident with the writer row; blocks loop over the rest
+    const int fit = kGateupBlocksPerCu * device_cus() / gx - 1;
+    gy = (slots < fit ? slots : (fit > 1 ? fit : 1)) + 1;
+  }
+  dim3 ggu(gx, gy);
   dim3 bgu(GU_WPB * kWave);
   dim3 gdn((a.H + DN_ROWS_PER_BLOCK - 1) / DN_ROWS_PER_BLOCK, slots), bdn(DN_WPB * kWave);
   auto dn = (a.I <= DN_SHORT_I) ? down_kernel<true> : down_kernel<false>;

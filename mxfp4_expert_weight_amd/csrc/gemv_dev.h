@@ -101,6 +101,15 @@ __device__ __forceinline__ void token_of(const ForwardArgs& a, const ExpertSlot&
   }
 }
 
+// This lane's index, opaque to the optimiser: the per-lane offsets derived
+// from it are then computed where they are used, not hoisted out of a caller's
+// loop over experts into registers held across the whole loop.
+__device__ __forceinline__ int opaque_lane() {
+  int lane = threadIdx.x & (kWave - 1);
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
 // Copy `nbytes` contiguous bytes from global to this wave's LDS slice.
 __device__ __forceinline__ void wave_stage_bytes(const uint8_t* __restrict__ src, uint8_t* dst,
                                                  int nbytes, int lane) {
@@ -141,7 +150,7 @@ __device__ __forceinline__ void act_from(const uint4* row, int hc, uint32_t* a8)
 template <int NP, int HC>
 __device__ __forceinline__ void gateup_short(const ForwardArgs& a, const ExpertSlot& s, int jp0,
                                              uint8_t* s_lds) {
-  const int lane = threadIdx.x & (kWave - 1);
+  const int lane = opaque_lane();
   const int grp = lane >> 5, j32 = lane & 31;
   const int H = a.H, I = a.I;
   const int KH = H / 16;
