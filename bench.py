@@ -263,10 +263,11 @@ def main():
     weights = [d.weights() for d in sets]
 
     # one eager pass: loads the kernels and records each set's distinct-expert count
-    D = []
+    D, G = [], []
     for d, w in zip(sets, weights):
         run_layer(d, buf, w)
         D.append(int(buf.num_active.item()))
+        G.append(buf.header()["gemv_experts"])   # experts on the GEMV path (the timed kernel)
     log(f"[bench] distinct routed experts per set: min {min(D)} max {max(D)} mean {sum(D) / len(D):.2f}")
 
     def capture(n):
@@ -311,9 +312,11 @@ def main():
     log(f"[bench] {args.steps} steps in {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms): "
         f"{ms_per_step * 1e3:.2f} us/layer, {layer_gbs:.0f} GB/s")
 
-    # Roofline of the dominant kernel (gate/up: 2/3 of the expert bytes): per-launch
-    # durations from HIP events bound to that kernel's own begin/end timestamps,
-    # over the same K steps run eagerly on the stream the kernels use.
+    # Roofline of the GEMV gate/up kernel (the dominant kernel of the decode
+    # batches: 2/3 of the expert bytes): per-launch durations from HIP events
+    # bound to that kernel's own begin/end timestamps, over the same K steps run
+    # eagerly on the stream the kernels use.  Its bytes are those of the experts
+    # the header reports on the GEMV path (all of them for M <= 4).
     hev = HipEvents()
     n_ev = min(args.steps, 4000)
     starts = [hev.create() for _ in range(n_ev)]
@@ -330,8 +333,7 @@ def main():
     for e in starts + stops:
         hev.destroy(e)
     gu_ms = sum(spans) / n_ev
-    gu_bytes = sum((D[step_sets[i]] + int(wl.shared)) * gateup_bytes_per_expert(wl.H, wl.I)
-                   for i in range(n_ev)) / n_ev
+    gu_bytes = sum(G[step_sets[i]] * gateup_bytes_per_expert(wl.H, wl.I) for i in range(n_ev)) / n_ev
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
     log(f"[bench] gate/up kernel: {gu_ms * 1e3:.2f} us per launch, {gu_bytes / 1e6:.2f} MB, "
         f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
