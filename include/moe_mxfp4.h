@@ -11,9 +11,16 @@
  *
  * Conventions shared by every call
  *  - Pointers marked "device" are HIP device pointers owned by the caller; the
- *    library allocates nothing, keeps no state between calls and never copies
- *    device data to the host.  All work is enqueued on `stream` (a hipStream_t;
- *    NULL = the default stream) and is asynchronous; no call synchronises.
+ *    library allocates no device memory and never copies device data to the
+ *    host.  All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and is asynchronous; no call synchronises.  The one piece of state:
+ *    for batches of more than 4 tokens, moe_layer and moe_mxfp4_forward run the
+ *    matrix-core expert kernels on two helper streams of their own (made on the
+ *    first such call on a device, default priority), forked from and joined back
+ *    to `stream` with events, so the work stays ordered on `stream` and can be
+ *    captured into a HIP graph (if that first call is itself being captured,
+ *    every kernel is enqueued on `stream`).  Host threads enqueueing such calls
+ *    at the same time are serialised around the fork and join.
  *  - Argument checks run on the host before anything is enqueued and return a
  *    status; nothing is launched when a check fails.  MOE_ERR_HIP means a launch
  *    was rejected by the HIP runtime (e.g. no gfx950 device).  No call aborts,

@@ -1,6 +1,9 @@
 // C ABI of the MXFP4 MoE layer: host-side argument checks, then launches.
-// Nothing here allocates, synchronises or keeps state.
+// Nothing here allocates device memory or synchronises.  The only state is a
+// pair of helper streams per device (with their events), made on first use,
+// on which batches run their matrix-core expert kernels beside the GEMV ones.
 #include <climits>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -72,23 +75,81 @@ RecOut layer_recout(const ForwardArgs& a, void* workspace) {
                 const_cast<int2*>(a.items), reinterpret_cast<WorkspaceHeader*>(workspace), a.mt_min, a.mt_max};
 }
 
+// Two helper streams per device (default priority) and the events that fork
+// them from, and join them back to, the caller's stream.  Made on the first
+// call that needs them, unless that call's stream is being captured into a
+// graph (then the kernels go on the caller's stream in order).
+struct SideStreams {
+  hipStream_t mt, mfma;
+  hipEvent_t fork, zeroed, mt_done, mfma_done;
+};
+std::mutex g_side_mu;                // one fork/join sequence is enqueued at a time
+
+SideStreams* side_streams(hipStream_t s) {
+  constexpr int kMaxDevices = 64;
+  static SideStreams side[kMaxDevices];
+  static bool made[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (made[dev]) return &side[dev];
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  SideStreams& q = side[dev];
+  if (hipStreamCreateWithFlags(&q.mt, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipStreamCreateWithFlags(&q.mfma, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  for (hipEvent_t* ev : {&q.fork, &q.zeroed, &q.mt_done, &q.mfma_done})
+    if (hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess) return nullptr;
+  made[dev] = true;
+  return &q;
+}
+
 // The expert stage: GEMV gate/up (zeroes y) and down for the experts with
 // one or two tokens; with the few-token path on, its kernels take experts of
 // kMtMinTokens..kMtMaxTokens tokens; with the MFMA path on, x is quantised
 // first and the dense kernels take the experts listed in the work items.
+// The three paths touch disjoint experts and h rows, so the matrix-core
+// kernels run on the helper streams beside the GEMV ones; only their down
+// kernels wait, for the GEMV gate/up kernel that zeroes y.
 hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const bool mfma = a.mfma_min == kMfmaMinTokens;
   const bool mt = a.mt_min == kMtMinTokens;
   hipError_t e = hipSuccess;
-  if (mfma && (e = launch_forward_mfma_front(a, s)) != hipSuccess) return e;
-  if ((e = launch_forward(a, s, start, stop)) != hipSuccess) return e;
+  std::unique_lock<std::mutex> lock(g_side_mu);
+  SideStreams* q = (mt || mfma) ? side_streams(s) : nullptr;
+  if (!q) {
+    lock.unlock();
+    if (mfma && (e = launch_forward_mfma_front(a, s)) != hipSuccess) return e;
+    if ((e = launch_forward(a, s, start, stop)) != hipSuccess) return e;
+    if (mt) {
+      if ((e = launch_gateup_mt(a, s)) != hipSuccess) return e;
+      if ((e = launch_down_mt(a, s)) != hipSuccess) return e;
+    }
+    if (mfma) {
+      if ((e = launch_gateup_mfma(a, s)) != hipSuccess) return e;
+      if ((e = launch_down_mfma(a, s)) != hipSuccess) return e;
+    }
+    return e;
+  }
+  if ((e = hipEventRecord(q->fork, s)) != hipSuccess) return e;
+  if (mt && (e = hipStreamWaitEvent(q->mt, q->fork, 0)) != hipSuccess) return e;
+  if (mfma && (e = hipStreamWaitEvent(q->mfma, q->fork, 0)) != hipSuccess) return e;
+  if (mfma) {
+    if ((e = launch_forward_mfma_front(a, q->mfma)) != hipSuccess) return e;
+    if ((e = launch_gateup_mfma(a, q->mfma)) != hipSuccess) return e;
+  }
+  if (mt && (e = launch_gateup_mt(a, q->mt)) != hipSuccess) return e;
+  if ((e = launch_forward(a, s, start, stop, q->zeroed)) != hipSuccess) return e;
   if (mt) {
-    if ((e = launch_gateup_mt(a, s)) != hipSuccess) return e;
-    if ((e = launch_down_mt(a, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(q->mt, q->zeroed, 0)) != hipSuccess) return e;
+    if ((e = launch_down_mt(a, q->mt)) != hipSuccess) return e;
+    if ((e = hipEventRecord(q->mt_done, q->mt)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s, q->mt_done, 0)) != hipSuccess) return e;
   }
   if (mfma) {
-    if ((e = launch_gateup_mfma(a, s)) != hipSuccess) return e;
-    if ((e = launch_down_mfma(a, s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(q->mfma, q->zeroed, 0)) != hipSuccess) return e;
+    if ((e = launch_down_mfma(a, q->mfma)) != hipSuccess) return e;
+    if ((e = hipEventRecord(q->mfma_done, q->mfma)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s, q->mfma_done, 0)) != hipSuccess) return e;
   }
   return e;
 }

@@ -257,7 +257,7 @@ int device_cus() {
 
 // routed: the gate/up grid has one more row (the routing writer).
 hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, const RouteOut& r,
-                       bool routed, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+                       bool routed, hipStream_t s, hipEvent_t start, hipEvent_t stop, hipEvent_t mid = nullptr) {
   const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
   const int gx = (a.I + GU_PAIRS_PER_BLOCK - 1) / GU_PAIRS_PER_BLOCK;
   int gy = slots;
@@ -273,16 +273,18 @@ hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, 
   hipExtLaunchKernelGGL(gu, ggu, bgu, 0, s, start, stop, 0, a, r);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;   // y is zeroed from here on
   hipExtLaunchKernelGGL(dn, gdn, bdn, 0, s, nullptr, nullptr, 0, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                          hipEvent_t zeroed) {
   const RouteOut none{};
   return launch_pair(a.H <= GU_SHORT_H ? gateup_kernel<true, 0> : gateup_kernel<false, 0>, a, none, false, s,
-                     start, stop);
+                     start, stop, zeroed);
 }
 
 hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s, hipEvent_t start,

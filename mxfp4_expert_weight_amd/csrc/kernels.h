@@ -147,8 +147,10 @@ hipError_t launch_topk_softmax(const float* logits, int M, int E, int k, int* id
 hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int* sorted_pairs,
                                  int* active, int* num_active, hipStream_t s,
                                  RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0, 0, nullptr, nullptr, 0, 0});
+// GEMV experts: gate/up (which zeroes y; `zeroed`, if given, is recorded on s
+// right after it), then down.
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start = nullptr,
-                          hipEvent_t stop = nullptr);
+                          hipEvent_t stop = nullptr, hipEvent_t zeroed = nullptr);
 // Gate/up with the top-k and the expert sort done in every block from the
 // logits (M <= kRoutedMaxTokens), then down.
 hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s,

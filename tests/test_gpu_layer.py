@@ -169,3 +169,42 @@ def test_down_scale_doubling_doubles_output():
     g2, _, _ = _run(torch, ls2)
     rms = float(np.sqrt(np.mean(g["y"] ** 2)))
     assert np.all(np.abs(g2["y"] - 2 * g["y"]) <= 1e-5 * (np.abs(2 * g["y"]) + 2 * rms))
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_graph_replays_match_eager(fused):
+    """A HIP graph of the layer (as bench.py replays it) gives the eager result
+    on every replay.  The layer has GEMV, few-token and scaled-MFMA experts, so
+    the graph holds the helper streams' fork and join; eager work and host
+    synchronisations run between the replays."""
+    torch = need_gpu()
+    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer
+    wl = synth.custom("graph24x512x512", 24, 512, 512, 10, 3, True, "zipf", seed=1048)
+    ls = synth.layer_set(wl)
+    say(f"graph replay {wl.name} {'moe_layer' if fused else 'three calls'}")
+    d = DeviceLayerSet.from_host(ls)
+    b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
+    w = d.weights()
+    run_layer(d, b, w, fused=fused)
+    torch.cuda.synchronize()
+    eager = b.y.clone()
+    hdr = b.header()
+    assert hdr["mt_experts"] > 0 and hdr["mfma_experts"] > 0 and hdr["gemv_experts"] > 0, hdr
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_layer(d, b, w, fused=fused)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_layer(d, b, w, fused=fused)
+    rms = float(eager.pow(2).mean().sqrt())
+    for rep in range(4):
+        b.y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        diff = (b.y - eager).abs()
+        assert bool(torch.all(diff <= 1e-5 * (eager.abs() + rms))), f"replay {rep}: max diff {float(diff.max())}"
+        run_layer(d, b, w, fused=fused)            # eager work between replays
+        torch.cuda.synchronize()
