@@ -33,7 +33,7 @@ __global__ __launch_bounds__(128) void router_logits_kernel(const uint16_t* __re
     const float4 t = wrow[min(v, nvec - 1)];
     w[i] = (v < nvec) ? t : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  for (int t0 = 0; t0 < M; t0 += TB) {
+  for (int t0 = blockIdx.y * TB; t0 < M; t0 += gridDim.y * TB) {   // grid rows split the tokens
     uint2 xv[TB][VMAX];
 #pragma unroll
     for (int q = 0; q < TB; ++q) {
@@ -266,7 +266,11 @@ hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const 
     return hipGetLastError();
   }
   const int waves_per_block = 2;
-  dim3 grid((E + waves_per_block - 1) / waves_per_block), block(waves_per_block * kWave);
+  // one pass of up to 8 tokens per grid row, so a batch of up to 63 tokens
+  // runs on up to 8x more waves instead of looping in one wave per expert
+  // (long rows, H > 2560: one grid row, each wave loops over the tokens)
+  const int rows = (H <= 2560) ? (M + 7) / 8 : 1;
+  dim3 grid((E + waves_per_block - 1) / waves_per_block, rows), block(waves_per_block * kWave);
   if (H <= 2560) {
     if (M == 1)
       router_logits_kernel<10, 1><<<grid, block, 0, s>>>(x, w_router, bias, bias_stride, M, H, E, logits);

@@ -4,6 +4,12 @@
 
 namespace moe {
 
+// Whether the sort's outputs also fit in LDS next to its working set (64 KiB
+// per workgroup), for the records epilogue.
+__host__ __device__ inline bool sort_keeps_lds(int nw, int N, int E) {
+  return sizeof(int) * (sort_lds_ints(nw, E) + N + E + 1 + 4 * nw + 4) <= 65536;
+}
+
 __global__ __launch_bounds__(512) void sort_by_expert_kernel(const int* __restrict__ ids, int N, int E,
                                                              int ebits, int* __restrict__ offsets,
                                                              int* __restrict__ sorted_pairs,
@@ -11,11 +17,26 @@ __global__ __launch_bounds__(512) void sort_by_expert_kernel(const int* __restri
                                                              int* __restrict__ num_active,
                                                              RecOut ro) {
   extern __shared__ int lds[];
+  const int nw = blockDim.x / kWave;
+  const size_t base = sort_lds_ints(nw, E);
+  if (ro.rec && sort_keeps_lds(nw, N, E)) {
+    // the records epilogue reads the sort from LDS: sorted pairs, active list,
+    // D and the offsets left at lds + nw*E
+    int* sp = lds + base;
+    int* act = sp + N;
+    int* na = act + E;
+    int* scan = na + 1;
+    block_sort_pairs(ids, N, E, ebits, lds, offsets, sorted_pairs, active, num_active, sp, act, na);
+    __syncthreads();
+    block_write_slot_records(ro, E, max_slots(ro.M, ro.k, E), lds + (size_t)nw * E, sp, act, na, scan);
+    return;
+  }
   block_sort_pairs(ids, N, E, ebits, lds, offsets, sorted_pairs, active, num_active);
   if (ro.rec) {
     __threadfence_block();
     __syncthreads();
-    block_write_slot_records(ro, E, max_slots(ro.M, ro.k, E), offsets, sorted_pairs, active, num_active, lds);
+    block_write_slot_records(ro, E, max_slots(ro.M, ro.k, E), offsets, sorted_pairs, active, num_active,
+                             lds + base);
   }
 }
 
@@ -37,9 +58,10 @@ int expert_bits(int E) {
 
 hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int* sorted_pairs,
                                  int* active, int* num_active, hipStream_t s, RecOut ro) {
-  int nw = (N + 511) / 512;
-  nw = nw < 1 ? 1 : (nw > 8 ? 8 : nw);
-  const size_t shmem = sizeof(int) * sort_lds_ints(nw, E);
+  // 8 waves whatever N: the records epilogue has a slot per thread
+  const int nw = 8;
+  const size_t shmem =
+      sizeof(int) * (sort_lds_ints(nw, E) + (ro.rec && sort_keeps_lds(nw, N, E) ? N + E + 1 : 0) + 4 * nw + 4);
   sort_by_expert_kernel<<<1, nw * kWave, shmem, s>>>(ids, N, E, expert_bits(E), offsets, sorted_pairs,
                                                      active, num_active, ro);
   return hipGetLastError();

@@ -31,17 +31,13 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 }
 
 // Ints of LDS block_sort_pairs needs with nw waves and E experts.
-// (at least what the records epilogue then reuses: 4 * nw + 4)
-__host__ __device__ inline size_t sort_lds_ints(int nw, int E) {
-  const size_t sort = (size_t)nw * E + E + 2 * nw, rec = 4 * (size_t)nw + 4;
-  return sort > rec ? sort : rec;
-}
+__host__ __device__ inline size_t sort_lds_ints(int nw, int E) { return (size_t)nw * E + E + 1 + 2 * nw; }
 
 // Sort `N` pairs whose expert ids are ids[0..N) (global or LDS).  Uses
 // sort_lds_ints(nw, E) ints of LDS at `lds`; every thread of the block calls it.
 // With sp_lds / act_lds / na_lds non-null it also keeps sorted_pairs, the
 // active list and D in LDS (for an epilogue in the same block); the exclusive
-// offsets stay at lds + nw*E after the call.
+// offsets (E + 1 of them) stay at lds + nw*E after the call.
 __device__ inline void block_sort_pairs(const int* ids, int N, int E, int ebits, int* lds,
                                  int* __restrict__ offsets, int* __restrict__ sorted_pairs,
                                  int* __restrict__ active, int* __restrict__ num_active,
@@ -51,8 +47,8 @@ __device__ inline void block_sort_pairs(const int* ids, int N, int E, int ebits,
   const int lane = threadIdx.x & (kWave - 1);
   const int bd = blockDim.x;
   int* cnt = lds;                 // [nw][E]: per-wave counts, then per-wave running bases
-  int* off = cnt + nw * E;        // [E]: exclusive offsets of each expert
-  int* wtot = off + E;            // [2 * nw]: per-wave scan totals
+  int* off = cnt + nw * E;        // [E + 1]: exclusive offsets of each expert
+  int* wtot = off + E + 1;        // [2 * nw]: per-wave scan totals
 
   for (int i = threadIdx.x; i < nw * E; i += bd) cnt[i] = 0;
   __syncthreads();
@@ -100,6 +96,7 @@ __device__ inline void block_sort_pairs(const int* ids, int N, int E, int ebits,
   }
   if (threadIdx.x == bd - 1) {
     offsets[E] = cbase;            // == number of valid pairs
+    off[E] = cbase;
     *num_active = abase;
     if (na_lds) *na_lds = abase;
   }
@@ -167,9 +164,9 @@ __device__ __forceinline__ int expert_path(int n, int mt_min, int mt_max, int mf
   return n >= mfma_min ? 2 : (n >= mt_min && n <= mt_max) ? 1 : 0;
 }
 
-// Slot records from the finished sort in global memory (this block wrote it
-// and a barrier made it visible).  Thread i handles a contiguous span of
-// slots.  Then the path counters in the header and, with the MFMA path on,
+// Slot records from the finished sort (offsets with E + 1 entries, sorted
+// pairs, active list and D: in LDS, or in global memory this block wrote and a
+// barrier made visible).  Thread i handles a contiguous span of slots.  Then the path counters in the header and, with the MFMA path on,
 // its work items: (slot, 64-token tile) for every slot with at least
 // ro.mfma_min tokens, in slot order.  `lds` holds 4 * waves + 4 ints.
 __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nslots,
@@ -213,7 +210,8 @@ __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nsl
   }
   if (ro.items) {
     for (int slot = s0; slot < s1; ++slot) {
-      const SlotRec r = ro.rec[slot];
+      const SlotRec r = make_slot_record(slot, D, offsets, sorted_pairs, active, ro.topk_weights, ro.M, ro.k,
+                                         E, ro.has_shared);
       if (r.e < 0 || r.n < ro.mfma_min) continue;
       for (int t = 0; t * kMfmaTileTokens < r.n; ++t) ro.items[base++] = make_int2(slot, t);
     }
