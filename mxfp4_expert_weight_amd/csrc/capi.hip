@@ -67,12 +67,17 @@ ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
     a.hq_slo = reinterpret_cast<uint8_t*>(ws + L.hq_slo);
     a.items = reinterpret_cast<const int2*>(ws + L.items);
   }
+  if (combine_rows(M, top_k, a.H)) {
+    a.yp = reinterpret_cast<float*>(ws + L.yp);
+    a.inv = reinterpret_cast<const int*>(ws + L.inv);
+  }
   return a;
 }
 
 RecOut layer_recout(const ForwardArgs& a, void* workspace) {
   return RecOut{const_cast<SlotRec*>(a.rec), a.topk_weights, a.M, a.k, a.has_shared, a.mfma_min,
-                const_cast<int2*>(a.items), reinterpret_cast<WorkspaceHeader*>(workspace), a.mt_min, a.mt_max};
+                const_cast<int2*>(a.items), reinterpret_cast<WorkspaceHeader*>(workspace), a.mt_min, a.mt_max,
+                const_cast<int*>(a.inv)};
 }
 
 // Two helper streams per device (default priority) and the events that fork
@@ -108,11 +113,13 @@ SideStreams* side_streams(hipStream_t s) {
 // kMtMinTokens..kMtMaxTokens tokens; with the MFMA path on, x is quantised
 // first and the dense kernels take the experts listed in the work items.
 // The three paths touch disjoint experts and h rows, so the matrix-core
-// kernels run on the helper streams beside the GEMV ones; only their down
-// kernels wait, for the GEMV gate/up kernel that zeroes y.
+// kernels run on the helper streams beside the GEMV ones.  With atomics into
+// y, their down kernels wait for the GEMV gate/up kernel that zeroes y; when
+// combining by rows nothing waits, and the combine kernel runs after the join.
 hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   const bool mfma = a.mfma_min == kMfmaMinTokens;
   const bool mt = a.mt_min == kMtMinTokens;
+  const bool rows = a.yp != nullptr;
   hipError_t e = hipSuccess;
   std::unique_lock<std::mutex> lock(g_side_mu);
   SideStreams* q = (mt || mfma) ? side_streams(s) : nullptr;
@@ -128,6 +135,7 @@ hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start,
       if ((e = launch_gateup_mfma(a, s)) != hipSuccess) return e;
       if ((e = launch_down_mfma(a, s)) != hipSuccess) return e;
     }
+    if (rows) e = launch_combine_rows(a, s);
     return e;
   }
   if ((e = hipEventRecord(q->fork, s)) != hipSuccess) return e;
@@ -140,17 +148,18 @@ hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start,
   if (mt && (e = launch_gateup_mt(a, q->mt)) != hipSuccess) return e;
   if ((e = launch_forward(a, s, start, stop, q->zeroed)) != hipSuccess) return e;
   if (mt) {
-    if ((e = hipStreamWaitEvent(q->mt, q->zeroed, 0)) != hipSuccess) return e;
+    if (!rows && (e = hipStreamWaitEvent(q->mt, q->zeroed, 0)) != hipSuccess) return e;
     if ((e = launch_down_mt(a, q->mt)) != hipSuccess) return e;
     if ((e = hipEventRecord(q->mt_done, q->mt)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s, q->mt_done, 0)) != hipSuccess) return e;
   }
   if (mfma) {
-    if ((e = hipStreamWaitEvent(q->mfma, q->zeroed, 0)) != hipSuccess) return e;
+    if (!rows && (e = hipStreamWaitEvent(q->mfma, q->zeroed, 0)) != hipSuccess) return e;
     if ((e = launch_down_mfma(a, q->mfma)) != hipSuccess) return e;
     if ((e = hipEventRecord(q->mfma_done, q->mfma)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(s, q->mfma_done, 0)) != hipSuccess) return e;
   }
+  if (rows) e = launch_combine_rows(a, s);
   return e;
 }
 

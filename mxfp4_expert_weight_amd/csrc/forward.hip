@@ -143,7 +143,7 @@ __device__ __forceinline__ SlotRec route_slot(const ForwardArgs& a, const RouteS
 template <bool SHORT, int C>
 __global__ __launch_bounds__(GU_WPB * kWave) __attribute__((amdgpu_waves_per_eu(1, 3)))
 void gateup_kernel(ForwardArgs a, RouteOut r) {
-  {   // every block zeroes a share of y for the down kernel's scatter-add
+  if (!a.yp) {   // every block zeroes a share of y for the down kernel's scatter-add
     const size_t nblk = (size_t)gridDim.x * gridDim.y;
     const size_t b = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
     const size_t total = (size_t)a.M * a.H;
@@ -221,6 +221,31 @@ __global__ __launch_bounds__(DN_WPB * kWave) void down_kernel(ForwardArgs a) {
     down_long<DN_NR, DN_HC>(a, s, r0, s_lds[wave]);
 }
 
+// ------------------------------------------------------------- combine --
+// Combine by rows: thread (token t, 4 columns) sums the token's partial rows
+// in a fixed order -- its k routed pairs in slot order, then the shared
+// expert's row -- and writes y (deterministic, no atomics).
+__global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ yp,
+                                                           const int* __restrict__ inv, int M, int k, int H,
+                                                           int has_shared, float* __restrict__ y) {
+  const int t = blockIdx.y;
+  const int c4 = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c4 >= H / 4) return;
+  const float4* p4 = reinterpret_cast<const float4*>(yp);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < k; ++s) {
+    const int row = inv[(size_t)t * k + s];
+    if (row < 0) continue;
+    const float4 v = p4[(size_t)row * (H / 4) + c4];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  if (has_shared) {
+    const float4 v = p4[((size_t)M * k + t) * (H / 4) + c4];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(y)[(size_t)t * (H / 4) + c4] = acc;
+}
+
 // ------------------------------------------------------------- dequant --
 // One thread per 32-bit code word (8 elements): the same pair routine as the
 // expert kernels, widened from bf16 to fp32 (exact).
@@ -296,6 +321,12 @@ hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStr
   else
     gu = short_h ? gateup_kernel<true, 16> : gateup_kernel<false, 16>;
   return launch_pair(gu, a, r, true, s, start, stop);
+}
+
+hipError_t launch_combine_rows(const ForwardArgs& a, hipStream_t s) {
+  dim3 grid((a.H / 4 + 255) / 256, a.M);
+  combine_rows_kernel<<<grid, dim3(256), 0, s>>>(a.yp, a.inv, a.M, a.k, a.H, a.has_shared, a.y);
+  return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols, float* out,

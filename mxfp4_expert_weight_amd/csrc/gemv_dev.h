@@ -375,7 +375,12 @@ __device__ __forceinline__ void down_short(const ForwardArgs& a, const ExpertSlo
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       const float v = group_sum<16>(acc[q]);
-      if (j16 == 0) unsafeAtomicAdd(&a.y[(size_t)t * H + r0 + 4 * q + grp], wgt * v);
+      if (j16 == 0) {
+        if (a.yp)
+          a.yp[(size_t)hrow * H + r0 + 4 * q + grp] = wgt * v;
+        else
+          unsafeAtomicAdd(&a.y[(size_t)t * H + r0 + 4 * q + grp], wgt * v);
+      }
     }
   }
 }
@@ -421,7 +426,12 @@ __device__ __forceinline__ void down_long(const ForwardArgs& a, const ExpertSlot
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       const float v = group_sum<16>(acc[q]);
-      if (j16 == 0) unsafeAtomicAdd(&a.y[(size_t)t * H + r0 + 4 * q + grp], wgt * v);
+      if (j16 == 0) {
+        if (a.yp)
+          a.yp[(size_t)hrow * H + r0 + 4 * q + grp] = wgt * v;
+        else
+          unsafeAtomicAdd(&a.y[(size_t)t * H + r0 + 4 * q + grp], wgt * v);
+      }
     }
   }
 }

@@ -49,6 +49,11 @@ struct ForwardArgs {
   uint8_t *hq_hi, *hq_lo;     // [M*k + M][I] two-term MXFP8 codes of h (MFMA experts' rows)
   uint8_t *hq_shi, *hq_slo;   // [M*k + M][I/32]
   const int2* items;          // MFMA work items (slot, 64-token tile); count in hdr->mfma_items
+  // Combine by rows (large batches): the down kernels store w * (h . Wd) of
+  // every pair into its own row of yp (same row order as h) and a combine
+  // kernel sums each token's rows into y; null: fp32 atomics into y.
+  float* yp;                  // [M*k + M][H] (workspace)
+  const int* inv;             // [M*k]: sorted position of flattened pair t*k+s, -1 if dropped
 };
 
 // The few-token matrix-core path (mt.hip): batches of more than
@@ -79,8 +84,15 @@ __host__ __device__ inline int mfma_max_items(int M, int k) {
 // Workspace: header | slot records (one per possible active expert + shared) |
 // h | (MFMA path only) two-term MXFP8 x, two-term MXFP8 h, MFMA work items.
 __host__ __device__ inline int max_slots(int M, int k, int E) { return (E < M * k ? E : M * k) + 1; }
+// Combine by rows: batches of at least kCombineRowsMinTokens tokens whose
+// partial rows fit in kCombineRowsMaxBytes.
+constexpr int kCombineRowsMinTokens = 64;
+constexpr size_t kCombineRowsMaxBytes = size_t(1) << 30;
+inline bool combine_rows(int M, int k, int H) {
+  return M >= kCombineRowsMinTokens && ((size_t)M * k + M) * H * sizeof(float) <= kCombineRowsMaxBytes;
+}
 struct WorkspaceLayout {
-  size_t rec, h, xq_hi, xq_lo, xq_shi, xq_slo, hq_hi, hq_lo, hq_shi, hq_slo, items, total;
+  size_t rec, h, xq_hi, xq_lo, xq_shi, xq_slo, hq_hi, hq_lo, hq_shi, hq_slo, items, yp, inv, total;
 };
 inline WorkspaceLayout workspace_layout(int M, int k, int E, int H, int I) {
   WorkspaceLayout w{};
@@ -100,6 +112,10 @@ inline WorkspaceLayout workspace_layout(int M, int k, int E, int H, int I) {
     w.hq_slo = take(pairs * I / 32);
     w.items = take((size_t)mfma_max_items(M, k) * sizeof(int2));
   }
+  if (combine_rows(M, k, H)) {
+    w.yp = take(pairs * H * sizeof(float));
+    w.inv = take((size_t)M * k * sizeof(int));
+  }
   w.total = o;
   return w;
 }
@@ -114,6 +130,7 @@ struct RecOut {
   int2* items;                // MFMA work items (null when the path is off)
   WorkspaceHeader* hdr;
   int mt_min, mt_max;         // few-token matrix-core range (mt_min = INT_MAX: off)
+  int* inv;                   // null, or [M*k]: sorted position of each flattened pair (-1: dropped)
 };
 
 // Routing done inside the gate/up kernel (decode batches): where the logits
@@ -146,7 +163,7 @@ hipError_t launch_topk_softmax(const float* logits, int M, int E, int k, int* id
                                hipStream_t s);
 hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int* sorted_pairs,
                                  int* active, int* num_active, hipStream_t s,
-                                 RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0, 0, nullptr, nullptr, 0, 0});
+                                 RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0, 0, nullptr, nullptr, 0, 0, nullptr});
 // GEMV experts: gate/up (which zeroes y; `zeroed`, if given, is recorded on s
 // right after it), then down.
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start = nullptr,
@@ -166,6 +183,8 @@ hipError_t launch_down_mfma(const ForwardArgs& a, hipStream_t s);
 // Slot records and MFMA items from the sort outputs (one workgroup).
 hipError_t launch_records(const int* offsets, const int* sorted_pairs, const int* active, const int* num_active,
                           int E, RecOut ro, hipStream_t s);
+// y[t] = sum over s of yp[inv[t*k + s]] (+ yp[M*k + t] for the shared expert).
+hipError_t launch_combine_rows(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols, float* out,
                           hipStream_t st);
 

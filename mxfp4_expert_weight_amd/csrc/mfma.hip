@@ -344,9 +344,14 @@ __global__ __launch_bounds__(MF_WAVES * kWave) void down_mfma_kernel(ForwardArgs
           t = t0 + tc;
           w = 1.f;
         }
-        float* yr = a.y + (int64_t)t * a.H + r0 + 16 * wave + 4 * g;
+        if (a.yp) {
+          float* yr = a.yp + ((int64_t)rec.hrow0 + t0 + tc) * a.H + r0 + 16 * wave + 4 * g;
+          *reinterpret_cast<float4*>(yr) = make_float4(w * acc[s][0], w * acc[s][1], w * acc[s][2], w * acc[s][3]);
+        } else {
+          float* yr = a.y + (int64_t)t * a.H + r0 + 16 * wave + 4 * g;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) unsafeAtomicAdd(yr + r, w * acc[s][r]);
+          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(yr + r, w * acc[s][r]);
+        }
       }
     }
   }

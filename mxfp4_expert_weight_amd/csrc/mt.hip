@@ -148,7 +148,7 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
       accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(wu, s), b, accu, 0, 0, 0);
     }
     if (more) mt_stage_store(st.rows[cur ^ 1], srow, part, x0, x1);
-    __syncthreads();
+    block_barrier_lds();                         // the next chunk's weights stay in flight
     wg = ng;
     wu = nu;
   }
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(w1, s), b, acc1, 0, 0, 0);
     }
     if (more) mt_stage_store(st.rows[cur ^ 1], srow, part, x0, x1);
-    __syncthreads();
+    block_barrier_lds();
     w0 = n0;
     w1 = n1;
   }
@@ -212,11 +212,17 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
     int t;
     float w;
     mt_token(a, rec, j, t, w);
-    float* yr = a.y + (int64_t)t * H + rw + 4 * g;
+    if (a.yp) {
+      float* yr = a.yp + ((int64_t)rec.hrow0 + j) * H + rw + 4 * g;
+      *reinterpret_cast<float4*>(yr) = make_float4(w * acc0[0], w * acc0[1], w * acc0[2], w * acc0[3]);
+      *reinterpret_cast<float4*>(yr + 16) = make_float4(w * acc1[0], w * acc1[1], w * acc1[2], w * acc1[3]);
+    } else {
+      float* yr = a.y + (int64_t)t * H + rw + 4 * g;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      unsafeAtomicAdd(yr + r, w * acc0[r]);
-      unsafeAtomicAdd(yr + 16 + r, w * acc1[r]);
+      for (int r = 0; r < 4; ++r) {
+        unsafeAtomicAdd(yr + r, w * acc0[r]);
+        unsafeAtomicAdd(yr + 16 + r, w * acc1[r]);
+      }
     }
   }
 }

@@ -176,6 +176,13 @@ __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nsl
                                                 const int* __restrict__ num_active, int* lds) {
   const int D = *num_active;
   const int bd = blockDim.x, tid = threadIdx.x;
+  if (ro.inv) {   // sorted position of every flattened pair (-1: dropped id)
+    const int N = ro.M * ro.k, nvalid = offsets[E];
+    for (int i = tid; i < N; i += bd) ro.inv[i] = -1;
+    __threadfence_block();
+    __syncthreads();
+    for (int i = tid; i < nvalid; i += bd) ro.inv[sorted_pairs[i]] = i;
+  }
   const int per = (nslots + bd - 1) / bd;
   const int s0 = min(nslots, tid * per), s1 = min(nslots, s0 + per);
   int tiles = 0, cnt[3] = {0, 0, 0};

@@ -172,14 +172,16 @@ def test_down_scale_doubling_doubles_output():
 
 
 @pytest.mark.parametrize("fused", [True, False])
-def test_graph_replays_match_eager(fused):
+@pytest.mark.parametrize("M,E", [(24, 10), (96, 24)])
+def test_graph_replays_match_eager(fused, M, E):
     """A HIP graph of the layer (as bench.py replays it) gives the eager result
-    on every replay.  The layer has GEMV, few-token and scaled-MFMA experts, so
-    the graph holds the helper streams' fork and join; eager work and host
+    on every replay.  The layers have GEMV, few-token and scaled-MFMA experts, so
+    the graph holds the helper streams' fork and join (M = 96 also combines by
+    rows: partial rows per pair, then the combine kernel); eager work and host
     synchronisations run between the replays."""
     torch = need_gpu()
     from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer
-    wl = synth.custom("graph24x512x512", 24, 512, 512, 10, 3, True, "zipf", seed=1048)
+    wl = synth.custom(f"graph{M}x512x512", M, 512, 512, E, 3, True, "zipf", seed=1048 + M)
     ls = synth.layer_set(wl)
     say(f"graph replay {wl.name} {'moe_layer' if fused else 'three calls'}")
     d = DeviceLayerSet.from_host(ls)
