@@ -86,7 +86,7 @@ __host__ __device__ inline int mfma_max_items(int M, int k) {
 __host__ __device__ inline int max_slots(int M, int k, int E) { return (E < M * k ? E : M * k) + 1; }
 // Combine by rows: batches of at least kCombineRowsMinTokens tokens whose
 // partial rows fit in kCombineRowsMaxBytes.
-constexpr int kCombineRowsMinTokens = 64;
+constexpr int kCombineRowsMinTokens = 16;
 constexpr size_t kCombineRowsMaxBytes = size_t(1) << 30;
 inline bool combine_rows(int M, int k, int H) {
   return M >= kCombineRowsMinTokens && ((size_t)M * k + M) * H * sizeof(float) <= kCombineRowsMaxBytes;
