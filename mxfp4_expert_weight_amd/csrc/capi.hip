@@ -71,13 +71,14 @@ ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
     a.yp = reinterpret_cast<float*>(ws + L.yp);
     a.inv = reinterpret_cast<const int*>(ws + L.inv);
   }
+  if (M > kRoutedMaxTokens) a.lists = reinterpret_cast<const int*>(ws + L.lists);
   return a;
 }
 
 RecOut layer_recout(const ForwardArgs& a, void* workspace) {
   return RecOut{const_cast<SlotRec*>(a.rec), a.topk_weights, a.M, a.k, a.has_shared, a.mfma_min,
                 const_cast<int2*>(a.items), reinterpret_cast<WorkspaceHeader*>(workspace), a.mt_min, a.mt_max,
-                const_cast<int*>(a.inv)};
+                const_cast<int*>(a.inv), const_cast<int*>(a.lists)};
 }
 
 // Two helper streams per device (default priority) and the events that fork
@@ -138,15 +139,17 @@ hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start,
     if (rows) e = launch_combine_rows(a, s);
     return e;
   }
+  // the GEMV kernels go first (their few workgroups are then not queued
+  // behind the matrix-core paths' many); the fork point is before them
   if ((e = hipEventRecord(q->fork, s)) != hipSuccess) return e;
+  if ((e = launch_forward(a, s, start, stop, q->zeroed)) != hipSuccess) return e;
   if (mt && (e = hipStreamWaitEvent(q->mt, q->fork, 0)) != hipSuccess) return e;
   if (mfma && (e = hipStreamWaitEvent(q->mfma, q->fork, 0)) != hipSuccess) return e;
+  if (mt && (e = launch_gateup_mt(a, q->mt)) != hipSuccess) return e;
   if (mfma) {
     if ((e = launch_forward_mfma_front(a, q->mfma)) != hipSuccess) return e;
     if ((e = launch_gateup_mfma(a, q->mfma)) != hipSuccess) return e;
   }
-  if (mt && (e = launch_gateup_mt(a, q->mt)) != hipSuccess) return e;
-  if ((e = launch_forward(a, s, start, stop, q->zeroed)) != hipSuccess) return e;
   if (mt) {
     if (!rows && (e = hipStreamWaitEvent(q->mt, q->zeroed, 0)) != hipSuccess) return e;
     if ((e = launch_down_mt(a, q->mt)) != hipSuccess) return e;
@@ -243,13 +246,15 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int3
   hipStream_t s = (hipStream_t)stream;
   ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
                              num_active, y, workspace);
-  if (a.mfma_min == kMfmaMinTokens || a.mt_min == kMtMinTokens) {
-    // the path choice needs per-expert token counts: records (and MFMA items) first
+  if (a.mfma_min == kMfmaMinTokens || a.mt_min == kMtMinTokens || a.yp) {
+    // the path choice needs per-expert token counts, the combine the pairs'
+    // sorted positions: records (slot lists, MFMA items, positions) first
     const RecOut ro = layer_recout(a, workspace);
     if (launch_records(expert_offsets, sorted_pairs, active_experts, num_active, a.E, ro, s) != hipSuccess)
       return MOE_ERR_HIP;
   } else {
     a.rec = nullptr;                 // few tokens: resolved from the sort outputs directly
+    a.lists = nullptr;
   }
   return hip_status(launch_experts(a, s, nullptr, nullptr));
 }
@@ -289,6 +294,7 @@ moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float
                      num_active, rec, expert_bits(E)};
     return hip_status(launch_forward_routed(a, r, s, start, stop));
   }
+  if (topk_sort_fits_one_block(M)) a.lists = nullptr;   // the one-workgroup sort writes records only
   const RecOut ro = layer_recout(a, workspace);
   hipError_t e;
   if (topk_sort_fits_one_block(M)) {

@@ -143,7 +143,8 @@ __device__ __forceinline__ SlotRec route_slot(const ForwardArgs& a, const RouteS
 template <bool SHORT, int C>
 __global__ __launch_bounds__(GU_WPB * kWave) __attribute__((amdgpu_waves_per_eu(1, 3)))
 void gateup_kernel(ForwardArgs a, RouteOut r) {
-  if (!a.yp) {   // every block zeroes a share of y for the down kernel's scatter-add
+  if (C > 0 || !a.yp) {   // every block zeroes a share of y for the down kernel's scatter-add
+                          // (decode batches never combine by rows)
     const size_t nblk = (size_t)gridDim.x * gridDim.y;
     const size_t b = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
     const size_t total = (size_t)a.M * a.H;
@@ -198,7 +199,12 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
       a.hdr->mfma_items = 0;
       a.hdr->mt_experts = 0;
     }
-    if (!resolve_slot(blockIdx.y, a, s)) return;
+    if (a.lists) {   // grid row y takes the y-th GEMV expert (rows past them exit)
+      if ((int)blockIdx.y >= a.hdr->gemv_experts) return;
+      resolve_slot(a.lists[blockIdx.y], a, s);
+    } else if (!resolve_slot(blockIdx.y, a, s)) {
+      return;
+    }
   }
   if (jp0 >= a.I) return;
   if constexpr (SHORT)
@@ -207,18 +213,23 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
     gateup_long<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
 }
 
-template <bool SHORT>
+template <bool SHORT, bool ROWS>
 __global__ __launch_bounds__(DN_WPB * kWave) void down_kernel(ForwardArgs a) {
   ExpertSlot s;
-  if (!resolve_slot(blockIdx.y, a, s)) return;
   __shared__ uint8_t s_lds[DN_WPB][DN_LDS_PER_WAVE];
   const int wave = threadIdx.x / kWave;
   const int r0 = (blockIdx.x * DN_WPB + wave) * 4 * DN_NR;
+  if (a.lists) {     // grid row y takes the y-th GEMV expert (rows past them exit)
+    if ((int)blockIdx.y >= a.hdr->gemv_experts) return;
+    resolve_slot(a.lists[blockIdx.y], a, s);
+  } else if (!resolve_slot(blockIdx.y, a, s)) {
+    return;
+  }
   if (r0 >= a.H) return;
   if constexpr (SHORT)
-    down_short<DN_NR, DN_HC>(a, s, r0, s_lds[wave]);
+    down_short<DN_NR, DN_HC, ROWS>(a, s, r0, s_lds[wave]);
   else
-    down_long<DN_NR, DN_HC>(a, s, r0, s_lds[wave]);
+    down_long<DN_NR, DN_HC, ROWS>(a, s, r0, s_lds[wave]);
 }
 
 // ------------------------------------------------------------- combine --
@@ -293,7 +304,8 @@ hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, 
   dim3 ggu(gx, gy);
   dim3 bgu(GU_WPB * kWave);
   dim3 gdn((a.H + DN_ROWS_PER_BLOCK - 1) / DN_ROWS_PER_BLOCK, slots), bdn(DN_WPB * kWave);
-  auto dn = (a.I <= DN_SHORT_I) ? down_kernel<true> : down_kernel<false>;
+  auto dn = (a.I <= DN_SHORT_I) ? (a.yp ? down_kernel<true, true> : down_kernel<true, false>)
+                                : (a.yp ? down_kernel<false, true> : down_kernel<false, false>);
   // with events, they take the gate/up kernel's own begin/end timestamps
   hipExtLaunchKernelGGL(gu, ggu, bgu, 0, s, start, stop, 0, a, r);
   hipError_t err = hipGetLastError();

@@ -303,7 +303,9 @@ __device__ __forceinline__ void gateup_long(const ForwardArgs& a, const ExpertSl
 // expert s's down projection for all of its tokens (lane group g = lane/16
 // takes rows r0 + g + 4q) and adds w * (h . Wd[r]) into y[t][r].  Same issue
 // order as gateup_short: first h row, scales, then codes chunk by chunk.
-template <int NR, int HC>
+// ROWS: store into the pair's partial row of yp (combine by rows) instead of
+// adding into y.
+template <int NR, int HC, bool ROWS>
 __device__ __forceinline__ void down_short(const ForwardArgs& a, const ExpertSlot& s, int r0,
                                            uint8_t* s_lds) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -376,7 +378,7 @@ __device__ __forceinline__ void down_short(const ForwardArgs& a, const ExpertSlo
     for (int q = 0; q < NR; ++q) {
       const float v = group_sum<16>(acc[q]);
       if (j16 == 0) {
-        if (a.yp)
+        if constexpr (ROWS)
           a.yp[(size_t)hrow * H + r0 + 4 * q + grp] = wgt * v;
         else
           unsafeAtomicAdd(&a.y[(size_t)t * H + r0 + 4 * q + grp], wgt * v);
@@ -386,7 +388,7 @@ __device__ __forceinline__ void down_short(const ForwardArgs& a, const ExpertSlo
 }
 
 // Long rows (any I): K passes per token.
-template <int NR, int HC>
+template <int NR, int HC, bool ROWS>
 __device__ __forceinline__ void down_long(const ForwardArgs& a, const ExpertSlot& s, int r0,
                                           uint8_t* s_lds) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -427,7 +429,7 @@ __device__ __forceinline__ void down_long(const ForwardArgs& a, const ExpertSlot
     for (int q = 0; q < NR; ++q) {
       const float v = group_sum<16>(acc[q]);
       if (j16 == 0) {
-        if (a.yp)
+        if constexpr (ROWS)
           a.yp[(size_t)hrow * H + r0 + 4 * q + grp] = wgt * v;
         else
           unsafeAtomicAdd(&a.y[(size_t)t * H + r0 + 4 * q + grp], wgt * v);

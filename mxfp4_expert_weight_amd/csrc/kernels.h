@@ -54,6 +54,10 @@ struct ForwardArgs {
   // kernel sums each token's rows into y; null: fp32 atomics into y.
   float* yp;                  // [M*k + M][H] (workspace)
   const int* inv;             // [M*k]: sorted position of flattened pair t*k+s, -1 if dropped
+  // Slot lists (batches with records): the GEMV experts' slots at lists[0..),
+  // the few-token experts' at lists[max_slots..), counts in the header; the
+  // kernels of those paths loop over them instead of a grid row per slot.
+  const int* lists;
 };
 
 // The few-token matrix-core path (mt.hip): batches of more than
@@ -92,7 +96,7 @@ inline bool combine_rows(int M, int k, int H) {
   return M >= kCombineRowsMinTokens && ((size_t)M * k + M) * H * sizeof(float) <= kCombineRowsMaxBytes;
 }
 struct WorkspaceLayout {
-  size_t rec, h, xq_hi, xq_lo, xq_shi, xq_slo, hq_hi, hq_lo, hq_shi, hq_slo, items, yp, inv, total;
+  size_t rec, h, xq_hi, xq_lo, xq_shi, xq_slo, hq_hi, hq_lo, hq_shi, hq_slo, items, yp, inv, lists, total;
 };
 inline WorkspaceLayout workspace_layout(int M, int k, int E, int H, int I) {
   WorkspaceLayout w{};
@@ -116,6 +120,7 @@ inline WorkspaceLayout workspace_layout(int M, int k, int E, int H, int I) {
     w.yp = take(pairs * H * sizeof(float));
     w.inv = take((size_t)M * k * sizeof(int));
   }
+  if (M > kRoutedMaxTokens) w.lists = take(2 * (size_t)max_slots(M, k, E) * sizeof(int));
   w.total = o;
   return w;
 }
@@ -131,6 +136,7 @@ struct RecOut {
   WorkspaceHeader* hdr;
   int mt_min, mt_max;         // few-token matrix-core range (mt_min = INT_MAX: off)
   int* inv;                   // null, or [M*k]: sorted position of each flattened pair (-1: dropped)
+  int* lists;                 // null, or [2][max_slots]: slots of the GEMV / few-token experts
 };
 
 // Routing done inside the gate/up kernel (decode batches): where the logits
@@ -163,7 +169,7 @@ hipError_t launch_topk_softmax(const float* logits, int M, int E, int k, int* id
                                hipStream_t s);
 hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int* sorted_pairs,
                                  int* active, int* num_active, hipStream_t s,
-                                 RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0, 0, nullptr, nullptr, 0, 0, nullptr});
+                                 RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0, 0, nullptr, nullptr, 0, 0, nullptr, nullptr});
 // GEMV experts: gate/up (which zeroes y; `zeroed`, if given, is recorded on s
 // right after it), then down.
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start = nullptr,

@@ -43,9 +43,16 @@ __device__ __forceinline__ void mt_token(const ForwardArgs& a, const SlotRec& r,
   }
 }
 
-// The slot belongs to this path.
-__device__ __forceinline__ bool mt_slot(const ForwardArgs& a, int slot, SlotRec& r) {
-  r = a.rec[slot];
+// The record of grid row y, if its expert is on this path: with the slot
+// list, row y takes the y-th few-token expert (rows past them exit); without
+// it, row y is slot y.
+__device__ __forceinline__ bool mt_slot(const ForwardArgs& a, int y, SlotRec& r) {
+  if (a.lists) {
+    if (y >= a.hdr->mt_experts) return false;
+    r = a.rec[a.lists[max_slots(a.M, a.k, a.E) + y]];
+    return true;
+  }
+  r = a.rec[y];
   return r.e >= 0 && r.n >= a.mt_min && r.n <= a.mt_max && r.n < a.mfma_min;
 }
 

@@ -166,7 +166,9 @@ __device__ __forceinline__ int expert_path(int n, int mt_min, int mt_max, int mf
 
 // Slot records from the finished sort (offsets with E + 1 entries, sorted
 // pairs, active list and D: in LDS, or in global memory this block wrote and a
-// barrier made visible).  Thread i handles a contiguous span of slots.  Then the path counters in the header and, with the MFMA path on,
+// barrier made visible).  Thread i handles a contiguous span of slots.  With
+// ro.lists: the slots of the GEMV experts at lists[0..), of the few-token
+// experts at lists[nslots..), in slot order.  Then the path counters in the header and, with the MFMA path on,
 // its work items: (slot, 64-token tile) for every slot with at least
 // ro.mfma_min tokens, in slot order.  `lds` holds 4 * waves + 4 ints.
 __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nslots,
@@ -209,11 +211,26 @@ __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nsl
     for (int p = 0; p < 3; ++p) lds[nw * (p + 1) + w] = csum[p];
   }
   __syncthreads();
-  int base = inc - tiles, tot[3] = {0, 0, 0};
+  int base = inc - tiles, tot[3] = {0, 0, 0}, pbase[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) pbase[p] = csum[p] - cnt[p];
   for (int v = 0; v < nw; ++v) {
     if (v < w) base += lds[v];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) tot[p] += lds[nw * (p + 1) + v];
+    for (int p = 0; p < 3; ++p) {
+      tot[p] += lds[nw * (p + 1) + v];
+      if (v < w) pbase[p] += lds[nw * (p + 1) + v];
+    }
+  }
+  if (ro.lists) {   // the GEMV and few-token experts' slots, each list in slot order
+    for (int slot = s0; slot < s1; ++slot) {
+      const SlotRec r = make_slot_record(slot, D, offsets, sorted_pairs, active, ro.topk_weights, ro.M, ro.k,
+                                         E, ro.has_shared);
+      if (r.e < 0) continue;
+      const int path = expert_path(r.n, ro.mt_min, ro.mt_max, ro.mfma_min);
+      if (path == 0) ro.lists[pbase[0]++] = slot;
+      if (path == 1) ro.lists[nslots + pbase[1]++] = slot;
+    }
   }
   if (ro.items) {
     for (int slot = s0; slot < s1; ++slot) {
