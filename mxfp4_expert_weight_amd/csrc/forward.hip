@@ -45,9 +45,11 @@ struct RouteState {           // per-wave: this wave's copy of the pairs and the
 };
 
 // Returns false for the writer (after writing the routing outputs).
-template <int C>
+// `before_barrier` runs in every thread after the top-k, before the block
+// barrier that publishes it (the caller stores its staged activations there).
+template <int C, class Pre>
 __device__ __forceinline__ bool route_prepare(const ForwardArgs& a, const RouteOut& r, RouteState& rs,
-                                              bool writer) {
+                                              bool writer, Pre before_barrier) {
   constexpr int kWords = MOE_MAX_EXPERTS / 32;           // bitmap words; index kWords is a sink
   __shared__ SmallSortLds<C, kRoutedMaxPairs> L;
   __shared__ uint32_t bits[GU_WPB][kWords + 1];
@@ -64,6 +66,7 @@ __device__ __forceinline__ bool route_prepare(const ForwardArgs& a, const RouteO
       L.tok[t * a.k + lane] = t;
     }
   }
+  before_barrier();
   __syncthreads();
   if (writer) {
     if (wave == 0) wave_sort_small(L, N, E, r.ebits);
@@ -159,8 +162,29 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
     // once, however many slots it takes); the last row is the writer
     const bool writer = blockIdx.y == gridDim.y - 1;
     if (writer && blockIdx.x != 0) return;
+    // short rows: every token's activations are staged in LDS for the GEMVs;
+    // the loads are issued before the top-k, whose logits wait covers them
+    constexpr int kXVec = kRoutedMaxTokens * GU_SHORT_H / 8;      // uint4 of x, at most
+    constexpr int kXPer = (kXVec + GU_WPB * kWave - 1) / (GU_WPB * kWave);
+    __shared__ uint4 s_x[SHORT ? kXVec : 1];
+    uint4 xs[SHORT ? kXPer : 1];
+    const int nxv = SHORT ? a.M * a.H / 8 : 0;
+    if constexpr (SHORT) {
+      const uint4* x4 = reinterpret_cast<const uint4*>(a.x);
+#pragma unroll
+      for (int q = 0; q < kXPer; ++q) xs[q] = x4[min((int)threadIdx.x + q * GU_WPB * kWave, nxv - 1)];
+    }
+    auto stage_x = [&]() {
+      if constexpr (SHORT) {
+#pragma unroll
+        for (int q = 0; q < kXPer; ++q) {
+          const int i = threadIdx.x + q * GU_WPB * kWave;
+          if (i < nxv) s_x[i] = xs[q];
+        }
+      }
+    };
     RouteState rs;
-    if (!route_prepare<C>(a, r, rs, writer)) return;     // uniform over the block
+    if (!route_prepare<C>(a, r, rs, writer, stage_x)) return;     // uniform over the block
     // this block's slots: blockIdx.y, + rows, + 2 rows, ...  Their records are
     // looked up first (one wave per slot) and parked in LDS, so no routing
     // state stays live in registers through the GEMVs.
@@ -186,7 +210,7 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
       for (int q = 0; q < kRecTokens; ++q) { s.tok[q] = rec.tok[q]; s.w[q] = rec.w[q]; }
       if (jp0 < a.I) {
         if constexpr (SHORT)
-          gateup_short<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
+          gateup_short<GU_NP, GU_HC, true>(a, s, jp0, s_lds[wave], reinterpret_cast<const uint16_t*>(s_x));
         else
           gateup_long<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
       }

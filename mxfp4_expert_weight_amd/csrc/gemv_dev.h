@@ -147,9 +147,12 @@ __device__ __forceinline__ void act_from(const uint4* row, int hc, uint32_t* a8)
 // issue order, so a wave issues, in this order: the first token's activations
 // (L2), its rows' scale bytes, then the weight codes chunk by chunk in the order
 // the math consumes them -- each chunk is computed as soon as it has landed.
-template <int NP, int HC>
+// XL: the tokens' activations come from LDS (xl = bf16 [M][H], staged by the
+// caller), read chunk by chunk as the products need them, so they hold no
+// registers while the weight codes are in flight.
+template <int NP, int HC, bool XL = false>
 __device__ __forceinline__ void gateup_short(const ForwardArgs& a, const ExpertSlot& s, int jp0,
-                                             uint8_t* s_lds) {
+                                             uint8_t* s_lds, const uint16_t* xl = nullptr) {
   const int lane = opaque_lane();
   const int grp = lane >> 5, j32 = lane & 31;
   const int H = a.H, I = a.I;
@@ -163,7 +166,7 @@ __device__ __forceinline__ void gateup_short(const ForwardArgs& a, const ExpertS
   for (int i = 0; i < HC; ++i) hcc[i] = min(j32 + 32 * i, KH - 1);
 
   uint4 xv[HC][2];
-  {
+  if constexpr (!XL) {
     const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)s.tok[0] * H);
 #pragma unroll
     for (int i = 0; i < HC; ++i) { xv[i][0] = xr[2 * hcc[i]]; xv[i][1] = xr[2 * hcc[i] + 1]; }
@@ -213,19 +216,25 @@ __device__ __forceinline__ void gateup_short(const ForwardArgs& a, const ExpertS
       for (int i = 0; i < HC; ++i) { keep_in_loop(cg[p][i]); keep_in_loop(cu[p][i]); }
     int t, hrow; float wgt;
     token_of(a, s, q, t, wgt, hrow);
-    if (q > 0) {                                   // later tokens' activations (L2)
+    if (!XL && q > 0) {                            // later tokens' activations (L2)
       const uint4* xr = reinterpret_cast<const uint4*>(a.x + (size_t)t * H);
 #pragma unroll
       for (int i = 0; i < HC; ++i) { xv[i][0] = xr[2 * hcc[i]]; xv[i][1] = xr[2 * hcc[i] + 1]; }
     }
+    const uint4* xlr = reinterpret_cast<const uint4*>(xl + (size_t)t * H);
     float accg[NP], accu[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) { accg[p] = 0.f; accu[p] = 0.f; }
 #pragma unroll
     for (int i = 0; i < HC; ++i) {
       uint32_t xa[8];
-      unpack8(xv[i][0], xa);
-      unpack8(xv[i][1], xa + 4);
+      if constexpr (XL) {
+        unpack8(xlr[2 * hcc[i]], xa);
+        unpack8(xlr[2 * hcc[i] + 1], xa + 4);
+      } else {
+        unpack8(xv[i][0], xa);
+        unpack8(xv[i][1], xa + 4);
+      }
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         accg[p] = dot8_mxfp4_bf16(cg[p][i].x, sg[p][i], xa, accg[p]);
