@@ -4,10 +4,11 @@
 
 namespace moe {
 
-// Whether the sort's outputs also fit in LDS next to its working set (64 KiB
-// per workgroup), for the records epilogue.
+// Whether the sort's outputs (and a copy of its input ids) also fit in LDS
+// next to its working set (64 KiB per workgroup), for the records epilogue.
+__host__ __device__ inline size_t sort_lds_extra(int nw, int N, int E) { return 2 * (size_t)N + E + 1 + 4 * nw + 4; }
 __host__ __device__ inline bool sort_keeps_lds(int nw, int N, int E) {
-  return sizeof(int) * (sort_lds_ints(nw, E) + N + E + 1 + 4 * nw + 4) <= 65536;
+  return sizeof(int) * (sort_lds_ints(nw, E) + sort_lds_extra(nw, N, E)) <= 65536;
 }
 
 __global__ __launch_bounds__(512) void sort_by_expert_kernel(const int* __restrict__ ids, int N, int E,
@@ -26,7 +27,21 @@ __global__ __launch_bounds__(512) void sort_by_expert_kernel(const int* __restri
     int* act = sp + N;
     int* na = act + E;
     int* scan = na + 1;
-    block_sort_pairs(ids, N, E, ebits, lds, offsets, sorted_pairs, active, num_active, sp, act, na);
+    int* ids_l = scan + 4 * nw + 4;
+    // the ids are read twice (histogram, placement): one coalesced copy first,
+    // so neither pass waits on global loads step by step
+    for (int i0 = 0; i0 < N; i0 += 8 * blockDim.x) {    // 8 loads in flight per thread
+      int v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = ids[min(i0 + q * (int)blockDim.x + (int)threadIdx.x, N - 1)];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = i0 + q * blockDim.x + threadIdx.x;
+        if (i < N) ids_l[i] = v[q];
+      }
+    }
+    __syncthreads();
+    block_sort_pairs(ids_l, N, E, ebits, lds, offsets, sorted_pairs, active, num_active, sp, act, na);
     __syncthreads();
     block_write_slot_records(ro, E, max_slots(ro.M, ro.k, E), lds + (size_t)nw * E, sp, act, na, scan);
     return;
@@ -61,7 +76,7 @@ hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int
   // 8 waves whatever N: the records epilogue has a slot per thread
   const int nw = 8;
   const size_t shmem =
-      sizeof(int) * (sort_lds_ints(nw, E) + (ro.rec && sort_keeps_lds(nw, N, E) ? N + E + 1 : 0) + 4 * nw + 4);
+      sizeof(int) * (sort_lds_ints(nw, E) + (ro.rec && sort_keeps_lds(nw, N, E) ? sort_lds_extra(nw, N, E) : 4 * nw + 4));
   sort_by_expert_kernel<<<1, nw * kWave, shmem, s>>>(ids, N, E, expert_bits(E), offsets, sorted_pairs,
                                                      active, num_active, ro);
   return hipGetLastError();
