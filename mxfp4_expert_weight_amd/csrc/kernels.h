@@ -154,7 +154,8 @@ struct RouteOut {
 };
 constexpr int kRoutedMaxPairs = kRoutedMaxTokens * MOE_MAX_TOPK;
 
-// Batches of at least this many tokens take the tiled router GEMM.
+// Batches of at least this many tokens take the matrix-core router (weights
+// split exactly into three bf16 parts).
 constexpr int kRouterGemmMinTokens = 64;
 hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias,
                                 int64_t bias_stride, int M, int H, int E, float* logits, hipStream_t s);

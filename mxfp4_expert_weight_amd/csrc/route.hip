@@ -65,133 +65,153 @@ __global__ __launch_bounds__(128) void router_logits_kernel(const uint16_t* __re
   }
 }
 
-// Batches: a tiled fp32 GEMM.  Workgroup = 32 tokens x TE experts, thread
-// (ty, tx) of 16 x 16 owns tokens {ty, ty + 16} and experts {tx + 16 j}.
-// K runs in 128-element chunks staged in LDS (x widened to fp32), double
-// buffered, so each memory round trip carries 4 KB per thread row group.
-// Each logit is summed in 16-product leaves, 16 leaves per group, then the
-// groups in order: the longest chain of fp32 roundings is
-// 16 + 16 + ceil(H/256) + 1 (bias), 43 at H = 2560 -- no longer than the
-// small-batch kernel's H/64 + 6 + 1.
-constexpr int RG_TT = 32, RG_KC = 128, RG_PITCH = RG_KC + 4;
-template <int TE>
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+// Batches on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16).  Each fp32
+// router weight is split exactly into three bf16 parts by truncation:
+// w1 = w with its low 16 bits cleared, w2 = (w - w1) the same way, w3 = the
+// rest (at most 8 significant bits, so exact in bf16).  x is bf16, so every
+// product x * w_j is exact in fp32 and the logit is the plain sum of 3H exact
+// products; only the summation order differs from the fp32 definition.  Each
+// 32-product matrix-core dot starts from zero (a leaf); per weight part, 16
+// leaves add into a group; the groups add into the total in K order, and the
+// last partial groups and the bias follow, so a logit's longest rounding chain
+// is 32 (leaf) + 16 (group) + 3 ceil(H / 512) (total) + 3 + 1.
+// Workgroup = 32 tokens x 32 experts, wave w = the 16 x 16 tile
+// (tokens 16 (w / 2), experts 16 (w % 2)); K runs in LDS-staged chunks of
+// 256, double-buffered (70 KB of LDS: one workgroup per CU).
+typedef __bf16 rv8bf __attribute__((ext_vector_type(8)));
+typedef float rv4f __attribute__((ext_vector_type(4)));
+constexpr int RM_T = 32, RM_E = 32, RM_KC = 256, RM_PITCH = RM_KC + 8;   // bf16 elements per LDS row
+constexpr int RM_WAVES = 4, RM_THREADS = RM_WAVES * 64;
+constexpr int RM_TPR = RM_THREADS / RM_T;      // staging threads per row (8)
+constexpr int RM_G = RM_KC / 8 / RM_TPR;       // 8-element groups per staging thread and chunk (4)
+// NK > 0: H is exactly NK chunks and the chunk loop is unrolled (the waits
+// for the prefetched chunks are then exact; a runtime loop makes the compiler
+// wait for every outstanding load at its back edge).  NK = 0: any H.
+template <int NK>
+__global__ __launch_bounds__(RM_THREADS) void router_mfma_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ w_router,
                                                           const float* __restrict__ bias, int64_t bias_stride,
                                                           int M, int H, int E, float* __restrict__ logits) {
-  constexpr int NE = TE / 16;
-  constexpr int WQ = TE * RG_KC / 4 / 256;      // float4s of W each thread stages per chunk
-  __shared__ __align__(16) float xs[2][RG_TT][RG_PITCH];
-  __shared__ __align__(16) float wsh[2][TE][RG_PITCH];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int t0 = blockIdx.y * RG_TT, e0 = blockIdx.x * TE;
-  // x staging: thread -> row tid/8, 16 bf16 at column (tid%8)*16
-  const int xr_row = tid >> 3, xr_col = (tid & 7) * 16;
-  const bool xv = t0 + xr_row < M;
-  const uint4* xsrc = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + xr_row, M - 1) * H + xr_col);
-  // W staging: float4 number q = tid + 256 i of the TE x 128 tile: row q/32, column (q%32)*4
-  const float4* wsrc[WQ];
-  bool wv[WQ];
+  __shared__ __align__(16) uint16_t xs[2][RM_T][RM_PITCH];
+  __shared__ __align__(16) uint16_t wsp[2][3][RM_E][RM_PITCH];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int t0 = blockIdx.y * RM_T, e0 = blockIdx.x * RM_E;
+  // staging thread = (row tid / RM_TPR, RM_G groups of 8 elements at columns
+  // (tid % RM_TPR) * 8 + 8 RM_TPR g): 16-byte x loads, 32-byte W loads
+  const int srow = tid / RM_TPR, scol = (tid % RM_TPR) * 8;
+  const bool xin = t0 + srow < M, win = e0 + srow < E;
+  const uint16_t* xrow = x + (size_t)min(t0 + srow, M - 1) * H;
+  const float* wrow = w_router + (size_t)min(e0 + srow, E - 1) * H;
+  const int nk = NK > 0 ? NK : (H + RM_KC - 1) / RM_KC;
+  // chunks kc+1 and kc+2 are in registers while chunk kc is computed (each
+  // chunk is one round trip to L2); the two register sets alternate, so no
+  // register copy waits on a load
+  struct Stage { uint4 x[RM_G]; float4 w[RM_G][2]; };
+  Stage sa{}, sb{};
+  auto load = [&](Stage& g, int kc) {
 #pragma unroll
-  for (int i = 0; i < WQ; ++i) {
-    const int q = tid + 256 * i, row = q >> 5;
-    wv[i] = e0 + row < E;
-    wsrc[i] = reinterpret_cast<const float4*>(w_router + (size_t)min(e0 + row, E - 1) * H + (q & 31) * 4);
-  }
-  float tot[2][NE], grp[2][NE];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < NE; ++j) { tot[i][j] = 0.f; grp[i][j] = 0.f; }
-  const int nk = H / RG_KC;
-  const int ktail = H - nk * RG_KC;              // < 128, multiple of 32: a last, partial chunk
-  const int nchunks = nk + (ktail ? 1 : 0);
-  uint4 xr0, xr1;
-  float4 wr[WQ];
-  auto load = [&](int kc) {
-    const int kbase = kc * RG_KC;
-    // columns past H read a clamped in-row address and are zeroed when staged
-    const int off = min(kbase + xr_col, H - 16);
-    xr0 = xsrc[(off - xr_col) / 8];
-    xr1 = xsrc[(off - xr_col) / 8 + 1];
-#pragma unroll
-    for (int i = 0; i < WQ; ++i) {
-      const int q = tid + 256 * i, col = (q & 31) * 4;
-      wr[i] = wsrc[i][(min(kbase + col, H - 4) - col) / 4];
+    for (int q = 0; q < RM_G; ++q) {
+      const int col = min(kc * RM_KC + scol + 8 * RM_TPR * q, H - 8);   // clamped in-row address; zeroed when staged
+      g.x[q] = *reinterpret_cast<const uint4*>(xrow + col);
+      g.w[q][0] = *reinterpret_cast<const float4*>(wrow + col);
+      g.w[q][1] = *reinterpret_cast<const float4*>(wrow + col + 4);
     }
   };
-  auto store = [&](int buf, int kc) {
-    const int kbase = kc * RG_KC;
-    const bool in = xv && kbase + xr_col < H;
-    const uint32_t w8[8] = {xr0.x, xr0.y, xr0.z, xr0.w, xr1.x, xr1.y, xr1.z, xr1.w};
+  auto store = [&](int buf, int kc, const Stage& g) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float4 f = in ? make_float4(bf16_bits_to_f32(w8[2 * h] & 0xFFFFu), bf16_bits_to_f32(w8[2 * h] >> 16),
-                                        bf16_bits_to_f32(w8[2 * h + 1] & 0xFFFFu),
-                                        bf16_bits_to_f32(w8[2 * h + 1] >> 16))
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-      *reinterpret_cast<float4*>(&xs[buf][xr_row][xr_col + 4 * h]) = f;
-    }
+    for (int q = 0; q < RM_G; ++q) {
+      const int c = scol + 8 * RM_TPR * q;
+      const bool ok = kc * RM_KC + c < H;
+      const uint32_t mx = (ok && xin) ? 0xFFFFFFFFu : 0u, mw = (ok && win) ? 0xFFFFFFFFu : 0u;
+      const uint4 xr = g.x[q];
+      *reinterpret_cast<uint4*>(&xs[buf][srow][c]) = make_uint4(xr.x & mx, xr.y & mx, xr.z & mx, xr.w & mx);
+      const float f[8] = {g.w[q][0].x, g.w[q][0].y, g.w[q][0].z, g.w[q][0].w,
+                          g.w[q][1].x, g.w[q][1].y, g.w[q][1].z, g.w[q][1].w};
+      uint32_t p1[4], p2[4], p3[4];
 #pragma unroll
-    for (int i = 0; i < WQ; ++i) {
-      const int q = tid + 256 * i, row = q >> 5, col = (q & 31) * 4;
-      *reinterpret_cast<float4*>(&wsh[buf][row][col]) =
-          (wv[i] && kbase + col < H) ? wr[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  load(0);
-  store(0, 0);
-  __syncthreads();
-  int leaves = 0;
-  for (int kc = 0; kc < nchunks; ++kc) {
-    const int cur = kc & 1;
-    if (kc + 1 < nchunks) load(kc + 1);
-    const int klen = (kc < nk) ? RG_KC : ktail;
-    for (int k0 = 0; k0 < klen; k0 += 16) {       // one 16-product leaf per step
-      float leaf[2][NE];
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h[3][2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < NE; ++j) leaf[i][j] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 16; kk += 4) {
-        const float4 a0 = *reinterpret_cast<const float4*>(&xs[cur][ty][k0 + kk]);
-        const float4 a1 = *reinterpret_cast<const float4*>(&xs[cur][ty + 16][k0 + kk]);
-#pragma unroll
-        for (int j = 0; j < NE; ++j) {
-          const float4 b = *reinterpret_cast<const float4*>(&wsh[cur][tx + 16 * j][k0 + kk]);
-          leaf[0][j] = fmaf(a0.x, b.x, leaf[0][j]); leaf[0][j] = fmaf(a0.y, b.y, leaf[0][j]);
-          leaf[0][j] = fmaf(a0.z, b.z, leaf[0][j]); leaf[0][j] = fmaf(a0.w, b.w, leaf[0][j]);
-          leaf[1][j] = fmaf(a1.x, b.x, leaf[1][j]); leaf[1][j] = fmaf(a1.y, b.y, leaf[1][j]);
-          leaf[1][j] = fmaf(a1.z, b.z, leaf[1][j]); leaf[1][j] = fmaf(a1.w, b.w, leaf[1][j]);
+        for (int r = 0; r < 2; ++r) {
+          const uint32_t u = __float_as_uint(f[2 * i + r]) & mw;
+          const uint32_t a1 = u & 0xFFFF0000u;
+          const float r1 = __uint_as_float(u) - __uint_as_float(a1);          // exact
+          const uint32_t a2 = __float_as_uint(r1) & 0xFFFF0000u;
+          const float r2 = r1 - __uint_as_float(a2);                           // exact, <= 8 bits
+          h[0][r] = a1 >> 16;
+          h[1][r] = a2 >> 16;
+          h[2][r] = __float_as_uint(r2) >> 16;
         }
+        p1[i] = h[0][0] | (h[0][1] << 16);
+        p2[i] = h[1][0] | (h[1][1] << 16);
+        p3[i] = h[2][0] | (h[2][1] << 16);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < NE; ++j) grp[i][j] += leaf[i][j];
-      if (++leaves == 16) {                        // a group is 16 leaves
-        leaves = 0;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < NE; ++j) { tot[i][j] += grp[i][j]; grp[i][j] = 0.f; }
-      }
+      *reinterpret_cast<uint4*>(&wsp[buf][0][srow][c]) = make_uint4(p1[0], p1[1], p1[2], p1[3]);
+      *reinterpret_cast<uint4*>(&wsp[buf][1][srow][c]) = make_uint4(p2[0], p2[1], p2[2], p2[3]);
+      *reinterpret_cast<uint4*>(&wsp[buf][2][srow][c]) = make_uint4(p3[0], p3[1], p3[2], p3[3]);
     }
-    if (kc + 1 < nchunks) store(cur ^ 1, kc + 1);
-    __syncthreads();
+  };
+  const int tw = wave >> 1, ew = wave & 1;
+  const int fr = lane & 15, fk = 8 * (lane >> 4);   // fragment row / column and K offset
+  const rv4f zero = {0.f, 0.f, 0.f, 0.f};
+  rv4f tot = zero, grp[3] = {zero, zero, zero};    // one group per weight part: three independent chains
+  int leaves = 0;
+  auto step = [&](int cur, int st) {
+    const rv8bf a = __builtin_bit_cast(rv8bf, *reinterpret_cast<const uint4*>(&xs[cur][16 * tw + fr][32 * st + fk]));
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const rv8bf b =
+          __builtin_bit_cast(rv8bf, *reinterpret_cast<const uint4*>(&wsp[cur][p][16 * ew + fr][32 * st + fk]));
+      grp[p] += __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, zero, 0, 0, 0);
+    }
+    if (++leaves == 16) {                            // 16 leaves per group, then into the total
+      leaves = 0;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) { tot += grp[p]; grp[p] = zero; }
+    }
+  };
+  auto compute = [&](int kc) {
+    const int cur = kc & 1;
+    if constexpr (NK > 0) {
+#pragma unroll
+      for (int st = 0; st < RM_KC / 32; ++st) step(cur, st);
+    } else {
+      const int steps = min(RM_KC, H - kc * RM_KC) / 32;
+      for (int st = 0; st < steps; ++st) step(cur, st);
+    }
+  };
+  {
+    Stage s0;
+    load(s0, 0);
+    if (nk > 1) load(sa, 1);
+    if (nk > 2) load(sb, 2);
+    store(0, 0, s0);
   }
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int kc = 0; kc < (NK > 0 ? NK : nk); kc += 2) {   // chunk kc from buffer 0, kc + 1 from buffer 1
+    compute(kc);
+    if (kc + 1 < nk) store(1, kc + 1, sa);
+    if (kc + 3 < nk) load(sa, kc + 3);
+    block_barrier_lds();                             // the prefetches stay in flight
+    if (kc + 1 >= nk) break;
+    compute(kc + 1);
+    if (kc + 2 < nk) store(0, kc + 2, sb);
+    if (kc + 4 < nk) load(sb, kc + 4);
+    block_barrier_lds();
+  }
+  const int e = e0 + 16 * ew + fr;
 #pragma unroll
-    for (int j = 0; j < NE; ++j) {
-      const int t = t0 + ty + 16 * i, e = e0 + tx + 16 * j;
-      if (t < M && e < E) {
-        float v = tot[i][j] + grp[i][j];
-        if (bias) v += bias[(size_t)t * bias_stride + e];
-        logits[(size_t)t * E + e] = v;
-      }
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + 16 * tw + 4 * (lane >> 4) + r;
+    if (t < M && e < E) {
+      float v = tot[r] + grp[0][r];
+      v += grp[1][r];
+      v += grp[2][r];
+      if (bias) v += bias[(size_t)t * bias_stride + e];
+      logits[(size_t)t * E + e] = v;
     }
+  }
 }
 
 // One wave per token.
@@ -255,14 +275,9 @@ hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const 
                                 int64_t bias_stride, int M, int H, int E, float* logits,
                                 hipStream_t s) {
   if (M >= kRouterGemmMinTokens) {
-    const int tt = (M + RG_TT - 1) / RG_TT;
-    if (M >= 256) {
-      router_gemm_kernel<32><<<dim3((E + 31) / 32, tt), dim3(256), 0, s>>>(x, w_router, bias, bias_stride, M, H,
-                                                                           E, logits);
-    } else {
-      router_gemm_kernel<16><<<dim3((E + 15) / 16, tt), dim3(256), 0, s>>>(x, w_router, bias, bias_stride, M, H,
-                                                                           E, logits);
-    }
+    auto kern = (H == 10 * RM_KC) ? router_mfma_kernel<10> : router_mfma_kernel<0>;
+    kern<<<dim3((E + RM_E - 1) / RM_E, (M + RM_T - 1) / RM_T), dim3(RM_THREADS), 0, s>>>(
+        x, w_router, bias, bias_stride, M, H, E, logits);
     return hipGetLastError();
   }
   const int waves_per_block = 2;
