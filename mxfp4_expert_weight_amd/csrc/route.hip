@@ -68,7 +68,8 @@ __global__ __launch_bounds__(128) void router_logits_kernel(const uint16_t* __re
 // Batches on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16).  Each fp32
 // router weight is split exactly into three bf16 parts by truncation:
 // w1 = w with its low 16 bits cleared, w2 = (w - w1) the same way, w3 = the
-// rest (at most 8 significant bits, so exact in bf16).  x is bf16, so every
+// rest (at most 8 significant bits, so exact in bf16; for w = 0 and
+// |w| >= 2^-102, where the parts stay normal).  x is bf16, so every
 // product x * w_j is exact in fp32 and the logit is the plain sum of 3H exact
 // products; only the summation order differs from the fp32 definition.  Each
 // 32-product matrix-core dot starts from zero (a leaf); per weight part, 16
