@@ -13,6 +13,7 @@ and routing examples in ``tests/golden/``, brute force on tiny inputs,
 closed forms, exact power-of-two metamorphics).  No function here is
 "parity unpinned".
 """
+from .lmhead_oracle import E4M3_MAX, e4m3_decode, e4m3_round, lmhead_logits, lmhead_quantize  # noqa: F401
 from .moe_oracle import (  # noqa: F401
     E2M1_MAGNITUDE,
     bf16_bits_to_f64,
