@@ -63,6 +63,7 @@ typedef enum {
 #define MOE_MAX_HIDDEN 8192    /* H, multiple of 32                         */
 #define MOE_MAX_INTER 4096     /* I, multiple of 32                         */
 #define MOE_MAX_TOKENS 65536   /* M                                         */
+#define MOE_LMHEAD_MAX_TOKENS 8 /* M of moe_lmhead_fp8_logits; also M*H <= 32768 */
 
 /* Expert bank of one layer: E routed experts, then (if has_shared) the shared
  * expert at index E.  All four pointers are device pointers, 16-byte aligned.
@@ -178,6 +179,37 @@ moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float
  * Limits: rows >= 1, cols >= 32, cols % 32 == 0, rows*cols < 2^40; q 16-byte aligned. */
 moe_status moe_mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
                                 float* out, void* stream);
+
+/* ---------------------------------------------------------------- FP8 LM head
+ * The LM head projects the hidden state onto the vocabulary (2,560 -> 157,184
+ * for the Ling model: digest, section 2).  Its bf16 weights are quantised
+ * online to FP8, which halves the bytes read per decode step (digest,
+ * section 4; Vietnamese rewrite, section 2).  FP8 is OCP E4M3 ("FN": bias 7,
+ * no infinities, 0x7F/0xFF NaN, largest finite 448) -- the pages name FP8 only.
+ * Weights row-major [V][H]; one fp32 scale per row. */
+
+/* Quantise a bf16 head [V][H] to E4M3 codes [V][H] and fp32 row scales [V]:
+ * s[v] = amax(|w[v][:]|) / 448 in fp32 (1 for an all-zero row); codes[v][k] =
+ * the E4M3 value nearest to clamp(w[v][k] / s[v], -448, 448) (fp32 quotient),
+ * ties to the even mantissa, sign kept (so -0 and negative values that round
+ * to zero give 0x80).
+ *   w_bf16 device bf16 bits [V][H], 16-byte aligned; codes device uint8 [V][H],
+ *   8-byte aligned; scales device fp32 [V].  All caller-owned.
+ * Limits: V >= 1, 32 <= H <= MOE_MAX_HIDDEN, H % 32 == 0.  Non-finite weights:
+ * undefined. */
+moe_status moe_lmhead_fp8_quantize(const uint16_t* w_bf16, int32_t V, int32_t H, uint8_t* codes,
+                                   float* scales, void* stream);
+
+/* logits[t][v] = (sum_k x[t][k] * e4m3(codes[v][k])) * scales[v] for M decode
+ * tokens (W8A16: x stays bf16; each product is exact in fp32, the sum is fp32,
+ * then one multiply by the scale).  Reads each code once per call.
+ *   x device bf16 bits [M][H], 16-byte aligned; codes device uint8 [V][H],
+ *   16-byte aligned; scales device fp32 [V]; logits device fp32 [M][V],
+ *   overwritten.
+ * Limits: 1 <= M <= MOE_LMHEAD_MAX_TOKENS, M*H <= 32768, V >= 1,
+ * 32 <= H <= MOE_MAX_HIDDEN, H % 32 == 0.  NaN codes (0x7F, 0xFF): undefined. */
+moe_status moe_lmhead_fp8_logits(const uint16_t* x, const uint8_t* codes, const float* scales, int32_t M,
+                                 int32_t V, int32_t H, float* logits, void* stream);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,8 @@ _SIGNATURES = {
     "moe_layer_timed": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32,
                                        _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
     "moe_mxfp4_dequantize": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+    "moe_lmhead_fp8_quantize": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P]),
+    "moe_lmhead_fp8_logits": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
 }
 
 
@@ -180,3 +182,13 @@ def moe_layer_timed(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weigh
 def moe_mxfp4_dequantize(q, s, rows, cols, out, stream=None):
     _check(lib().moe_mxfp4_dequantize(_ptr(q), _ptr(s), rows, cols, _ptr(out), _stream(stream)),
            "moe_mxfp4_dequantize")
+
+
+def moe_lmhead_fp8_quantize(w_bf16, V, H, codes, scales, stream=None):
+    _check(lib().moe_lmhead_fp8_quantize(_ptr(w_bf16), V, H, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_lmhead_fp8_quantize")
+
+
+def moe_lmhead_fp8_logits(x, codes, scales, M, V, H, logits, stream=None):
+    _check(lib().moe_lmhead_fp8_logits(_ptr(x), _ptr(codes), _ptr(scales), M, V, H, _ptr(logits), _stream(stream)),
+           "moe_lmhead_fp8_logits")

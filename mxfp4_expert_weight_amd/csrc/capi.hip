@@ -329,4 +329,23 @@ moe_status moe_mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows
   return hip_status(launch_dequant(q, s, rows, cols, out, (hipStream_t)stream));
 }
 
+moe_status moe_lmhead_fp8_quantize(const uint16_t* w_bf16, int32_t V, int32_t H, uint8_t* codes, float* scales,
+                                   void* stream) {
+  if (!w_bf16 || !codes || !scales) return MOE_ERR_NULL;
+  if (V < 1 || H < 32 || H % 32 || H > MOE_MAX_HIDDEN || (int64_t)V * H >= (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  if (!aligned16(w_bf16) || ((uintptr_t)codes & 7u) || ((uintptr_t)scales & 3u)) return MOE_ERR_ALIGN;
+  return hip_status(launch_lmhead_quantize(w_bf16, V, H, codes, scales, (hipStream_t)stream));
+}
+
+moe_status moe_lmhead_fp8_logits(const uint16_t* x, const uint8_t* codes, const float* scales, int32_t M,
+                                 int32_t V, int32_t H, float* logits, void* stream) {
+  if (!x || !codes || !scales || !logits) return MOE_ERR_NULL;
+  if (M < 1 || M > MOE_LMHEAD_MAX_TOKENS || V < 1 || H < 32 || H % 32 || H > MOE_MAX_HIDDEN ||
+      (int64_t)M * H > MOE_LMHEAD_MAX_TOKENS * 4096 || (int64_t)V * H >= (int64_t(1) << 40))
+    return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)scales & 3u) || ((uintptr_t)logits & 3u))
+    return MOE_ERR_ALIGN;
+  return hip_status(launch_lmhead_fp8(x, codes, scales, M, V, H, logits, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -194,5 +194,9 @@ hipError_t launch_records(const int* offsets, const int* sorted_pairs, const int
 hipError_t launch_combine_rows(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols, float* out,
                           hipStream_t st);
+// FP8 LM head (lmhead.hip).
+hipError_t launch_lmhead_quantize(const uint16_t* w, int V, int H, uint8_t* codes, float* scales, hipStream_t s);
+hipError_t launch_lmhead_fp8(const uint16_t* x, const uint8_t* codes, const float* scales, int M, int V, int H,
+                             float* logits, hipStream_t s);
 
 }  // namespace moe

@@ -1,0 +1,148 @@
+// FP8 LM head: online quantisation of the bf16 head to OCP E4M3 with one fp32
+// scale per vocabulary row, and the decode projection logits = x . W^T read
+// from the FP8 codes (half the bytes of the bf16 head: "3 Ways to Improve MoE
+// Inference on NVIDIA DGX Spark" digest, section 4; the head projects the
+// 2,560-wide hidden state onto 157,184 tokens, section 2).
+//
+// Arithmetic: E4M3 decodes exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8 with
+// scale 1), x is bf16, so every product is exact in fp32 (v_dot2_f32_bf16
+// accumulates in fp32); the row sum is then multiplied by the row's scale.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr float kE4M3Max = 448.f;
+
+// ------------------------------------------------------------ quantise --
+// One wave per row: amax over the row, s = amax / 448 (fp32; 1 for a zero
+// row), code = E4M3 nearest to clamp(w / s, -448, 448), ties to even
+// (v_cvt_pk_fp8_f32 rounds to nearest even; the clamp makes saturation
+// explicit).  Lane l handles 8 consecutive elements per 512-element step.
+__global__ __launch_bounds__(256) void lmhead_quantize_kernel(const uint16_t* __restrict__ w, int V, int H,
+                                                              uint8_t* __restrict__ codes,
+                                                              float* __restrict__ scales) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int v = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (v >= V) return;                               // uniform over the wave
+  const uint16_t* row = w + (size_t)v * H;
+  uint32_t amax_bits = 0u;                          // |w| as fp32 bits: ordered like the values
+  for (int c = lane * 8; c < H; c += kWave * 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + c);
+    const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax_bits = max(amax_bits, (p[i] << 16) & 0x7FFFFFFFu);
+      amax_bits = max(amax_bits, p[i] & 0x7FFF0000u);
+    }
+  }
+  amax_bits = wave_max_u32(amax_bits);
+  const float amax = __uint_as_float(amax_bits);
+  const float s = amax > 0.f ? amax / kE4M3Max : 1.f;
+  if (lane == 0) scales[v] = s;
+  for (int c = lane * 8; c < H; c += kWave * 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + c);
+    const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[2 * i] = fminf(fmaxf(__uint_as_float(p[i] << 16) / s, -kE4M3Max), kE4M3Max);
+      q[2 * i + 1] = fminf(fmaxf(__uint_as_float(p[i] & 0xFFFF0000u) / s, -kE4M3Max), kE4M3Max);
+    }
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], hi, true);
+    *reinterpret_cast<uint2*>(codes + (size_t)v * H + c) = make_uint2((uint32_t)lo, (uint32_t)hi);
+  }
+}
+
+// ---------------------------------------------------------- projection --
+// Workgroup = 4 waves x LH_RB rows each; the tokens' x rows are staged in LDS
+// once per workgroup.  A wave issues the 16-byte code loads of all LH_RB rows
+// (lane l takes 16-byte chunks l, l + 64, ... of each row) before any product,
+// so each wave keeps LH_RB * H bytes in flight; then per token the exact
+// products are summed per lane, across the wave (DPP) and scaled.
+constexpr int LH_RB = 4;
+constexpr int LH_WAVES = 4;
+constexpr int LH_MAX_CHUNKS = (MOE_MAX_HIDDEN / 16 + kWave - 1) / kWave;   // per lane and row (8)
+
+template <int CH>   // chunks per lane and row: ceil(H / 16 / 64)
+__global__ __launch_bounds__(LH_WAVES * kWave) void lmhead_fp8_kernel(const uint16_t* __restrict__ x,
+                                                                      const uint8_t* __restrict__ codes,
+                                                                      const float* __restrict__ scales, int M,
+                                                                      int V, int H, float* __restrict__ logits) {
+  extern __shared__ uint4 xs[];                     // [M][H] bf16
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nx = M * H / 8;
+  for (int i = threadIdx.x; i < nx; i += blockDim.x) xs[i] = reinterpret_cast<const uint4*>(x)[i];
+  __syncthreads();
+  const int v0 = (blockIdx.x * LH_WAVES + wave) * LH_RB;
+  if (v0 >= V) return;                              // uniform over the wave (no barrier follows)
+  const int nch = H / 16;
+  uint4 cw[LH_RB][CH];
+#pragma unroll
+  for (int r = 0; r < LH_RB; ++r) {
+    const uint4* row = reinterpret_cast<const uint4*>(codes + (size_t)min(v0 + r, V - 1) * H);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) cw[r][i] = row[min(lane + kWave * i, nch - 1)];   // clamped; masked below
+  }
+  for (int t = 0; t < M; ++t) {
+    const uint4* xr = xs + (size_t)t * (H / 8);
+    float acc[LH_RB];
+#pragma unroll
+    for (int r = 0; r < LH_RB; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int ch = lane + kWave * i;
+      if (ch < nch) {
+        const uint4 x0 = xr[2 * ch], x1 = xr[2 * ch + 1];   // 16 bf16 of the chunk
+        const uint32_t xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int r = 0; r < LH_RB; ++r) {
+          const uint32_t c4[4] = {cw[r][i].x, cw[r][i].y, cw[r][i].z, cw[r][i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[q], 1.f, false);
+            const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[q], 1.f, true);
+            acc[r] = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2, xa[2 * q]), acc[r], false);
+            acc[r] = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, xa[2 * q + 1]), acc[r], false);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < LH_RB; ++r) {
+      const float sum = group_sum<kWave>(acc[r]);
+      if (lane == 0 && v0 + r < V) logits[(size_t)t * V + v0 + r] = sum * scales[v0 + r];
+    }
+  }
+}
+
+hipError_t launch_lmhead_quantize(const uint16_t* w, int V, int H, uint8_t* codes, float* scales,
+                                  hipStream_t s) {
+  lmhead_quantize_kernel<<<(V + 3) / 4, 256, 0, s>>>(w, V, H, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead_fp8(const uint16_t* x, const uint8_t* codes, const float* scales, int M, int V, int H,
+                             float* logits, hipStream_t s) {
+  const int ch = (H / 16 + kWave - 1) / kWave;
+  const unsigned grid = (V + LH_WAVES * LH_RB - 1) / (LH_WAVES * LH_RB);
+  const size_t shmem = (size_t)M * H * sizeof(uint16_t);
+  void (*k)(const uint16_t*, const uint8_t*, const float*, int, int, int, float*);
+  switch (ch) {
+    case 1: k = lmhead_fp8_kernel<1>; break;
+    case 2: k = lmhead_fp8_kernel<2>; break;
+    case 3: k = lmhead_fp8_kernel<3>; break;
+    case 4: k = lmhead_fp8_kernel<4>; break;
+    case 5: case 6: k = lmhead_fp8_kernel<6>; break;
+    default: k = lmhead_fp8_kernel<LH_MAX_CHUNKS>; break;
+  }
+  k<<<grid, LH_WAVES * kWave, shmem, s>>>(x, codes, scales, M, V, H, logits);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -189,17 +189,22 @@ __global__ __launch_bounds__(RM_THREADS) void router_mfma_kernel(const uint16_t*
     store(0, 0, s0);
   }
   __syncthreads();
-#pragma unroll
-  for (int kc = 0; kc < (NK > 0 ? NK : nk); kc += 2) {   // chunk kc from buffer 0, kc + 1 from buffer 1
+  auto two_chunks = [&](int kc) {                 // chunk kc from buffer 0, kc + 1 from buffer 1
     compute(kc);
     if (kc + 1 < nk) store(1, kc + 1, sa);
     if (kc + 3 < nk) load(sa, kc + 3);
     block_barrier_lds();                             // the prefetches stay in flight
-    if (kc + 1 >= nk) break;
+    if (kc + 1 >= nk) return;
     compute(kc + 1);
     if (kc + 2 < nk) store(0, kc + 2, sb);
     if (kc + 4 < nk) load(sb, kc + 4);
     block_barrier_lds();
+  };
+  if constexpr (NK > 0) {
+#pragma unroll
+    for (int kc = 0; kc < NK; kc += 2) two_chunks(kc);
+  } else {
+    for (int kc = 0; kc < nk; kc += 2) two_chunks(kc);
   }
   const int e = e0 + 16 * ew + fr;
 #pragma unroll

@@ -179,3 +179,29 @@ def custom(name: str, M: int, H: int, I: int, E: int, k: int, shared: bool = Tru
     if H % 32 or I % 32:
         raise ValueError("H and I must be multiples of the 32-element scale block")
     return Workload(name, M, H, I, E, k, shared, routing, sets, seed)
+
+
+# --------------------------------------------------------------- LM head --
+# The Ling LM head: 2,560 -> 157,184 (digest, section 2).
+LMHEAD_VOCAB, LMHEAD_HIDDEN = 157184, 2560
+
+
+@dataclass
+class LmHeadSet:
+    x_bits: np.ndarray       # bf16 [M][H]
+    w_bits: np.ndarray       # bf16 [V][H] head weights (input of the quantiser)
+    codes: np.ndarray        # uint8 [V][H] E4M3 codes, uniform over the 254 finite codes
+    scales: np.ndarray       # fp32 [V], log-uniform in [2^-13, 2^-12) (near the quantiser's s = amax/448 of N(0, 0.02) rows)
+
+
+def lmhead_set(M: int, V: int, H: int, seed: int) -> LmHeadSet:
+    """x ~ N(0, 1) and head weights ~ N(0, 0.02), rounded to bf16; random
+    finite E4M3 codes and row scales for the projection alone (independent of
+    the weights, so the projection can be checked at any size)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    x = f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    w = f32_to_bf16_bits((rng.standard_normal((V, H)) * 0.02).astype(np.float32))
+    codes = random_bytes(rng, (V, H))
+    codes = np.where((codes & 0x7F) == 0x7F, codes ^ 0x01, codes).astype(np.uint8)   # no NaN codes
+    scales = (2.0 ** rng.uniform(-13, -12, V)).astype(np.float32)
+    return LmHeadSet(x, w, codes, scales)

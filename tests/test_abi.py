@@ -125,3 +125,17 @@ def test_library_has_no_oracle_or_fallback():
             if fn.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(root, fn)).read()
                 assert "import oracle" not in src and "from oracle" not in src, fn
+
+
+def test_lmhead_host_checks(lib):
+    q, p = B.moe_lmhead_fp8_quantize, B.moe_lmhead_fp8_logits
+    assert _status(q, None, 10, 2560, A, A, 0) == B.MOE_ERR_NULL
+    assert _status(q, A, 0, 2560, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(q, A, 10, 2550, A, A, 0) == B.MOE_ERR_SHAPE          # H % 32
+    assert _status(q, A, 10, 16384, A, A, 0) == B.MOE_ERR_SHAPE         # H > limit
+    assert _status(q, MIS, 10, 2560, A, A, 0) == B.MOE_ERR_ALIGN
+    assert _status(p, A, A, None, 1, 10, 2560, A, 0) == B.MOE_ERR_NULL
+    assert _status(p, A, A, A, 9, 10, 2560, A, 0) == B.MOE_ERR_SHAPE     # M > 8
+    assert _status(p, A, A, A, 5, 10, 8192, A, 0) == B.MOE_ERR_SHAPE     # M * H > 32768
+    assert _status(p, A, A, A, 1, 0, 2560, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(p, A, MIS, A, 1, 10, 2560, A, 0) == B.MOE_ERR_ALIGN
