@@ -118,10 +118,10 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic(workload):
-    """HBM bytes per gate/up launch from the committed counter summary, or None
-    when there is none or it was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"gateup_kernel_{workload}.txt")
+def recorded_traffic(workload, kernel="gateup_kernel"):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -208,12 +208,75 @@ def cpu_baseline(wl, seconds_budget=20.0):
             "us_per_layer": sec * 1e6}
 
 
+def bench_lmhead(torch, binding, synth, args):
+    """The FP8 LM head (157,184 x 2,560, E4M3 codes + fp32 row scales) for M
+    tokens: K projections replayed from a HIP graph over enough distinct code
+    sets that the 256 MB Infinity Cache cannot hold them; value = bytes the
+    projection must read (codes, scales, x) and write (logits) per second."""
+    M = 4 if args.workload == "lmhead_fp8_m4" else 1
+    V, H = synth.LMHEAD_VOCAB, synth.LMHEAD_HIDDEN
+    nsets = args.sets or 4
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4321)
+    sets = []
+    for _ in range(nsets):
+        codes = torch.randint(0, 256, (V, H), dtype=torch.uint8, device="cuda", generator=g)
+        codes = torch.where((codes & 0x7F) == 0x7F, codes ^ 1, codes)       # no NaN codes
+        scales = torch.exp2(torch.rand(V, device="cuda", generator=g) - 13.0)
+        sets.append((codes, scales))
+    x = torch.from_numpy(synth.lmhead_set(M, 1, H, seed=5).x_bits.view("int16")).cuda()
+    out = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    for c, sc in sets:
+        binding.moe_lmhead_fp8_logits(x, c, sc, M, V, H, out)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        for c, sc in sets:
+            binding.moe_lmhead_fp8_logits(x, c, sc, M, V, H, out)
+    torch.cuda.current_stream().wait_stream(st)
+    with torch.cuda.graph(gr):
+        for c, sc in sets:
+            binding.moe_lmhead_fp8_logits(x, c, sc, M, V, H, out)
+    steps = max(nsets, args.steps // nsets * nsets)
+    for _ in range(max(1, args.warmup // nsets)):
+        gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps // nsets):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = V * H + V * 4 + M * H * 2 + M * V * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] lmhead M={M}: {steps} projections, {ms * 1e3:.2f} us each, {nbytes / 1e6:.1f} MB, "
+        f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+    out_json = {
+        "metric": "FP8 LM-head projection GB/s (157184x2560 E4M3, fp32 row scales)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "vocab": V, "hidden": H, "weights": "E4M3 + fp32/row",
+                   "activations": "bf16", "code_sets_rotated": nsets},
+        "us_per_projection": ms * 1e3,
+        "roofline": {"bound": "hbm", "kernel": "lmhead_fp8_kernel", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic(args.workload, "lmhead_fp8_kernel")},
+    }
+    print(json.dumps(out_json), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="ling_m1")
+    ap.add_argument("--workload", default="ling_m1",
+                    help="a MoE workload (ling_m1, ling_m4_mtp, ling_m32_zipf, ling_m512_prefill, tiny) "
+                         "or the FP8 LM head (lmhead_fp8, lmhead_fp8_m4)")
     ap.add_argument("--sets", type=int, default=None, help="layer sets rotated (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--three-calls", action="store_true",
@@ -251,6 +314,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log("copy probe: 3 x 1 GiB device-to-device copies")
+        return
+
+    if args.workload.startswith("lmhead"):
+        bench_lmhead(torch, binding, synth, args)
         return
 
     wl = synth.WORKLOADS[args.workload]

@@ -63,13 +63,16 @@ __global__ __launch_bounds__(256) void lmhead_quantize_kernel(const uint16_t* __
 // Workgroup = 4 waves x LH_RB rows each; the tokens' x rows are staged in LDS
 // once per workgroup.  A wave issues the 16-byte code loads of all LH_RB rows
 // (lane l takes 16-byte chunks l, l + 64, ... of each row) before any product,
-// so each wave keeps LH_RB * H bytes in flight; then per token the exact
-// products are summed per lane, across the wave (DPP) and scaled.
+// so each wave keeps LH_RB * H bytes in flight; each chunk's codes are decoded
+// once and used by every token (up to MM tokens in registers); then the
+// per-lane sums are summed across the wave (DPP) and scaled.  (Waves that walk
+// several row groups with the next group's loads rolling in behind the decode
+// measured slower: fewer resident waves, and a tail of long-lived waves.)
 constexpr int LH_RB = 4;
 constexpr int LH_WAVES = 4;
 constexpr int LH_MAX_CHUNKS = (MOE_MAX_HIDDEN / 16 + kWave - 1) / kWave;   // per lane and row (8)
 
-template <int CH>   // chunks per lane and row: ceil(H / 16 / 64)
+template <int CH, int MM>   // CH: chunks per lane and row, ceil(H / 16 / 64); MM: tokens, at least M
 __global__ __launch_bounds__(LH_WAVES * kWave) void lmhead_fp8_kernel(const uint16_t* __restrict__ x,
                                                                       const uint8_t* __restrict__ codes,
                                                                       const float* __restrict__ scales, int M,
@@ -89,34 +92,49 @@ __global__ __launch_bounds__(LH_WAVES * kWave) void lmhead_fp8_kernel(const uint
 #pragma unroll
     for (int i = 0; i < CH; ++i) cw[r][i] = row[min(lane + kWave * i, nch - 1)];   // clamped; masked below
   }
-  for (int t = 0; t < M; ++t) {
-    const uint4* xr = xs + (size_t)t * (H / 8);
-    float acc[LH_RB];
+  float acc[LH_RB][MM];
 #pragma unroll
-    for (int r = 0; r < LH_RB; ++r) acc[r] = 0.f;
+  for (int r = 0; r < LH_RB; ++r)
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int ch = lane + kWave * i;
-      if (ch < nch) {
-        const uint4 x0 = xr[2 * ch], x1 = xr[2 * ch + 1];   // 16 bf16 of the chunk
-        const uint32_t xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int t = 0; t < MM; ++t) acc[r][t] = 0.f;
 #pragma unroll
-        for (int r = 0; r < LH_RB; ++r) {
-          const uint32_t c4[4] = {cw[r][i].x, cw[r][i].y, cw[r][i].z, cw[r][i].w};
+  for (int i = 0; i < CH; ++i) {
+    const int ch = lane + kWave * i;
+    if (ch < nch) {
+      bf16x2 wb[LH_RB][8];                          // the chunk's 16 weights of each row, as bf16 pairs
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[q], 1.f, false);
-            const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[q], 1.f, true);
-            acc[r] = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2, xa[2 * q]), acc[r], false);
-            acc[r] = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, xa[2 * q + 1]), acc[r], false);
-          }
+      for (int r = 0; r < LH_RB; ++r) {
+        const uint32_t c4[4] = {cw[r][i].x, cw[r][i].y, cw[r][i].z, cw[r][i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          wb[r][2 * q] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[q], 1.f, false);
+          wb[r][2 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[q], 1.f, true);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < MM; ++t) {
+        if (t < M) {
+          const uint4* xr = xs + (size_t)t * (H / 8) + 2 * ch;
+          const uint4 x0 = xr[0], x1 = xr[1];       // 16 bf16 of the chunk
+          const uint32_t xa[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int r = 0; r < LH_RB; ++r)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              acc[r][t] = __builtin_amdgcn_fdot2_f32_bf16(wb[r][q], __builtin_bit_cast(bf16x2, xa[q]), acc[r][t],
+                                                          false);
         }
       }
     }
+  }
 #pragma unroll
-    for (int r = 0; r < LH_RB; ++r) {
-      const float sum = group_sum<kWave>(acc[r]);
-      if (lane == 0 && v0 + r < V) logits[(size_t)t * V + v0 + r] = sum * scales[v0 + r];
+  for (int t = 0; t < MM; ++t) {
+    if (t < M) {
+#pragma unroll
+      for (int r = 0; r < LH_RB; ++r) {
+        const float sum = group_sum<kWave>(acc[r][t]);
+        if (lane == 0 && v0 + r < V) logits[(size_t)t * V + v0 + r] = sum * scales[v0 + r];
+      }
     }
   }
 }
@@ -133,13 +151,30 @@ hipError_t launch_lmhead_fp8(const uint16_t* x, const uint8_t* codes, const floa
   const unsigned grid = (V + LH_WAVES * LH_RB - 1) / (LH_WAVES * LH_RB);
   const size_t shmem = (size_t)M * H * sizeof(uint16_t);
   void (*k)(const uint16_t*, const uint8_t*, const float*, int, int, int, float*);
-  switch (ch) {
-    case 1: k = lmhead_fp8_kernel<1>; break;
-    case 2: k = lmhead_fp8_kernel<2>; break;
-    case 3: k = lmhead_fp8_kernel<3>; break;
-    case 4: k = lmhead_fp8_kernel<4>; break;
-    case 5: case 6: k = lmhead_fp8_kernel<6>; break;
-    default: k = lmhead_fp8_kernel<LH_MAX_CHUNKS>; break;
+  if (M == 1) {
+    switch (ch) {
+      case 1: k = lmhead_fp8_kernel<1, 1>; break;
+      case 2: k = lmhead_fp8_kernel<2, 1>; break;
+      case 3: k = lmhead_fp8_kernel<3, 1>; break;
+      case 4: k = lmhead_fp8_kernel<4, 1>; break;
+      default: k = lmhead_fp8_kernel<LH_MAX_CHUNKS, 1>; break;
+    }
+  } else if (M <= 4) {
+    switch (ch) {
+      case 1: k = lmhead_fp8_kernel<1, 4>; break;
+      case 2: k = lmhead_fp8_kernel<2, 4>; break;
+      case 3: k = lmhead_fp8_kernel<3, 4>; break;
+      case 4: k = lmhead_fp8_kernel<4, 4>; break;
+      default: k = lmhead_fp8_kernel<LH_MAX_CHUNKS, 4>; break;
+    }
+  } else {
+    switch (ch) {
+      case 1: k = lmhead_fp8_kernel<1, 8>; break;
+      case 2: k = lmhead_fp8_kernel<2, 8>; break;
+      case 3: k = lmhead_fp8_kernel<3, 8>; break;
+      case 4: k = lmhead_fp8_kernel<4, 8>; break;
+      default: k = lmhead_fp8_kernel<LH_MAX_CHUNKS, 8>; break;   // M >= 5 and M * H <= 32768: H <= 6528
+    }
   }
   k<<<grid, LH_WAVES * kWave, shmem, s>>>(x, codes, scales, M, V, H, logits);
   return hipGetLastError();

@@ -83,7 +83,7 @@ def test_projection_decodes_every_code_exactly():
 
 
 @pytest.mark.parametrize("M,V,H", [(1, 1000, 2560), (4, 777, 2560), (8, 513, 2560), (4, 100, 8192),
-                                   (2, 33, 96), (1, 5, 32), (3, 64, 1056)])
+                                   (2, 33, 96), (1, 5, 32), (3, 64, 1056), (5, 70, 6528), (6, 40, 5440)])
 def test_projection_within_rounding_bound(M, V, H):
     torch = need_gpu()
     say(f"lmhead logits M={M} V={V} H={H}")
