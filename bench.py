@@ -104,17 +104,37 @@ def device_sets(torch, wl, nsets):
     return out
 
 
-def kernel_source_hash():
-    """sha256 over the HIP sources and the header: a traffic figure measured on
-    other sources is stale."""
+# the translation unit that defines each profiled kernel
+KERNEL_SOURCE = {"gateup_kernel": "forward.hip", "lmhead_fp8_kernel": "lmhead.hip"}
+
+
+def kernel_source_hash(kernel=None):
+    """sha256 over the kernel's translation unit and every local header it
+    includes (all HIP sources and the header when no kernel is named): a
+    traffic figure measured on other sources is stale."""
     import hashlib
-    h = hashlib.sha256()
+    import re
     csrc = os.path.join(ROOT, "mxfp4_expert_weight_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    h.update(open(os.path.join(ROOT, "include", "moe_mxfp4.h"), "rb").read())
+    inc = os.path.join(ROOT, "include")
+    if kernel is None:
+        files = [os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h"))]
+        files.append(os.path.join(inc, "moe_mxfp4.h"))
+    else:
+        files, todo = [], [os.path.join(csrc, KERNEL_SOURCE[kernel])]
+        while todo:
+            f = todo.pop()
+            if f in files:
+                continue
+            files.append(f)
+            for name in re.findall(r'^#include "([^"]+)"', open(f).read(), re.M):
+                for d in (csrc, inc):
+                    if os.path.exists(os.path.join(d, name)):
+                        todo.append(os.path.join(d, name))
+                        break
+    h = hashlib.sha256()
+    for f in sorted(files, key=os.path.basename):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
     return h.hexdigest()
 
 
@@ -129,7 +149,7 @@ def recorded_traffic(workload, kernel="gateup_kernel"):
         if ":" in line and not line.startswith((" ", "#", "|")):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_sources_sha256") != kernel_source_hash():
+    if fields.get("kernel_sources_sha256") != kernel_source_hash(kernel):
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
@@ -166,17 +186,22 @@ def profile_summary(dirs, kernel):
     print("\n".join(lines))
 
 
+def blas_threads():
+    """Threads of the BLAS the oracle's matrix products run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
 def cpu_baseline(wl, seconds_budget=20.0):
     """The oracle as it stands, on host-generated sets of the same workload."""
     import numpy as np
 
     import oracle
     from mxfp4_expert_weight_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+    threads = blas_threads()
     times, nbytes, tokens = [], [], 0
     start = time.time()
     l = 0
@@ -266,7 +291,30 @@ def bench_lmhead(torch, binding, synth, args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                      "traffic": recorded_traffic(args.workload, "lmhead_fp8_kernel")},
     }
+    if not args.no_cpu_baseline:
+        out_json["cpu_baseline"] = lmhead_cpu_baseline(synth, M, V, H)
     print(json.dumps(out_json), flush=True)
+
+
+def lmhead_cpu_baseline(synth, M, V, H, seconds_budget=10.0):
+    """The oracle's float64 projection of M tokens onto samples of 8,192 head
+    rows, repeated within the budget; GB/s of the sampled rows' bytes."""
+    import statistics
+
+    import oracle
+    rows = 8192
+    s = synth.lmhead_set(M, rows, H, seed=11)
+    nbytes = rows * H + rows * 4 + M * H * 2 + M * rows * 4
+    times = []
+    t_end = time.perf_counter() + seconds_budget
+    while time.perf_counter() < t_end or not times:
+        t0 = time.perf_counter()
+        oracle.lmhead_logits(s.x_bits, s.codes, s.scales)
+        times.append(time.perf_counter() - t0)
+    sec = statistics.median(times)
+    return {"value": nbytes / sec / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{len(times)} projections of {M} token(s) onto {rows} of the {V} rows (H = {H}); "
+                      f"{sec * 1e3:.1f} ms each, {sec * V / rows * 1e3:.0f} ms scaled to the whole head"}
 
 
 def main():
@@ -286,13 +334,14 @@ def main():
     ap.add_argument("--profile-summary", nargs="+", metavar="DIR",
                     help="print a text summary of rocprofv3 csv output directories and exit")
     ap.add_argument("--kernel", default="gateup_kernel", help="kernel kept in --profile-summary counters")
-    ap.add_argument("--source-hash", action="store_true", help="print the kernel sources' sha256 and exit")
+    ap.add_argument("--source-hash", nargs="?", const="", default=None, metavar="KERNEL",
+                    help="print the sha256 of KERNEL's sources (of all kernel sources without KERNEL) and exit")
     args = ap.parse_args()
     if args.profile_summary:
         profile_summary(args.profile_summary, args.kernel)
         return
-    if args.source_hash:
-        print(kernel_source_hash())
+    if args.source_hash is not None:
+        print(kernel_source_hash(args.source_hash or None))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
