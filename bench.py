@@ -195,7 +195,7 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline(wl, seconds_budget=20.0):
+def cpu_baseline(wl, seconds_budget=20.0, w4a8=False):
     """The oracle as it stands, on host-generated sets of the same workload."""
     import numpy as np
 
@@ -209,14 +209,15 @@ def cpu_baseline(wl, seconds_budget=20.0):
         ls = synth.layer_set(wl, l)
         t0 = time.perf_counter()
         if wl.M <= 8:
-            r = oracle.moe_layer(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s,
-                                 wl.k, wl.shared)
+            layer = oracle.moe_layer_w4a8 if w4a8 else oracle.moe_layer
+            r = layer(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s, wl.k, wl.shared)
             D = r["num_active"]
             frac = 1.0
         else:   # large batches: a bounded token sample, scaled to the layer
             sample = list(range(0, wl.M, max(1, wl.M // 4)))[:4]
-            oracle.moe_layer_tokens(sample, ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s,
-                                    ls.w2_q, ls.w2_s, wl.k, wl.shared)
+            tokens_fn = oracle.moe_layer_w4a8_tokens if w4a8 else oracle.moe_layer_tokens
+            tokens_fn(sample, ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s, wl.k,
+                      wl.shared)
             D = int(np.unique(oracle.topk_softmax(oracle.router_logits(
                 oracle.bf16_bits_to_f64(ls.x_bits), ls.w_router, ls.bias), wl.k)[0]).size)
             frac = len(sample) / wl.M
@@ -327,6 +328,8 @@ def main():
                          "or the FP8 LM head (lmhead_fp8, lmhead_fp8_m4)")
     ap.add_argument("--sets", type=int, default=None, help="layer sets rotated (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--w4a8", action="store_true",
+                    help="the W4A8 variant (moe_layer_w4a8: MXFP8 activations into the experts)")
     ap.add_argument("--three-calls", action="store_true",
                     help="time moe_route + moe_sort_by_expert + moe_mxfp4_forward instead of moe_layer")
     ap.add_argument("--copy-probe", action="store_true",
@@ -381,7 +384,7 @@ def main():
     # one eager pass: loads the kernels and records each set's distinct-expert count
     D, G = [], []
     for d, w in zip(sets, weights):
-        run_layer(d, buf, w)
+        run_layer(d, buf, w, w4a8=args.w4a8)
         D.append(int(buf.num_active.item()))
         G.append(buf.header()["gemv_experts"])   # experts on the GEMV path (the timed kernel)
     log(f"[bench] distinct routed experts per set: min {min(D)} max {max(D)} mean {sum(D) / len(D):.2f}")
@@ -392,11 +395,11 @@ def main():
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for i in range(n):
-                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls)
+                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls, w4a8=args.w4a8)
         torch.cuda.current_stream().wait_stream(s)
         with torch.cuda.graph(g):
             for i in range(n):
-                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls)
+                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls, w4a8=args.w4a8)
         return g
 
     g_full = capture(nsets)
@@ -441,9 +444,10 @@ def main():
     torch.cuda.synchronize()
     for i in range(n_ev):
         d, w = sets[step_sets[i]], weights[step_sets[i]]
-        binding.moe_layer_timed(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits,
-                                buf.ids, buf.weights, buf.offsets, buf.pairs, buf.active, buf.num_active,
-                                buf.y, buf.ws, buf.ws_bytes, starts[i], stops[i], stream)
+        timed = binding.moe_layer_w4a8_timed if args.w4a8 else binding.moe_layer_timed
+        timed(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits, buf.ids, buf.weights,
+              buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y, buf.ws, buf.ws_bytes, starts[i], stops[i],
+              stream)
     torch.cuda.synchronize()
     spans = [hev.elapsed_ms(starts[i], stops[i]) for i in range(n_ev)]
     for e in starts + stops:
@@ -467,23 +471,26 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "entry": "three calls" if args.three_calls else "moe_layer", "M": wl.M, "hidden": wl.H, "inter": wl.I, "experts": wl.E,
+        "config": {"workload": wl.name,
+                   "entry": "moe_layer_w4a8" if args.w4a8 else ("three calls" if args.three_calls else "moe_layer"),
+                   "M": wl.M, "hidden": wl.H, "inter": wl.I, "experts": wl.E,
                    "top_k": wl.k, "shared_expert": wl.shared, "routing": wl.routing,
                    "layer_sets_rotated": nsets, "weights": "MXFP4 (E2M1 + E8M0/32)",
-                   "activations": "bf16"},
+                   "activations": "MXFP8 (E4M3 + E8M0/32) into the experts" if args.w4a8 else "bf16"},
         "us_per_layer": ms_per_step * 1e3,
         "layer_bytes": sum(lay_b) / len(lay_b),
         "layer_frac_of_hbm_peak": layer_gbs / HBM_PEAK_GBS,
         "mean_distinct_experts": sum(D[l] for l in step_sets) / len(step_sets),
         "roofline": {"bound": "hbm", "kernel": "gateup_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(wl.name),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic(wl.name + ("_w4a8" if args.w4a8 else "")),
                      "us_per_launch": gu_ms * 1e3, "bytes_per_launch": gu_bytes},
     }
     if not args.no_cpu_baseline:
         del sets
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, w4a8=args.w4a8)
     print(json.dumps(out), flush=True)
 
 

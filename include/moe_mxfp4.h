@@ -173,6 +173,45 @@ moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float
                            void* workspace, size_t workspace_bytes, void* start_event, void* stop_event,
                            void* stream);
 
+/* ------------------------------------------------------------------- W4A8
+ * The baseline deployment of the Ling model runs the MXFP4 experts with 8-bit
+ * activations, W4A8 (digest, section 2).  Here the 8-bit format is MXFP8 in
+ * the OCP microscaling sense (the pages name W4A8 only): blocks of 32
+ * consecutive elements along the reduction axis share one E8M0 scale
+ * X = 2^(floor(log2 amax) - 8), exponent clamped to [-127, 127] (2^-127 for an
+ * all-zero block); each element is the E4M3 code nearest to v / X, ties to
+ * even, the quotient clamped to +-448. */
+
+/* Quantise bf16 rows [rows][K] to MXFP8 along K.
+ *   x       device bf16 [rows][K], 16-byte aligned
+ *   codes   device uint8 [rows][K] E4M3 codes, 16-byte aligned, or NULL
+ *   scales  device uint8 [rows][K/32] E8M0 bytes (exponent + 127), or NULL
+ *   values  device bf16 [rows][K]: each code's value (code * X), 16-byte aligned,
+ *           or NULL; exact for blocks whose largest magnitude is >= 2^-110
+ * At least one output. Limits: rows >= 1, K >= 32, K % 32 == 0, rows*K < 2^40. */
+moe_status moe_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                              uint16_t* values, void* stream);
+
+/* moe_layer in the W4A8 variant.  Same arguments, outputs and limits; the
+ * routing (logits, ids, weights, sort outputs) is moe_layer's, on the bf16 x.
+ * The experts (routed and shared) take x as MXFP8 (each element replaced by
+ * its code's value), and the down projection takes h as MXFP8 along I after h
+ * is rounded to bf16.  Experts with >= 16 tokens run on the scaled MXFP4
+ * matrix cores with one MXFP8 activation term. */
+moe_status moe_layer_w4a8(const uint16_t* x, const float* w_router, const float* logit_bias,
+                          int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                          float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                          int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_layer_w4a8 with the gate/up kernel's timestamps (as moe_layer_timed). */
+moe_status moe_layer_w4a8_timed(const uint16_t* x, const float* w_router, const float* logit_bias,
+                                int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                                float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                                int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                                void* workspace, size_t workspace_bytes, void* start_event, void* stop_event,
+                                void* stream);
+
 /* Dequantise an MXFP4 tensor [rows][cols] (layout above) to fp32 with the same
  * device routine the expert kernels use (exposes it for exact checks).
  *   q device uint8 [rows][cols/2], s device uint8 [rows][cols/32], out device fp32 [rows][cols]

@@ -33,10 +33,12 @@ moe_status check_inter(int32_t I) {
 }
 
 // Arguments of the expert stage; the slot records live in the workspace.  The
-// MFMA fields are set when the path is on for these sizes.
+// MFMA fields are set when the path is on for these sizes.  act8 (W4A8): the
+// experts read the MXFP8 x from the workspace.
 ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
                        const float* topk_weights, const int32_t* expert_offsets, const int32_t* sorted_pairs,
-                       const int32_t* active_experts, const int32_t* num_active, float* y, void* workspace) {
+                       const int32_t* active_experts, const int32_t* num_active, float* y, void* workspace,
+                       bool act8 = false) {
   const WorkspaceLayout L = workspace_layout(M, top_k, w->num_experts, w->hidden, w->inter);
   char* ws = reinterpret_cast<char*>(workspace);
   ForwardArgs a{};
@@ -72,6 +74,10 @@ ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
     a.inv = reinterpret_cast<const int*>(ws + L.inv);
   }
   if (M > kRoutedMaxTokens) a.lists = reinterpret_cast<const int*>(ws + L.lists);
+  if (act8) {
+    a.act8 = 1;
+    a.x = reinterpret_cast<const uint16_t*>(ws + L.xdq);
+  }
   return a;
 }
 
@@ -126,10 +132,11 @@ hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start,
   SideStreams* q = (mt || mfma) ? side_streams(s) : nullptr;
   if (!q) {
     lock.unlock();
-    if (mfma && (e = launch_forward_mfma_front(a, s)) != hipSuccess) return e;
+    if (mfma && !a.act8 && (e = launch_forward_mfma_front(a, s)) != hipSuccess) return e;
     if ((e = launch_forward(a, s, start, stop)) != hipSuccess) return e;
     if (mt) {
       if ((e = launch_gateup_mt(a, s)) != hipSuccess) return e;
+      if (a.act8 && (e = launch_h_round_trip(a, 1, s)) != hipSuccess) return e;
       if ((e = launch_down_mt(a, s)) != hipSuccess) return e;
     }
     if (mfma) {
@@ -146,8 +153,9 @@ hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start,
   if (mt && (e = hipStreamWaitEvent(q->mt, q->fork, 0)) != hipSuccess) return e;
   if (mfma && (e = hipStreamWaitEvent(q->mfma, q->fork, 0)) != hipSuccess) return e;
   if (mt && (e = launch_gateup_mt(a, q->mt)) != hipSuccess) return e;
+  if (mt && a.act8 && (e = launch_h_round_trip(a, 1, q->mt)) != hipSuccess) return e;
   if (mfma) {
-    if ((e = launch_forward_mfma_front(a, q->mfma)) != hipSuccess) return e;
+    if (!a.act8 && (e = launch_forward_mfma_front(a, q->mfma)) != hipSuccess) return e;
     if ((e = launch_gateup_mfma(a, q->mfma)) != hipSuccess) return e;
   }
   if (mt) {
@@ -164,6 +172,69 @@ hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start,
   }
   if (rows) e = launch_combine_rows(a, s);
   return e;
+}
+
+moe_status layer_impl(const uint16_t* x, const float* w_router, const float* logit_bias,
+                           int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                           void* workspace, size_t workspace_bytes_, void* start_event, void* stop_event,
+                           void* stream, bool act8) {
+  if (!x || !w_router || !w || !logits || !topk_ids || !topk_weights || !expert_offsets ||
+      !sorted_pairs || !active_experts || !num_active || !y || !workspace)
+    return MOE_ERR_NULL;
+  if (!w->w13_q || !w->w13_s || !w->w2_q || !w->w2_s) return MOE_ERR_NULL;
+  const int32_t E = w->num_experts, H = w->hidden;
+  moe_status st = check_route_sizes(M, E, top_k);
+  if (st != MOE_OK) return st;
+  if ((st = check_hidden(H)) != MOE_OK) return st;
+  if ((st = check_inter(w->inter)) != MOE_OK) return st;
+  if (w->has_shared != 0 && w->has_shared != 1) return MOE_ERR_SHAPE;
+  if (logit_bias && bias_row_stride != 0 && bias_row_stride != E) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w->w13_q) || !aligned16(w->w13_s) ||
+      !aligned16(w->w2_q) || !aligned16(w->w2_s) || ((uintptr_t)workspace & 255u))
+    return MOE_ERR_ALIGN;
+  if (workspace_bytes_ < workspace_layout(M, top_k, E, H, w->inter).total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_router_logits(x, w_router, logit_bias, logit_bias ? bias_row_stride : 0, M, H, E, logits,
+                           s) != hipSuccess)
+    return MOE_ERR_HIP;
+  ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
+                             num_active, y, workspace, act8);
+  if (act8) {
+    if (M <= kRoutedMaxTokens && routed_stages_x(H)) {
+      a.x = x;                       // the decode gate/up kernel rounds x to MXFP8 as it stages it
+    } else {
+      // the experts' input: x as MXFP8 values (bf16), and its codes and
+      // scales for the MFMA path, which takes them as one term
+      const bool mfma = a.mfma_min == kMfmaMinTokens;
+      if (launch_mxfp8_quantize(x, M, H, mfma ? a.xq_hi : nullptr, mfma ? a.xq_shi : nullptr,
+                                const_cast<uint16_t*>(a.x), s) != hipSuccess)
+        return MOE_ERR_HIP;
+    }
+  }
+  SlotRec* rec = const_cast<SlotRec*>(a.rec);
+  hipEvent_t start = (hipEvent_t)start_event, stop = (hipEvent_t)stop_event;
+  if (M <= kRoutedMaxTokens) {
+    // decode: every gate/up block routes itself from the logits
+    const RouteOut r{logits, topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts,
+                     num_active, rec, expert_bits(E)};
+    return hip_status(launch_forward_routed(a, r, s, start, stop));
+  }
+  if (topk_sort_fits_one_block(M)) a.lists = nullptr;   // the one-workgroup sort writes records only
+  const RecOut ro = layer_recout(a, workspace);
+  hipError_t e;
+  if (topk_sort_fits_one_block(M)) {
+    e = launch_topk_sort_small(logits, M, E, top_k, topk_ids, topk_weights, expert_offsets,
+                               sorted_pairs, active_experts, num_active, s, ro);
+  } else {
+    e = launch_topk_softmax(logits, M, E, top_k, topk_ids, topk_weights, s);
+    if (e == hipSuccess)
+      e = launch_sort_by_expert(topk_ids, M * top_k, E, expert_offsets, sorted_pairs, active_experts,
+                                num_active, s, ro);
+  }
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_experts(a, s, start, stop));
 }
 
 }  // namespace
@@ -265,49 +336,20 @@ moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float
                            int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                            void* workspace, size_t workspace_bytes_, void* start_event, void* stop_event,
                            void* stream) {
-  if (!x || !w_router || !w || !logits || !topk_ids || !topk_weights || !expert_offsets ||
-      !sorted_pairs || !active_experts || !num_active || !y || !workspace)
-    return MOE_ERR_NULL;
-  if (!w->w13_q || !w->w13_s || !w->w2_q || !w->w2_s) return MOE_ERR_NULL;
-  const int32_t E = w->num_experts, H = w->hidden;
-  moe_status st = check_route_sizes(M, E, top_k);
-  if (st != MOE_OK) return st;
-  if ((st = check_hidden(H)) != MOE_OK) return st;
-  if ((st = check_inter(w->inter)) != MOE_OK) return st;
-  if (w->has_shared != 0 && w->has_shared != 1) return MOE_ERR_SHAPE;
-  if (logit_bias && bias_row_stride != 0 && bias_row_stride != E) return MOE_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w->w13_q) || !aligned16(w->w13_s) ||
-      !aligned16(w->w2_q) || !aligned16(w->w2_s) || ((uintptr_t)workspace & 255u))
-    return MOE_ERR_ALIGN;
-  if (workspace_bytes_ < workspace_layout(M, top_k, E, H, w->inter).total) return MOE_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  if (launch_router_logits(x, w_router, logit_bias, logit_bias ? bias_row_stride : 0, M, H, E, logits,
-                           s) != hipSuccess)
-    return MOE_ERR_HIP;
-  ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
-                             num_active, y, workspace);
-  SlotRec* rec = const_cast<SlotRec*>(a.rec);
-  hipEvent_t start = (hipEvent_t)start_event, stop = (hipEvent_t)stop_event;
-  if (M <= kRoutedMaxTokens) {
-    // decode: every gate/up block routes itself from the logits
-    const RouteOut r{logits, topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts,
-                     num_active, rec, expert_bits(E)};
-    return hip_status(launch_forward_routed(a, r, s, start, stop));
-  }
-  if (topk_sort_fits_one_block(M)) a.lists = nullptr;   // the one-workgroup sort writes records only
-  const RecOut ro = layer_recout(a, workspace);
-  hipError_t e;
-  if (topk_sort_fits_one_block(M)) {
-    e = launch_topk_sort_small(logits, M, E, top_k, topk_ids, topk_weights, expert_offsets,
-                               sorted_pairs, active_experts, num_active, s, ro);
-  } else {
-    e = launch_topk_softmax(logits, M, E, top_k, topk_ids, topk_weights, s);
-    if (e == hipSuccess)
-      e = launch_sort_by_expert(topk_ids, M * top_k, E, expert_offsets, sorted_pairs, active_experts,
-                                num_active, s, ro);
-  }
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(launch_experts(a, s, start, stop));
+  return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
+                    expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
+                    start_event, stop_event, stream, false);
+}
+
+moe_status moe_layer_w4a8_timed(const uint16_t* x, const float* w_router, const float* logit_bias,
+                                int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                                float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                                int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                                void* workspace, size_t workspace_bytes_, void* start_event, void* stop_event,
+                                void* stream) {
+  return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
+                    expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
+                    start_event, stop_event, stream, true);
 }
 
 moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logit_bias,
@@ -318,6 +360,25 @@ moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logi
   return moe_layer_timed(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids,
                          topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
                          workspace, workspace_bytes_, nullptr, nullptr, stream);
+}
+
+moe_status moe_layer_w4a8(const uint16_t* x, const float* w_router, const float* logit_bias,
+                          int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                          float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                          int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                          void* workspace, size_t workspace_bytes_, void* stream) {
+  return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
+                    expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
+                    nullptr, nullptr, stream, true);
+}
+
+moe_status moe_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                              uint16_t* values, void* stream) {
+  if (!x || (!codes && !scales && !values)) return MOE_ERR_NULL;
+  if (rows < 1 || K < 32 || K % 32 || rows * K >= (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  if ((rows * (K / 32) + 255) / 256 > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || (codes && !aligned16(codes)) || (values && !aligned16(values))) return MOE_ERR_ALIGN;
+  return hip_status(launch_mxfp8_quantize(x, rows, K, codes, scales, values, (hipStream_t)stream));
 }
 
 moe_status moe_mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,

@@ -113,6 +113,75 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   p = swap32(v); return min(p.a, p.b);
 }
 
+// ---------------------------------------------------------------- MXFP8 --
+// OCP microscaling with E4M3 elements over 32-element blocks (the 8-bit
+// activations of the W4A8 variant): block exponent e = floor(log2 amax) - 8
+// (8 is the exponent of E4M3's largest power of two), clamped to the E8M0
+// range [-127, 127], -127 for an all-zero block; element code = E4M3 nearest
+// to v * 2^-e clamped to +-448, ties to even.  From the fp32 bits: a zero or
+// subnormal amax (< 2^-126) gives -127.
+__device__ __forceinline__ int mxfp8_exponent(float amax) {
+  const int f = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  return f == 0 ? -127 : max(f - 135, -127);
+}
+// Codes of a and b into bytes 0-1 (HI = false) or 2-3 (HI = true) of `word`.
+// v * 2^-e is exact (v_ldexp_f32); v_cvt_pk_fp8_f32 rounds to nearest even.
+template <bool HI>
+__device__ __forceinline__ int mxfp8_pack2(float a, float b, int e, int word) {
+  const float qa = fminf(fmaxf(ldexpf(a, -e), -448.f), 448.f);
+  const float qb = fminf(fmaxf(ldexpf(b, -e), -448.f), 448.f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(qa, qb, word, HI);
+}
+// MXFP8 round trip of one value of a block with exponent e, in fp32
+// arithmetic: clamp to +-448 * 2^e, then round to nearest even at the E4M3
+// quantum of the value's binade (3 fraction bits; below 2^(e-6), the fixed
+// subnormal quantum 2^(e-9)).  Gives the value of the code the converter
+// above produces, without the conversion instructions.
+__device__ __forceinline__ float mxfp8_round_value(float v, int e) {
+  const float lim = ldexpf(448.f, e);
+  const float c = fminf(fmaxf(v, -lim), lim);
+  const int f = (int)((__float_as_uint(c) >> 23) & 0xFFu) - 127;   // floor(log2 |c|) (-127 for 0 / subnormal)
+  const int qe = max(f, e - 6) - 3;
+  return ldexpf(__builtin_rintf(ldexpf(c, -qe)), qe);
+}
+// MXFP8 round trip of 16 bf16 values (8 words, low half first) that are half
+// of a 32-element block whose other half lane ^ 1 holds and passes at the
+// same time (the exchange is a DPP quad swap, so lane ^ 1 must be active).
+// Each value becomes the value of its code, as bf16 (exact for blocks whose
+// largest magnitude is at least 2^-110).
+__device__ __forceinline__ void mxfp8_round_trip16(uint32_t (&w)[8]) {
+  uint32_t m = 0u;                                   // |v| as bf16 bits: ordered like the values
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  m = max(m, dpp_quad_xor1(m));
+  const int e = mxfp8_exponent(__uint_as_float(m << 16));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float lo = mxfp8_round_value(bf16_bits_to_f32(w[i] & 0xFFFFu), e);
+    const float hi = mxfp8_round_value(bf16_bits_to_f32(w[i] >> 16), e);
+    w[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  }
+}
+
+// MXFP8 round trip of 8 bf16 values (one uint4) that are a quarter of a
+// 32-element block held by the four lanes of a DPP quad (all four active).
+__device__ __forceinline__ void mxfp8_round_trip8_quad(uint4& u) {
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  m = max(m, dpp_quad_xor1(m));
+  m = max(m, dpp_quad_xor2(m));
+  const int e = mxfp8_exponent(__uint_as_float(m << 16));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = mxfp8_round_value(bf16_bits_to_f32(w[i] & 0xFFFFu), e);
+    const float hi = mxfp8_round_value(bf16_bits_to_f32(w[i] >> 16), e);
+    w[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  }
+  u = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Workgroup barrier that orders LDS only: it does not wait for outstanding
 // global loads (gfx950 barriers do not imply a memory wait), so prefetched
 // weights stay in flight across it.  (__syncthreads waits for all of them.)

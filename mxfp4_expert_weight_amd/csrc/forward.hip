@@ -143,7 +143,9 @@ __device__ __forceinline__ SlotRec route_slot(const ForwardArgs& a, const RouteS
 // at most 3 waves per SIMD: the codes, scales and staged activations of a wave
 // stay in registers without spilling (M=1 needs under 2 waves per SIMD anyway).
 // C > 0: the block routes itself (C = experts per lane of the top-k).
-template <bool SHORT, int C>
+// A8 (W4A8 decode, short rows): x goes through the MXFP8 round trip as it is
+// staged (the four threads of a DPP quad hold one 32-element block).
+template <bool SHORT, int C, bool A8 = false>
 __global__ __launch_bounds__(GU_WPB * kWave) __attribute__((amdgpu_waves_per_eu(1, 3)))
 void gateup_kernel(ForwardArgs a, RouteOut r) {
   if (C > 0 || !a.yp) {   // every block zeroes a share of y for the down kernel's scatter-add
@@ -179,6 +181,7 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
 #pragma unroll
         for (int q = 0; q < kXPer; ++q) {
           const int i = threadIdx.x + q * GU_WPB * kWave;
+          if constexpr (A8) mxfp8_round_trip8_quad(xs[q]);   // quads never straddle nxv (H % 32 == 0)
           if (i < nxv) s_x[i] = xs[q];
         }
       }
@@ -335,6 +338,13 @@ hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;   // y is zeroed from here on
+  // W4A8: h goes through the MXFP8 round trip once, in place, between the
+  // two kernels (decode: every row; batches: the rows of this path's experts)
+  if (a.act8) {
+    err = routed ? launch_mxfp8_round_trip_rows(a.h, (int64_t)a.M * a.k + a.M, a.I, s)
+                 : launch_h_round_trip(a, 0, s);
+    if (err != hipSuccess) return err;
+  }
   hipExtLaunchKernelGGL(dn, gdn, bdn, 0, s, nullptr, nullptr, 0, a);
   return hipGetLastError();
 }
@@ -348,14 +358,17 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start,
                      start, stop, zeroed);
 }
 
+bool routed_stages_x(int H) { return H <= GU_SHORT_H; }
+
 hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s, hipEvent_t start,
                                  hipEvent_t stop) {
   const bool short_h = a.H <= GU_SHORT_H;
+  const bool a8x = a.act8 && short_h;                // x rounded while staged (else a.x is already MXFP8)
   void (*gu)(ForwardArgs, RouteOut);
   if (topk_lane_experts(a.E) == 8)
-    gu = short_h ? gateup_kernel<true, 8> : gateup_kernel<false, 8>;
+    gu = short_h ? (a8x ? gateup_kernel<true, 8, true> : gateup_kernel<true, 8>) : gateup_kernel<false, 8>;
   else
-    gu = short_h ? gateup_kernel<true, 16> : gateup_kernel<false, 16>;
+    gu = short_h ? (a8x ? gateup_kernel<true, 16, true> : gateup_kernel<true, 16>) : gateup_kernel<false, 16>;
   return launch_pair(gu, a, r, true, s, start, stop);
 }
 

@@ -58,6 +58,12 @@ struct ForwardArgs {
   // the few-token experts' at lists[max_slots..), counts in the header; the
   // kernels of those paths loop over them instead of a grid row per slot.
   const int* lists;
+  // W4A8 variant: the experts take x as MXFP8 values (bf16: a.x holds them,
+  // or the decode gate/up kernel rounds x as it stages it), h goes through an
+  // MXFP8 round trip in place between gate/up and down, and the MFMA path
+  // carries x and h as one MXFP8 term (codes in xq_hi/hq_hi, scales in
+  // xq_shi/hq_shi; the _lo terms are unused).
+  int act8;
 };
 
 // The few-token matrix-core path (mt.hip): batches of more than
@@ -96,7 +102,7 @@ inline bool combine_rows(int M, int k, int H) {
   return M >= kCombineRowsMinTokens && ((size_t)M * k + M) * H * sizeof(float) <= kCombineRowsMaxBytes;
 }
 struct WorkspaceLayout {
-  size_t rec, h, xq_hi, xq_lo, xq_shi, xq_slo, hq_hi, hq_lo, hq_shi, hq_slo, items, yp, inv, lists, total;
+  size_t rec, h, xq_hi, xq_lo, xq_shi, xq_slo, hq_hi, hq_lo, hq_shi, hq_slo, items, yp, inv, lists, xdq, total;
 };
 inline WorkspaceLayout workspace_layout(int M, int k, int E, int H, int I) {
   WorkspaceLayout w{};
@@ -121,6 +127,7 @@ inline WorkspaceLayout workspace_layout(int M, int k, int E, int H, int I) {
     w.inv = take((size_t)M * k * sizeof(int));
   }
   if (M > kRoutedMaxTokens) w.lists = take(2 * (size_t)max_slots(M, k, E) * sizeof(int));
+  w.xdq = take((size_t)M * H * sizeof(uint16_t));   // W4A8: the experts' MXFP8 x as bf16 values
   w.total = o;
   return w;
 }
@@ -176,7 +183,10 @@ hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start = nullptr,
                           hipEvent_t stop = nullptr, hipEvent_t zeroed = nullptr);
 // Gate/up with the top-k and the expert sort done in every block from the
-// logits (M <= kRoutedMaxTokens), then down.
+// logits (M <= kRoutedMaxTokens), then down.  W4A8 (act8): rows of at most
+// this many elements are rounded to MXFP8 as the kernel stages x (a.x is the
+// bf16 x); longer rows need a.x to hold the MXFP8 values already.
+bool routed_stages_x(int H);
 hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s,
                                  hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // MFMA path (mfma.hip): two-term MXFP8 quantisation of x, the dense gate/up
@@ -194,6 +204,14 @@ hipError_t launch_records(const int* offsets, const int* sorted_pairs, const int
 hipError_t launch_combine_rows(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols, float* out,
                           hipStream_t st);
+// MXFP8 quantisation of bf16 rows [rows][K] (mxfp8.hip): codes, scale bytes
+// and the codes' values as bf16, each optional.
+hipError_t launch_mxfp8_quantize(const uint16_t* src, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
+                                 uint16_t* deq, hipStream_t s);
+// MXFP8 round trip (codes' values, as bf16) of rows [rows][K] in place; and
+// of the h rows of one path's experts (path 0: GEMV, 1: few-token) in place.
+hipError_t launch_mxfp8_round_trip_rows(uint16_t* p, int64_t rows, int K, hipStream_t s);
+hipError_t launch_h_round_trip(const ForwardArgs& a, int path, hipStream_t s);
 // FP8 LM head (lmhead.hip).
 hipError_t launch_lmhead_quantize(const uint16_t* w, int V, int H, uint8_t* codes, float* scales, hipStream_t s);
 hipError_t launch_lmhead_fp8(const uint16_t* x, const uint8_t* codes, const float* scales, int M, int V, int H,

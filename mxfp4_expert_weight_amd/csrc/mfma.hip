@@ -10,6 +10,9 @@
 // encodes the residual of hi.  Each term keeps 4 significant bits, so the
 // pair keeps about 8, and the two products accumulate into one fp32 tile.
 //
+// The W4A8 variant carries x and h as one MXFP8 term (OCP rule, common.h),
+// so each K chunk takes one scaled MFMA instead of two.
+//
 // Operand layout of the instruction (16 x 16 output tile, K = 128), lane l:
 //   FP4 A:   row l%16, K = 32*(l/16) + p for nibble p of 16 bytes (low nibble first)
 //   FP8 B:   column l%16, K = 64*(p/16) + 16*(l/16) + p%16 for byte p of 32 bytes
@@ -116,6 +119,21 @@ __global__ __launch_bounds__(256) void quantize_x_kernel(const uint16_t* __restr
   slo[b] = (uint8_t)sl;
 }
 
+// W4A8: 32 values -> one MXFP8 term (codes, E8M0 byte), OCP block rule.
+__device__ __forceinline__ void encode_one_term(const float (&v)[32], uint32_t (&c)[8], uint32_t& sb) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const int e = mxfp8_exponent(amax);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    int w = mxfp8_pack2<false>(v[4 * q], v[4 * q + 1], e, 0);
+    w = mxfp8_pack2<true>(v[4 * q + 2], v[4 * q + 3], e, w);
+    c[q] = (uint32_t)w;
+  }
+  sb = (uint32_t)(e + 127);
+}
+
 // ------------------------------------------------------ staging in LDS --
 // A work item's 64 token rows of one 128-element chunk, both terms, are staged
 // by the 256 threads of the workgroup: thread (row c, quarter q) moves bytes
@@ -128,15 +146,18 @@ struct StageRegs {
 
 // Raw loads (clamped row); the mask for rows past the tile is applied when
 // the registers are written to LDS, so the load's wait is not forced early.
+template <bool ONE>
 __device__ __forceinline__ void stage_load(StageRegs& st, const uint8_t* qhi, const uint8_t* qlo,
                                            const uint8_t* shi, const uint8_t* slo, int64_t row, int K, int kc,
                                            int q) {
   const uint4* ph = reinterpret_cast<const uint4*>(qhi + row * K + kc * kMfmaK + 32 * q);
-  const uint4* pl = reinterpret_cast<const uint4*>(qlo + row * K + kc * kMfmaK + 32 * q);
   st.h0 = ph[0]; st.h1 = ph[1];
-  st.l0 = pl[0]; st.l1 = pl[1];
   st.sh = shi[row * (K / 32) + kc * 4 + q];
-  st.sl = slo[row * (K / 32) + kc * 4 + q];
+  if constexpr (!ONE) {
+    const uint4* pl = reinterpret_cast<const uint4*>(qlo + row * K + kc * kMfmaK + 32 * q);
+    st.l0 = pl[0]; st.l1 = pl[1];
+    st.sl = slo[row * (K / 32) + kc * 4 + q];
+  }
 }
 
 struct __align__(16) StageBuf {
@@ -146,17 +167,20 @@ struct __align__(16) StageBuf {
   uint8_t slo[MF_TT * 4];
 };
 
+template <bool ONE>
 __device__ __forceinline__ void stage_store(StageBuf& b, const StageRegs& st, int c, int q, bool valid) {
   // mask word by word (a select of whole vectors goes through scratch memory)
   const uint32_t m = valid ? 0xFFFFFFFFu : 0u;
   uint4* dh = reinterpret_cast<uint4*>(b.hi + c * MF_PITCH + 32 * q);
-  uint4* dl = reinterpret_cast<uint4*>(b.lo + c * MF_PITCH + 32 * q);
   dh[0] = make_uint4(st.h0.x & m, st.h0.y & m, st.h0.z & m, st.h0.w & m);
   dh[1] = make_uint4(st.h1.x & m, st.h1.y & m, st.h1.z & m, st.h1.w & m);
-  dl[0] = make_uint4(st.l0.x & m, st.l0.y & m, st.l0.z & m, st.l0.w & m);
-  dl[1] = make_uint4(st.l1.x & m, st.l1.y & m, st.l1.z & m, st.l1.w & m);
   b.shi[c * 4 + q] = (uint8_t)(st.sh & m);
-  b.slo[c * 4 + q] = (uint8_t)(st.sl & m);
+  if constexpr (!ONE) {
+    uint4* dl = reinterpret_cast<uint4*>(b.lo + c * MF_PITCH + 32 * q);
+    dl[0] = make_uint4(st.l0.x & m, st.l0.y & m, st.l0.z & m, st.l0.w & m);
+    dl[1] = make_uint4(st.l1.x & m, st.l1.y & m, st.l1.z & m, st.l1.w & m);
+    b.slo[c * 4 + q] = (uint8_t)(st.sl & m);
+  }
 }
 
 // B operand of token sub-tile s for lane (g, j): bytes [16g, +16) and
@@ -180,6 +204,7 @@ __device__ __forceinline__ v8i frag_b(const uint8_t* rows, int s, int g, int j) 
 // prefetched weights stay in flight across them.
 constexpr int MF_ADEPTH = 8;
 static_assert(MF_ADEPTH % 2 == 0, "the staging registers alternate by chunk parity");
+template <bool ONE>
 __device__ __forceinline__ void mfma_tile(v4f (&acc)[4], const uint8_t* row_q, const uint8_t* row_s,
                                           const uint8_t* qhi, const uint8_t* qlo, const uint8_t* shi,
                                           const uint8_t* slo, const int64_t stage_row, bool stage_valid, int K,
@@ -201,9 +226,9 @@ __device__ __forceinline__ void mfma_tile(v4f (&acc)[4], const uint8_t* row_q, c
   // activation chunks: loaded two chunks ahead into st[chunk & 1], written to
   // LDS one chunk ahead (chunks past the end repeat the last: never read)
   StageRegs st[2];
-  stage_load(st[0], qhi, qlo, shi, slo, stage_row, K, 0, q);
-  stage_store(buf[0], st[0], c, q, stage_valid);
-  stage_load(st[1], qhi, qlo, shi, slo, stage_row, K, min(1, nk - 1), q);
+  stage_load<ONE>(st[0], qhi, qlo, shi, slo, stage_row, K, 0, q);
+  stage_store<ONE>(buf[0], st[0], c, q, stage_valid);
+  stage_load<ONE>(st[1], qhi, qlo, shi, slo, stage_row, K, min(1, nk - 1), q);
   block_barrier_lds();
   for (int kb = 0; kb < nk; kb += MF_ADEPTH) {
 #pragma unroll
@@ -211,7 +236,7 @@ __device__ __forceinline__ void mfma_tile(v4f (&acc)[4], const uint8_t* row_q, c
       const int kc = kb + d;
       if (kc < nk) {                               // uniform
         const int cur = kc & 1;                    // == d & 1 (MF_ADEPTH is even)
-        stage_load(st[d & 1], qhi, qlo, shi, slo, stage_row, K, min(kc + 2, nk - 1), q);
+        stage_load<ONE>(st[d & 1], qhi, qlo, shi, slo, stage_row, K, min(kc + 2, nk - 1), q);
         v8i a;
         a[0] = (int)ar[d].x; a[1] = (int)ar[d].y; a[2] = (int)ar[d].z; a[3] = (int)ar[d].w;
         a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
@@ -224,13 +249,15 @@ __device__ __forceinline__ void mfma_tile(v4f (&acc)[4], const uint8_t* row_q, c
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const v8i bh = frag_b(buf[cur].hi, s, g, j);
-          const v8i bl = frag_b(buf[cur].lo, s, g, j);
           const int sbh = buf[cur].shi[(16 * s + j) * 4 + g];
-          const int sbl = buf[cur].slo[(16 * s + j) * 4 + g];
           acc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bh, acc[s], 4, 0, 0, sa, 0, sbh);
-          acc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bl, acc[s], 4, 0, 0, sa, 0, sbl);
+          if constexpr (!ONE) {
+            const v8i bl = frag_b(buf[cur].lo, s, g, j);
+            const int sbl = buf[cur].slo[(16 * s + j) * 4 + g];
+            acc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bl, acc[s], 4, 0, 0, sa, 0, sbl);
+          }
         }
-        stage_store(buf[cur ^ 1], st[(d + 1) & 1], c, q, stage_valid);
+        stage_store<ONE>(buf[cur ^ 1], st[(d + 1) & 1], c, q, stage_valid);
         block_barrier_lds();
       }
     }
@@ -246,7 +273,9 @@ __device__ __forceinline__ int item_token(const ForwardArgs& a, const SlotRec& r
 // Workgroup (32 intermediate indices, items): waves 0-1 take the 32 gate
 // rows, waves 2-3 the 32 up rows, each over the item's 64 tokens.  Epilogue:
 // h = SiLU(g) * u through LDS, then one thread per token encodes its 32
-// h values (one MXFP8 block along the down projection's K) in two terms.
+// h values (one MXFP8 block along the down projection's K) in two terms
+// (ONE, W4A8: h rounded to bf16, then one MXFP8 term).
+template <bool ONE>
 __global__ __launch_bounds__(MF_WAVES * kWave) void gateup_mfma_kernel(ForwardArgs a) {
   __shared__ StageBuf buf[2];
   __shared__ float ul[MF_TT][MF_J + 1];
@@ -267,7 +296,7 @@ __global__ __launch_bounds__(MF_WAVES * kWave) void gateup_mfma_kernel(ForwardAr
     const bool sv = c < nt;
     const int64_t srow = sv ? item_token(a, rec, t0 + c) : 0;
     v4f acc[4];
-    mfma_tile(acc, row_q, row_s, a.xq_hi, a.xq_lo, a.xq_shi, a.xq_slo, srow, sv, a.H, buf);
+    mfma_tile<ONE>(acc, row_q, row_s, a.xq_hi, a.xq_lo, a.xq_shi, a.xq_slo, srow, sv, a.H, buf);
     // acc[s][r] = (gate or up) row 16*half + 4g + r, token 16s + j
     if (is_up) {
 #pragma unroll
@@ -291,17 +320,28 @@ __global__ __launch_bounds__(MF_WAVES * kWave) void gateup_mfma_kernel(ForwardAr
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] = ul[tc][i];
-      uint32_t h[8], l[8], sh, sl;
-      encode_two_term(v, h, l, sh, sl);
       const int64_t hrow = rec.hrow0 + t0 + tc;
-      uint4* dh = reinterpret_cast<uint4*>(a.hq_hi + hrow * a.I + j0);
-      uint4* dl = reinterpret_cast<uint4*>(a.hq_lo + hrow * a.I + j0);
-      dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
-      dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
-      dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
-      dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
-      a.hq_shi[hrow * (a.I / 32) + j0 / 32] = (uint8_t)sh;
-      a.hq_slo[hrow * (a.I / 32) + j0 / 32] = (uint8_t)sl;
+      if constexpr (ONE) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) v[i] = bf16_bits_to_f32(f32_to_bf16_bits(v[i]));
+        uint32_t h[8], sh;
+        encode_one_term(v, h, sh);
+        uint4* dh = reinterpret_cast<uint4*>(a.hq_hi + hrow * a.I + j0);
+        dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
+        a.hq_shi[hrow * (a.I / 32) + j0 / 32] = (uint8_t)sh;
+      } else {
+        uint32_t h[8], l[8], sh, sl;
+        encode_two_term(v, h, l, sh, sl);
+        uint4* dh = reinterpret_cast<uint4*>(a.hq_hi + hrow * a.I + j0);
+        uint4* dl = reinterpret_cast<uint4*>(a.hq_lo + hrow * a.I + j0);
+        dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
+        dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
+        dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
+        dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+        a.hq_shi[hrow * (a.I / 32) + j0 / 32] = (uint8_t)sh;
+        a.hq_slo[hrow * (a.I / 32) + j0 / 32] = (uint8_t)sl;
+      }
     }
     block_barrier_lds();
   }
@@ -310,7 +350,8 @@ __global__ __launch_bounds__(MF_WAVES * kWave) void gateup_mfma_kernel(ForwardAr
 // ---------------------------------------------------------------- down --
 // Workgroup (64 output rows, items): wave w takes rows 16w..16w+15 over the
 // item's 64 tokens; the epilogue adds w_token * result into y (fp32 atomics,
-// as the GEMV path's combine).
+// as the GEMV path's combine).  ONE (W4A8): h is one MXFP8 term.
+template <bool ONE>
 __global__ __launch_bounds__(MF_WAVES * kWave) void down_mfma_kernel(ForwardArgs a) {
   __shared__ StageBuf buf[2];
   const int n_items = a.hdr->mfma_items;
@@ -329,7 +370,7 @@ __global__ __launch_bounds__(MF_WAVES * kWave) void down_mfma_kernel(ForwardArgs
     const bool sv = c < nt;
     const int64_t srow = sv ? (int64_t)rec.hrow0 + t0 + c : 0;
     v4f acc[4];
-    mfma_tile(acc, row_q, row_s, a.hq_hi, a.hq_lo, a.hq_shi, a.hq_slo, srow, sv, a.I, buf);
+    mfma_tile<ONE>(acc, row_q, row_s, a.hq_hi, a.hq_lo, a.hq_shi, a.hq_slo, srow, sv, a.I, buf);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int tc = 16 * s + j;
@@ -375,13 +416,21 @@ hipError_t launch_forward_mfma_front(const ForwardArgs& a, hipStream_t s) {
 
 hipError_t launch_gateup_mfma(const ForwardArgs& a, hipStream_t s) {
   const int tiles = a.I / MF_J;
-  gateup_mfma_kernel<<<dim3(tiles, item_rows(tiles, a.M, a.k)), dim3(MF_WAVES * kWave), 0, s>>>(a);
+  const dim3 grid(tiles, item_rows(tiles, a.M, a.k)), block(MF_WAVES * kWave);
+  if (a.act8)
+    gateup_mfma_kernel<true><<<grid, block, 0, s>>>(a);
+  else
+    gateup_mfma_kernel<false><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mfma(const ForwardArgs& a, hipStream_t s) {
   const int tiles = a.H / MF_R;
-  down_mfma_kernel<<<dim3(tiles, item_rows(tiles, a.M, a.k)), dim3(MF_WAVES * kWave), 0, s>>>(a);
+  const dim3 grid(tiles, item_rows(tiles, a.M, a.k)), block(MF_WAVES * kWave);
+  if (a.act8)
+    down_mfma_kernel<true><<<grid, block, 0, s>>>(a);
+  else
+    down_mfma_kernel<false><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -79,11 +79,17 @@ class LayerBuffers:
 
 
 def run_layer(d: DeviceLayerSet, b: LayerBuffers, w: Optional[binding.moe_mxfp4_weights] = None,
-              stream=None, fused: bool = True):
+              stream=None, fused: bool = True, w4a8: bool = False):
     """One layer: moe_layer (fused=True) or moe_route -> moe_sort_by_expert ->
-    moe_mxfp4_forward (fused=False); same outputs, stream-ordered."""
+    moe_mxfp4_forward (fused=False); same outputs, stream-ordered.  w4a8:
+    moe_layer_w4a8 (MXFP8 activations into the experts)."""
     if w is None:
         w = d.weights()
+    if w4a8:
+        binding.moe_layer_w4a8(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, b.logits, b.ids,
+                               b.weights, b.offsets, b.pairs, b.active, b.num_active, b.y, b.ws, b.ws_bytes,
+                               stream)
+        return
     if fused:
         binding.moe_layer(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, b.logits, b.ids,
                           b.weights, b.offsets, b.pairs, b.active, b.num_active, b.y, b.ws, b.ws_bytes,

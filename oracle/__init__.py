@@ -14,6 +14,17 @@ closed forms, exact power-of-two metamorphics).  No function here is
 "parity unpinned".
 """
 from .lmhead_oracle import E4M3_MAX, e4m3_decode, e4m3_round, lmhead_logits, lmhead_quantize  # noqa: F401
+from .w4a8_oracle import (  # noqa: F401
+    bf16_round,
+    expert_hidden,
+    expert_mlp_w4a8,
+    moe_layer_w4a8,
+    moe_layer_w4a8_tokens,
+    mxfp8_dequantize,
+    mxfp8_fake_quant,
+    mxfp8_quantize,
+    mxfp8_scale_exponent,
+)
 from .moe_oracle import (  # noqa: F401
     E2M1_MAGNITUDE,
     bf16_bits_to_f64,

@@ -100,3 +100,28 @@ def check_routing(ids_gpu, w_gpu, logits_gpu, ref_logits, bound, k, what=""):
         tol = 2.0 * b[g].max() + (k + 16 + float(sel.max() - sel.min())) * U
         assert np.all(np.abs(w_gpu[t] - w_ref) <= tol), f"{what}: token {t} weights"
     return ambiguous
+
+
+def expected_paths(wl, ids):
+    """(GEMV, few-token matrix-core, scaled-MFMA) expert counts of a layer.
+    Scaled MFMA: experts with >= 16 tokens when M >= 16 and H, I are multiples
+    of 128.  Few-token matrix cores: 3..16 tokens (below the MFMA range) when
+    M > 4 and H, I are multiples of 256.  The rest: GEMV."""
+    counts = np.bincount(np.asarray(ids).ravel(), minlength=wl.E)
+    n = [int(c) for c in counts if c > 0] + ([wl.M] if wl.shared else [])
+    mfma_on = wl.M >= 16 and wl.H % 128 == 0 and wl.I % 128 == 0
+    mt_on = wl.M > 4 and wl.H % 256 == 0 and wl.I % 256 == 0
+    paths = [0, 0, 0]
+    for c in n:
+        if mfma_on and c >= 16:
+            paths[2] += 1
+        elif mt_on and 3 <= c <= 16:
+            paths[1] += 1
+        else:
+            paths[0] += 1
+    return paths
+
+
+def assert_paths(hdr, wl, ids, what):
+    got = [hdr["gemv_experts"], hdr["mt_experts"], hdr["mfma_experts"]]
+    assert got == expected_paths(wl, ids), f"{what}: expert paths (gemv, mt, mfma) {got}"

@@ -96,10 +96,11 @@ def test_forward_host_checks(lib):
     assert _status(f, *(args[:11] + [ws - 1, 0])) == B.MOE_ERR_WORKSPACE
 
 
-def test_layer_host_checks(lib):
+@pytest.mark.parametrize("name", ["moe_layer", "moe_layer_w4a8"])
+def test_layer_host_checks(lib, name):
     w = B.make_weights(A, A, A, A, 512, 2560, 768, 1)
     ws = B.moe_workspace_bytes(1, 8, 512, 2560, 768)
-    f = B.moe_layer
+    f = getattr(B, name)
     args = [A, A, None, 0, w, 1, 8, A, A, A, A, A, A, A, A, A, ws, 0]
     assert _status(f, *([None] + args[1:])) == B.MOE_ERR_NULL
     assert _status(f, *(args[:4] + [None] + args[5:])) == B.MOE_ERR_NULL
@@ -139,3 +140,14 @@ def test_lmhead_host_checks(lib):
     assert _status(p, A, A, A, 5, 10, 8192, A, 0) == B.MOE_ERR_SHAPE     # M * H > 32768
     assert _status(p, A, A, A, 1, 0, 2560, A, 0) == B.MOE_ERR_SHAPE
     assert _status(p, A, MIS, A, 1, 10, 2560, A, 0) == B.MOE_ERR_ALIGN
+
+
+def test_mxfp8_quantize_host_checks(lib):
+    f = B.moe_mxfp8_quantize
+    assert _status(f, None, 4, 64, A, A, A, 0) == B.MOE_ERR_NULL
+    assert _status(f, A, 4, 64, None, None, None, 0) == B.MOE_ERR_NULL        # no output at all
+    assert _status(f, A, 0, 64, A, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(f, A, 4, 48, A, A, A, 0) == B.MOE_ERR_SHAPE                # K % 32
+    assert _status(f, A, 4, 0, A, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(f, MIS, 4, 64, A, A, A, 0) == B.MOE_ERR_ALIGN
+    assert _status(f, A, 4, 64, MIS, A, A, 0) == B.MOE_ERR_ALIGN

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_common import assert_layer_close, check_routing, logit_error_bound, need_gpu, say
+from gpu_common import assert_layer_close, assert_paths, check_routing, logit_error_bound, need_gpu, say
 from mxfp4_expert_weight_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -27,31 +27,6 @@ def _run(torch, ls, fused=True):
                logits=b.logits.cpu().numpy(), hdr=b.header(),
                num_active=int(b.num_active.item()))
     return out, d, b
-
-
-def expected_paths(wl, ids):
-    """(GEMV, few-token matrix-core, scaled-MFMA) expert counts of a layer.
-    Scaled MFMA: experts with >= 16 tokens when M >= 16 and H, I are multiples
-    of 128.  Few-token matrix cores: 3..16 tokens (below the MFMA range) when
-    M > 4 and H, I are multiples of 256.  The rest: GEMV."""
-    counts = np.bincount(np.asarray(ids).ravel(), minlength=wl.E)
-    n = [int(c) for c in counts if c > 0] + ([wl.M] if wl.shared else [])
-    mfma_on = wl.M >= 16 and wl.H % 128 == 0 and wl.I % 128 == 0
-    mt_on = wl.M > 4 and wl.H % 256 == 0 and wl.I % 256 == 0
-    paths = [0, 0, 0]
-    for c in n:
-        if mfma_on and c >= 16:
-            paths[2] += 1
-        elif mt_on and 3 <= c <= 16:
-            paths[1] += 1
-        else:
-            paths[0] += 1
-    return paths
-
-
-def assert_paths(hdr, wl, ids, what):
-    got = [hdr["gemv_experts"], hdr["mt_experts"], hdr["mfma_experts"]]
-    assert got == expected_paths(wl, ids), f"{what}: expert paths (gemv, mt, mfma) {got}"
 
 
 def _check_full(torch, ls, what, fused=True):

@@ -1,0 +1,234 @@
+"""GPU parity of the W4A8 variant (MXFP8 activations into the MXFP4 experts)
+against the float64 W4A8 oracle, through the C ABI.
+
+Quantiser (moe_mxfp8_quantize): codes and scale bytes bit-exact; the codes'
+values bit-exact as bf16 for blocks inside the documented range (largest
+magnitude >= 2^-110).  Both sides decide on the same bf16 inputs with exact
+power-of-two scaling, so the codes are a deterministic function of the input.
+
+Layer (moe_layer_w4a8): h is quantised from the GPU's fp32 h and from the
+oracle's float64 h.  An h element whose value lies within fp32 rounding
+distance of an MXFP8 decision point (an E4M3 midpoint, or a power of two for
+a block's largest element) may take the neighbouring code on the GPU: both
+are correct roundings of a correctly computed h.  Such elements are rare (the
+fp32 error of h is ~1e-6 of it, an E4M3 step 1/16 to 1/8 of it), but one step
+moves the token's whole output row by up to 1/8 of that element's
+contribution, which can exceed the bf16 layer's per-element bar
+|gpu - ref| <= 1e-2 (|ref| + rms(ref)).  So the bar here is three-fold:
+  * every element within the bf16 bar plus one step per token and expert,
+    w * max_i (2 gap_i) |Wd[r][i]| (gap_i: the distance from h_i's code value
+    to the next one up; doubled for a block whose scale steps up);
+  * at most 1% of the elements beyond the bf16 bar (steps are rare);
+  * rms(gpu - ref) <= 3e-3 rms(ref): an activation left unquantised or
+    quantised at the wrong point moves y by 1-3% rms.
+The rounding rule itself is checked bit-exactly by the quantiser test: every
+path takes its codes from the same device routine.
+Routing follows the bf16 layer's rules."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import assert_paths, check_routing, logit_error_bound, need_gpu, say
+from mxfp4_expert_weight_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _quantize_gpu(torch, x_bits):
+    from mxfp4_expert_weight_amd import binding
+    rows, K = x_bits.shape
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+    codes = torch.full((rows, K), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, K // 32), 0xAB, dtype=torch.uint8, device="cuda")
+    values = torch.full((rows, K), -1, dtype=torch.int16, device="cuda")
+    binding.moe_mxfp8_quantize(x, rows, K, codes, scales, values)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy(), values.cpu().numpy().view(np.uint16)
+
+
+def _blocky_rows(rows, K, seed):
+    """bf16 rows whose 32-blocks span many magnitudes, with zero blocks,
+    signed zeros, ties at E4M3 midpoints and blocks that saturate."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((rows, K)) * 2.0 ** rng.integers(-60, 60, (rows, K // 32)).repeat(32, axis=1)
+    nb = rows * K // 32
+    flat = v.reshape(nb, 32)
+    pick = rng.random(nb)
+    flat[pick < 0.05] = 0.0                                            # all-zero blocks
+    flat[(pick >= 0.05) & (pick < 0.08)] = -0.0                        # negative zeros
+    ties = (pick >= 0.08) & (pick < 0.2)                               # E4M3 midpoints: X = 2^-8, and
+    flat[ties] = (rng.integers(8, 14, (int(ties.sum()), 32)) * 2 + 1) / 16.0 * np.where(   # odd * 16 / X
+        rng.random((int(ties.sum()), 32)) < 0.5, -1, 1)                # is midway in [256, 512)
+    flat[ties, 0] = 1.75 + 1.0 / 64                                    # pins the block max below 2
+    small = (pick >= 0.2) & (pick < 0.25)                              # clamped scale exponent
+    flat[small] = rng.standard_normal((int(small.sum()), 32)) * 2.0 ** -128
+    sat = (pick >= 0.25) & (pick < 0.3)                                # elements above 448 X
+    flat[sat, 0] = 1.9999 * 2.0 ** 5
+    return synth.f32_to_bf16_bits(v.astype(np.float32))
+
+
+@pytest.mark.parametrize("rows,K", [(7, 96), (64, 2560), (3, 8192), (1, 32), (513, 768)])
+def test_mxfp8_quantize_bit_exact(rows, K):
+    torch = need_gpu()
+    say(f"mxfp8 quantize rows={rows} K={K}")
+    xb = _blocky_rows(rows, K, seed=rows * 31 + K)
+    codes, scales, values = _quantize_gpu(torch, xb)
+    xf = oracle.bf16_bits_to_f64(xb)
+    want_c, want_s = oracle.mxfp8_quantize(xf)
+    assert np.array_equal(scales, want_s)
+    assert np.array_equal(codes, want_c), np.argwhere(codes != want_c)[:5]
+    want_v = oracle.mxfp8_dequantize(want_c, want_s)
+    amax = np.abs(xf).reshape(rows, K // 32, 32).max(axis=2).repeat(32, axis=1)
+    inside = amax >= 2.0 ** -110
+    got_v = oracle.bf16_bits_to_f64(values)
+    assert np.array_equal(got_v[inside], want_v[inside])
+    assert inside.mean() > 0.8
+
+
+U = 2.0 ** -24
+
+
+def flip_allowance(ls, ids, weights, xq_rows):
+    """Allowance [tokens][H]: for each of a token's experts, one h element may
+    take the neighbouring MXFP8 code (the module docstring says why), so
+    allow[t][r] = sum over the token's experts of w * max_i gap_i * |Wd[r][i]|,
+    gap_i the distance from h_i's code value to the next code value away from
+    zero (a scale step up for a block's largest element is covered by it).
+    ids, weights: the oracle's routing of the tokens; xq_rows: the oracle's
+    quantised x rows."""
+    wl = ls.wl
+    I, H = wl.I, wl.H
+    grid = np.unique(np.abs(oracle.e4m3_decode(np.arange(0x7F))))     # 0 .. 448
+    step = np.append(np.diff(grid), grid[-1] - grid[-2])             # gap to the next value up
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = np.abs(oracle.dequant_mxfp4(ls.w2_q[e], ls.w2_s[e]))
+        return cache[e]
+
+    allow = np.zeros((len(xq_rows), H))
+    for n in range(len(xq_rows)):
+        pairs = [(int(e), float(wt)) for e, wt in zip(ids[n], weights[n])]
+        if wl.shared:
+            pairs.append((wl.E, 1.0))
+        for e, wt in pairs:
+            h = oracle.bf16_round(oracle.expert_hidden(xq_rows[n][None], ls.w13_q[e], ls.w13_s[e]))[0]
+            codes, sb = oracle.mxfp8_quantize(h[None])
+            X = np.repeat(2.0 ** (sb[0].astype(np.int64) - 127), 32)
+            mag = np.abs(oracle.e4m3_decode(codes[0]))
+            gap = 2 * step[np.searchsorted(grid, mag)] * X              # x2: the block scale may step up too
+            allow[n] += wt * np.max(expert(e) * gap[None, :], axis=1)
+    return allow
+
+
+def assert_w4a8_close(y_gpu, y_ref, rms, allow, what):
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite output"
+    err = np.abs(y_gpu - y_ref)
+    base = 1e-2 * (np.abs(y_ref) + rms)
+    over = float(np.mean(err > base))
+    rel = float(np.sqrt(np.mean(err ** 2)) / rms)
+    say(f"  {what}: worst err/bar {(err / base).max():.3g}, {over:.2%} beyond the bar, rms err {rel:.2e} of rms")
+    assert float((err / (base + allow)).max()) <= 1.0, f"{what}: beyond the bar plus one step per row"
+    assert over <= 0.01, f"{what}: {over:.2%} of the elements beyond the bar"
+    assert rel <= 3e-3, f"{what}: rms error {rel:.3g} of rms(ref)"
+
+
+def _run(torch, ls, w4a8=True):
+    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer
+    wl = ls.wl
+    d = DeviceLayerSet.from_host(ls)
+    b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
+    run_layer(d, b, w4a8=w4a8)
+    torch.cuda.synchronize()
+    return dict(y=b.y.cpu().numpy(), ids=b.ids.cpu().numpy(), w=b.weights.cpu().numpy(),
+                logits=b.logits.cpu().numpy(), hdr=b.header(), num_active=int(b.num_active.item()))
+
+
+def _check_full(torch, ls, what):
+    wl = ls.wl
+    say(f"w4a8 layer {what}: M={wl.M} H={wl.H} I={wl.I} E={wl.E} k={wl.k} shared={wl.shared} {wl.routing}")
+    g = _run(torch, ls)
+    r = oracle.moe_layer_w4a8(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s,
+                              wl.k, wl.shared)
+    xf = oracle.bf16_bits_to_f64(ls.x_bits)
+    bound = logit_error_bound(xf, ls.w_router, ls.bias, wl.H, wl.M)
+    amb = check_routing(g["ids"], g["w"], g["logits"], r["logits"], bound, wl.k, what)
+    keep = np.setdiff1d(np.arange(wl.M), amb)
+    rms = float(np.sqrt(np.mean(r["y"] ** 2)))
+    allow = flip_allowance(ls, r["ids"][keep], r["weights"][keep], r["xq"][keep])
+    assert_w4a8_close(g["y"][keep], r["y"][keep], rms, allow, what)
+    if not amb:
+        assert g["num_active"] == r["num_active"]
+        assert_paths(g["hdr"], wl, r["ids"], what)
+    assert len(amb) <= max(1, wl.M // 50), f"{what}: {len(amb)} ambiguous tokens"
+    return g, r
+
+
+def test_tiny_config_every_element():
+    torch = need_gpu()
+    _check_full(torch, synth.layer_set("tiny"), "tiny")
+
+
+@pytest.mark.parametrize("M,H,I,E,k,shared,routing", [
+    (7, 96, 64, 5, 3, True, "plain"),        # ragged lanes, GEMV only
+    (3, 2592, 800, 9, 2, True, "plain"),     # K tails: the long down kernel
+    (1, 32, 32, 1, 1, False, "plain"),       # smallest layer
+    (2, 64, 4096, 3, 1, True, "plain"),      # largest intermediate size
+    (2, 8192, 64, 3, 2, True, "plain"),      # largest hidden size
+    (40, 256, 128, 4, 2, True, "plain"),     # every expert on the scaled MFMA path (one term)
+    (130, 384, 256, 3, 2, True, "plain"),    # ragged 64-token MFMA tiles
+    (12, 256, 256, 6, 4, True, "plain"),     # few-token matrix cores
+    (24, 512, 512, 10, 3, True, "zipf"),     # GEMV, few-token and scaled-MFMA experts in one layer
+    (64, 128, 96, 16, 4, True, "zipf"),      # many tokens per expert, combine by rows
+])
+def test_edge_shapes_every_element(M, H, I, E, k, shared, routing):
+    torch = need_gpu()
+    wl = synth.custom(f"w4a8_edge{M}x{H}x{I}", M, H, I, E, k, shared, routing, seed=M + H + I + 1)
+    _check_full(torch, synth.layer_set(wl), wl.name)
+
+
+@pytest.mark.parametrize("name", ["ling_m1", "ling_m4_mtp"])
+def test_ling_decode_full_size(name):
+    torch = need_gpu()
+    _check_full(torch, synth.layer_set(name, 3), f"{name}/set3")
+
+
+@pytest.mark.parametrize("name,tokens", [("ling_m32_zipf", [0, 9, 31]),
+                                         ("ling_m512_prefill", [0, 200, 511])])
+def test_ling_batch_sampled_tokens(name, tokens):
+    torch = need_gpu()
+    ls = synth.layer_set(name, 1)
+    wl = ls.wl
+    say(f"w4a8 layer {name}: M={wl.M} sampled {tokens}")
+    g = _run(torch, ls)
+    r = oracle.moe_layer_w4a8_tokens(tokens, ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s,
+                                     ls.w2_q, ls.w2_s, wl.k, wl.shared)
+    xf = oracle.bf16_bits_to_f64(ls.x_bits[tokens])
+    b = ls.bias if ls.bias is None or ls.bias.ndim == 1 else ls.bias[tokens]
+    bound = logit_error_bound(xf, ls.w_router, b, wl.H, wl.M)
+    amb = check_routing(g["ids"][tokens], g["w"][tokens], g["logits"][tokens], r["logits"], bound,
+                        wl.k, name)
+    keep = [i for i in range(len(tokens)) if i not in amb]
+    rms = float(np.sqrt(np.mean(r["y"] ** 2)))
+    xq = oracle.mxfp8_fake_quant(xf)
+    allow = flip_allowance(ls, r["ids"][keep], r["weights"][keep], xq[keep])
+    assert_w4a8_close(g["y"][tokens][keep], r["y"][keep], rms, allow, name)
+    assert np.all(np.isfinite(g["y"]))
+    assert_paths(g["hdr"], wl, g["ids"], name)
+
+
+@pytest.mark.parametrize("name", ["ling_m4_mtp", "ling_m32_zipf"])
+def test_routing_is_the_bf16_layers(name):
+    """Same kernels, same bf16 x: the W4A8 call routes bit-identically to
+    moe_layer, and its output differs from moe_layer's only by the 8-bit
+    activations."""
+    torch = need_gpu()
+    ls = synth.layer_set(name, 2)
+    a = _run(torch, ls, w4a8=False)
+    b = _run(torch, ls, w4a8=True)
+    assert np.array_equal(a["logits"], b["logits"]) and np.array_equal(a["ids"], b["ids"])
+    assert np.array_equal(a["w"], b["w"])
+    rel = np.sqrt(np.mean((a["y"] - b["y"]) ** 2) / np.mean(a["y"] ** 2))
+    assert 1e-4 < rel < 0.1, rel
