@@ -13,6 +13,7 @@ and routing examples in ``tests/golden/``, brute force on tiny inputs,
 closed forms, exact power-of-two metamorphics).  No function here is
 "parity unpinned".
 """
+from .prefetch_oracle import expert_heat, prefetch_checksums, prefetch_priority, select_experts  # noqa: F401
 from .lmhead_oracle import E4M3_MAX, e4m3_decode, e4m3_round, lmhead_logits, lmhead_quantize  # noqa: F401
 from .w4a8_oracle import (  # noqa: F401
     bf16_round,
