@@ -24,11 +24,15 @@ Readings taken where the article is silent (each listed in the design doc):
     lower expert index; experts with heat 0 are not predicted.
   * The shared expert is used by every token, so when the bank has one it is
     always listed, first; the list holds at most max_experts entries.
-  * "Prefetch" reads every byte of the chosen arrays of each listed expert
-    (parts bit 0: the gate/up codes and scales, bit 1: the down codes and
-    scales).  Its observable result is one checksum per list entry: the sum,
-    modulo 2^32, of the little-endian 32-bit words read.  Entries whose id is
-    outside the bank, and entries at or past the live count, read nothing.
+  * "Prefetch" brings every 64-byte line of the chosen arrays of each listed
+    expert into the cache (parts bit 0: the gate/up codes and scales, bit 1:
+    the down codes and scales); one 32-bit word per line is enough to make the
+    memory system fetch the line, so that is what is read: the word at each
+    offset 0, 64, 128, ... below the array's per-expert size, offsets counted
+    from the start of that expert's part of the array.  The observable result
+    is one checksum per list entry: the sum, modulo 2^32, of those
+    little-endian words.  Entries whose id is outside the bank, and entries at
+    or past the live count, read nothing.
 """
 from __future__ import annotations
 
@@ -72,18 +76,23 @@ def select_experts(draft_ids, E: int, has_shared: bool, max_experts: int,
     return np.asarray(lst[:max(max_experts, 0)], dtype=np.int64)
 
 
-def _words_sum(a: np.ndarray) -> int:
-    """Sum of the little-endian 32-bit words of a byte array (len % 4 == 0)."""
+LINE_BYTES = 64
+
+
+def _line_words_sum(a: np.ndarray) -> int:
+    """Sum of the first little-endian 32-bit word of every 64-byte line of a
+    byte array (len % 4 == 0; a last, shorter line counts too)."""
     b = np.ascontiguousarray(a, dtype=np.uint8).ravel()
     assert b.size % 4 == 0
     w = b.view("<u4").astype(np.uint64)
-    return int(w.sum())
+    return int(w[::LINE_BYTES // 4].sum())
 
 
 def prefetch_checksums(w13_q, w13_s, w2_q, w2_s, expert_ids, num_live: int, parts: int) -> np.ndarray:
     """Checksum of each list entry (uint32 [len(expert_ids)]): for r < num_live
     with 0 <= expert_ids[r] < number of bank entries, the sum mod 2^32 of the
-    32-bit words of that expert's chosen arrays; 0 otherwise."""
+    first 32-bit word of every 64-byte line of that expert's chosen arrays;
+    0 otherwise."""
     ids = np.asarray(expert_ids, dtype=np.int64).ravel()
     out = np.zeros(ids.size, dtype=np.uint32)
     nbank = w13_q.shape[0]
@@ -94,6 +103,6 @@ def prefetch_checksums(w13_q, w13_s, w2_q, w2_s, expert_ids, num_live: int, part
             continue
         total = 0
         for arr in chosen:
-            total += _words_sum(arr[e])
+            total += _line_words_sum(arr[e])
         out[r] = total % (1 << 32)
     return out

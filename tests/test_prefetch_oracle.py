@@ -1,5 +1,5 @@
 """Pins of the expert prefetch oracle (CPU): hand-worked lists, priorities and
-checksums (tests/golden/prefetch_handworked.json), a byte-by-byte brute force
+line checksums (tests/golden/prefetch_handworked.json), a byte-by-byte brute force
 of the checksum, a pairwise-rank brute force of the selection, and the
 invariants the definition fixes (MoE-SpeQ article, 4.1 and 4.3)."""
 import json
@@ -51,19 +51,23 @@ def test_checksum_handworked(golden):
 
 
 def _brute_checksum(arrays, e):
-    """Byte loop: byte i of a region adds b * 256^(i mod 4)."""
+    """Byte loop: byte i of a region adds b * 256^(i mod 64) when i mod 64 < 4
+    (the first word of each 64-byte line)."""
     total = 0
     for a in arrays:
         flat = a[e].reshape(-1).tolist()
         for i, b in enumerate(flat):
-            total += int(b) << (8 * (i % 4))
+            if i % 64 < 4:
+                total += int(b) << (8 * (i % 64))
     return total % (1 << 32)
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_checksum_brute_force(seed):
+@pytest.mark.parametrize("seed,H,I", [(0, 64, 32), (1, 32, 32), (2, 96, 160)])
+def test_checksum_brute_force(seed, H, I):
+    """Random banks; (32, 32) and (96, 160) give down scales of 32 and 480
+    bytes per expert, whose last line is short."""
     rng = np.random.default_rng(seed)
-    E, H, I = 3, 64, 32
+    E = 3
     bank = (rng.integers(0, 256, (E + 1, 2 * I, H // 2), dtype=np.uint8),
             rng.integers(0, 256, (E + 1, 2 * I, H // 32), dtype=np.uint8),
             rng.integers(0, 256, (E + 1, H, I // 2), dtype=np.uint8),
