@@ -81,6 +81,55 @@ class HipEvents:
         self.hip.hipEventDestroy(ctypes.c_void_p(ev))
 
 
+class Prefetcher:
+    """Expert prefetch beside the layers: on a side stream forked from the
+    current one, moe_prefetch_select ranks a synthetic draft pass's routing of
+    each layer set of a window, and moe_prefetch_experts reads the listed
+    experts (gate/up and down); join() makes the current stream wait for it.  The
+    draft keeps each of the set's true routed experts with probability
+    `accuracy` (synth.draft_ids); the list holds the shared expert and every
+    drafted expert."""
+
+    def __init__(self, torch, binding, synth, wl, sets, weights, true_ids, accuracy, window, parts=3):
+        import numpy as np
+        self.torch, self.B, self.wl, self.weights = torch, binding, wl, weights
+        self.accuracy, self.window, self.parts = accuracy, window, parts
+        rng = np.random.default_rng(1000 + wl.seed)
+        drafts = [synth.draft_ids(t, wl.E, accuracy, rng) for t in true_ids]
+        self.hits = sum(len(set(d.ravel()) & set(t.ravel())) for d, t in zip(drafts, true_ids))
+        self.needed = sum(len(set(t.ravel())) for t in true_ids)
+        self.n_ids = wl.M * wl.k
+        self.max_n = self.n_ids + int(wl.shared)
+        self.drafts = [torch.tensor(d.reshape(-1), dtype=torch.int32, device="cuda") for d in drafts]
+        self.lst = torch.zeros(self.max_n, dtype=torch.int32, device="cuda")
+        self.num = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.cs = torch.zeros(self.max_n, dtype=torch.int32, device="cuda")
+        self.side = torch.cuda.Stream()
+        self.done = torch.cuda.Event()
+
+    def fork(self, set_ids):
+        """Prefetch the listed layer sets, in order, on the side stream."""
+        t = self.torch
+        self.side.wait_stream(t.cuda.current_stream())
+        s = self.side.cuda_stream
+        for set_idx in set_ids:
+            self.B.moe_prefetch_select(self.drafts[set_idx], self.n_ids, self.wl.E, int(self.wl.shared),
+                                       self.max_n, self.lst, self.num, s)
+            self.B.moe_prefetch_experts(self.weights[set_idx], self.lst, self.num, self.max_n, self.parts,
+                                        self.cs, s)
+        self.done.record(self.side)
+
+    def join(self):
+        self.torch.cuda.current_stream().wait_event(self.done)
+
+    def describe(self):
+        return {"accuracy": self.accuracy, "window": self.window,
+                "parts": {1: "gate/up", 2: "down", 3: "gate/up + down"}[self.parts],
+                "list": "shared + drafted experts by heat",
+                "predicted_fraction_of_needed_experts": round(self.hits / max(self.needed, 1), 4),
+                "when": "the W layers after the next W, read on a side stream while those run"}
+
+
 def device_sets(torch, wl, nsets):
     """x / router / bias from the seeded numpy generator; the expert banks are
     filled on the device with torch's seeded generator (same distribution:
@@ -330,6 +379,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w4a8", action="store_true",
                     help="the W4A8 variant (moe_layer_w4a8: MXFP8 activations into the experts)")
+    ap.add_argument("--prefetch", type=float, default=None, metavar="ACC",
+                    help="prefetch each next layer's predicted experts (moe_prefetch_select + "
+                         "moe_prefetch_experts on a side stream) while the current layer runs; the "
+                         "synthetic draft keeps each true expert with probability ACC")
+    ap.add_argument("--prefetch-window", type=int, default=4, metavar="W",
+                    help="with --prefetch: layers prefetched per fork of the side stream; the layers "
+                         "W..2W-1 ahead are read while the next W run")
     ap.add_argument("--three-calls", action="store_true",
                     help="time moe_route + moe_sort_by_expert + moe_mxfp4_forward instead of moe_layer")
     ap.add_argument("--copy-probe", action="store_true",
@@ -382,47 +438,68 @@ def main():
     weights = [d.weights() for d in sets]
 
     # one eager pass: loads the kernels and records each set's distinct-expert count
-    D, G = [], []
+    D, G, true_ids = [], [], []
     for d, w in zip(sets, weights):
         run_layer(d, buf, w, w4a8=args.w4a8)
         D.append(int(buf.num_active.item()))
         G.append(buf.header()["gemv_experts"])   # experts on the GEMV path (the timed kernel)
+        true_ids.append(buf.ids.cpu().numpy())
     log(f"[bench] distinct routed experts per set: min {min(D)} max {max(D)} mean {sum(D) / len(D):.2f}")
 
-    def capture(n):
+    pf = None
+    if args.prefetch is not None:
+        assert args.prefetch_window >= 1 and nsets % args.prefetch_window == 0, \
+            "the prefetch window must divide the number of layer sets"
+        pf = Prefetcher(torch, binding, synth, wl, sets, weights, true_ids, args.prefetch, args.prefetch_window)
+
+    def capture(n, prefetch):
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
+
+        def steps():
+            W = args.prefetch_window
+            for i in range(n):
+                if prefetch and i % W == 0:
+                    if i:
+                        pf.join()
+                    pf.fork([(i + W + j) % nsets for j in range(W)])
+                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls, w4a8=args.w4a8)
+            if prefetch:
+                pf.join()
+
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for i in range(n):
-                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls, w4a8=args.w4a8)
+            steps()
         torch.cuda.current_stream().wait_stream(s)
         with torch.cuda.graph(g):
-            for i in range(n):
-                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls, w4a8=args.w4a8)
+            steps()
         return g
 
-    g_full = capture(nsets)
-    rem = args.steps % nsets
-    g_rem = capture(rem) if rem else None
-    reps = args.steps // nsets
+    def timed_replays(prefetch):
+        g_full = capture(nsets, prefetch)
+        rem = args.steps % nsets
+        g_rem = capture(rem, prefetch) if rem else None
+        reps = args.steps // nsets
+        for _ in range(math.ceil(args.warmup / nsets)):
+            g_full.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        ev0.record()
+        for _ in range(reps):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1), time.perf_counter() - w0
 
-    for _ in range(math.ceil(args.warmup / nsets)):
-        g_full.replay()
-    torch.cuda.synchronize()
-
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    ev0.record()
-    for _ in range(reps):
-        g_full.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_total = ev0.elapsed_time(ev1)
+    plain_ms = None
+    if pf is not None:
+        plain_ms, _ = timed_replays(False)
+        log(f"[bench] without prefetch: {plain_ms / args.steps * 1e3:.2f} us/layer")
+    ms_total, wall = timed_replays(pf is not None)
     ms_per_step = ms_total / args.steps
     step_sets = [i % nsets for i in range(args.steps)]
     exp_b = [layer_bytes(wl, D[l])[0] for l in step_sets]
@@ -442,12 +519,20 @@ def main():
     stops = [hev.create() for _ in range(n_ev)]
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
+    W = args.prefetch_window
+    if pf is not None:           # the first window's experts, as the replays leave them
+        pf.fork([step_sets[j % len(step_sets)] for j in range(W)])
     for i in range(n_ev):
         d, w = sets[step_sets[i]], weights[step_sets[i]]
+        if pf is not None and i % W == 0:
+            pf.join()
+            pf.fork([(step_sets[i] + W + j) % nsets for j in range(W)])
         timed = binding.moe_layer_w4a8_timed if args.w4a8 else binding.moe_layer_timed
         timed(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits, buf.ids, buf.weights,
               buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y, buf.ws, buf.ws_bytes, starts[i], stops[i],
               stream)
+    if pf is not None:
+        pf.join()
     torch.cuda.synchronize()
     spans = [hev.elapsed_ms(starts[i], stops[i]) for i in range(n_ev)]
     for e in starts + stops:
@@ -487,6 +572,10 @@ def main():
                      "traffic": recorded_traffic(wl.name + ("_w4a8" if args.w4a8 else "")),
                      "us_per_launch": gu_ms * 1e3, "bytes_per_launch": gu_bytes},
     }
+    if pf is not None:
+        out["config"]["prefetch"] = pf.describe()
+        out["us_per_layer_without_prefetch"] = plain_ms / args.steps * 1e3
+        out["roofline"]["traffic"] = None     # counters were taken without the prefetch beside the layer
     if not args.no_cpu_baseline:
         del sets
         torch.cuda.empty_cache()

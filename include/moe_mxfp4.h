@@ -219,6 +219,56 @@ moe_status moe_layer_w4a8_timed(const uint16_t* x, const float* w_router, const 
 moe_status moe_mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols,
                                 float* out, void* stream);
 
+/* ------------------------------------------------------------ Expert prefetch
+ * Speculative decoding can tell ahead of a layer which experts it will use:
+ * the draft model's routing for the next tokens is counted into an expert
+ * heat map, and the predicted experts are fetched in priority order on a
+ * stream of their own before the verify pass needs them (MoE-SpeQ article,
+ * 4.1 and 4.3).  Here every layer's experts already reside in HBM, so a
+ * prefetch reads the predicted experts' weights into the GPU's memory-side
+ * last-level cache (the Infinity Cache), from which the layer's own reads are
+ * then served.  Results of the layer do not depend on whether, or what, was
+ * prefetched. */
+#define MOE_PREFETCH_MAX_DRAFT_IDS 1048575  /* n_ids of moe_prefetch_select      */
+#define MOE_PREFETCH_MAX_LIST 65535         /* max_ids of moe_prefetch_experts   */
+
+/* The prefetch list of one layer from the draft's routing.
+ *   draft_ids    device int32 [n_ids]: the routed expert ids the draft pass
+ *                produced for this layer (e.g. moe_route's topk_ids of the
+ *                draft tokens, flattened); ids outside [0, E) count for nothing
+ *   expert_ids   device int32 [max_experts], output: the shared expert (index E)
+ *                first when has_shared, then every expert with heat > 0 (heat =
+ *                how many draft ids equal it) by descending heat, ties to the
+ *                lower index, cut to max_experts entries; entries past the list
+ *                are set to -1.  (The article's priority 0.6 heat + 0.3 size +
+ *                0.1 transfer time orders a bank of equal-sized experts by heat.)
+ *   num_selected device int32 [1], output: the list's length
+ * Limits: 0 <= n_ids <= MOE_PREFETCH_MAX_DRAFT_IDS, 1 <= E <= MOE_MAX_EXPERTS,
+ * has_shared in {0, 1}, 0 <= max_experts <= MOE_PREFETCH_MAX_LIST; pointers
+ * 4-byte aligned.  One workgroup. */
+moe_status moe_prefetch_select(const int32_t* draft_ids, int32_t n_ids, int32_t E, int32_t has_shared,
+                               int32_t max_experts, int32_t* expert_ids, int32_t* num_selected, void* stream);
+
+/* Read the listed experts' weights (every byte of the chosen arrays) so that
+ * they are cache-resident when the layer runs.
+ *   w          host pointer to the expert bank descriptor (as moe_mxfp4_forward)
+ *   expert_ids device int32 [max_ids]: bank entries to read (0..E-1 routed, E the
+ *              shared expert when the bank has one); entries outside the bank
+ *              are skipped, a repeated entry is read again
+ *   num_live   device int32 [1] (e.g. moe_prefetch_select's num_selected): only
+ *              entries 0..min(*num_live, max_ids)-1 are read; NULL: all max_ids
+ *   parts      1: gate/up codes and scales, 2: down codes and scales, 3: both
+ *   checksums  device uint32 [max_ids]: entry r's sum, modulo 2^32, of the
+ *              little-endian 32-bit words read is added to checksums[r] (so
+ *              every load is used and the bytes read can be checked); skipped
+ *              entries add nothing.  The caller sets the initial values.
+ * Limits: the bank's sizes as moe_mxfp4_forward, its pointers 16-byte aligned;
+ * 0 <= max_ids <= MOE_PREFETCH_MAX_LIST (0 launches nothing); 1 <= parts <= 3;
+ * expert_ids, num_live and checksums 4-byte aligned.  Launched as one grid row
+ * of 64 KB workgroups per list entry; calls on other streams run beside it. */
+moe_status moe_prefetch_experts(const moe_mxfp4_weights* w, const int32_t* expert_ids, const int32_t* num_live,
+                                int32_t max_ids, int32_t parts, uint32_t* checksums, void* stream);
+
 /* ---------------------------------------------------------------- FP8 LM head
  * The LM head projects the hidden state onto the vocabulary (2,560 -> 157,184
  * for the Ling model: digest, section 2).  Its bf16 weights are quantised

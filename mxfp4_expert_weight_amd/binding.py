@@ -63,6 +63,8 @@ _SIGNATURES = {
                                             _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
     "moe_mxfp8_quantize": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
     "moe_mxfp4_dequantize": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
+    "moe_prefetch_select": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_prefetch_experts": (ctypes.c_int, [ctypes.POINTER(moe_mxfp4_weights), _P, _P, _I32, _I32, _P, _P]),
     "moe_lmhead_fp8_quantize": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P]),
     "moe_lmhead_fp8_logits": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, _P]),
 }
@@ -213,6 +215,16 @@ def moe_mxfp8_quantize(x, rows, K, codes, scales, values, stream=None):
 def moe_mxfp4_dequantize(q, s, rows, cols, out, stream=None):
     _check(lib().moe_mxfp4_dequantize(_ptr(q), _ptr(s), rows, cols, _ptr(out), _stream(stream)),
            "moe_mxfp4_dequantize")
+
+
+def moe_prefetch_select(draft_ids, n_ids, E, has_shared, max_experts, expert_ids, num_selected, stream=None):
+    _check(lib().moe_prefetch_select(_ptr(draft_ids), n_ids, E, int(has_shared), max_experts, _ptr(expert_ids),
+                                     _ptr(num_selected), _stream(stream)), "moe_prefetch_select")
+
+
+def moe_prefetch_experts(w: moe_mxfp4_weights, expert_ids, num_live, max_ids, parts, checksums, stream=None):
+    _check(lib().moe_prefetch_experts(ctypes.byref(w) if w is not None else None, _ptr(expert_ids), _ptr(num_live),
+                                      max_ids, parts, _ptr(checksums), _stream(stream)), "moe_prefetch_experts")
 
 
 def moe_lmhead_fp8_quantize(w_bf16, V, H, codes, scales, stream=None):

@@ -390,6 +390,51 @@ moe_status moe_mxfp4_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows
   return hip_status(launch_dequant(q, s, rows, cols, out, (hipStream_t)stream));
 }
 
+moe_status moe_prefetch_select(const int32_t* draft_ids, int32_t n_ids, int32_t E, int32_t has_shared,
+                               int32_t max_experts, int32_t* expert_ids, int32_t* num_selected, void* stream) {
+  if (!num_selected || (n_ids > 0 && !draft_ids) || (max_experts > 0 && !expert_ids)) return MOE_ERR_NULL;
+  if (n_ids < 0 || n_ids > kPrefetchMaxIds || E < 1 || E > MOE_MAX_EXPERTS || (has_shared != 0 && has_shared != 1) ||
+      max_experts < 0 || max_experts > kPrefetchMaxList)
+    return MOE_ERR_SHAPE;
+  if (((uintptr_t)draft_ids & 3u) || ((uintptr_t)expert_ids & 3u) || ((uintptr_t)num_selected & 3u))
+    return MOE_ERR_ALIGN;
+  return hip_status(launch_prefetch_select(draft_ids, n_ids, E, has_shared, max_experts, expert_ids, num_selected,
+                                           (hipStream_t)stream));
+}
+
+moe_status moe_prefetch_experts(const moe_mxfp4_weights* w, const int32_t* expert_ids, const int32_t* num_live,
+                                int32_t max_ids, int32_t parts, uint32_t* checksums, void* stream) {
+  if (!w || !w->w13_q || !w->w13_s || !w->w2_q || !w->w2_s) return MOE_ERR_NULL;
+  if (max_ids > 0 && (!expert_ids || !checksums)) return MOE_ERR_NULL;
+  if (w->num_experts < 1 || w->num_experts > MOE_MAX_EXPERTS || (w->has_shared != 0 && w->has_shared != 1))
+    return MOE_ERR_SHAPE;
+  if (check_hidden(w->hidden) != MOE_OK || check_inter(w->inter) != MOE_OK) return MOE_ERR_SHAPE;
+  if (max_ids < 0 || max_ids > kPrefetchMaxList || parts < 1 || parts > 3) return MOE_ERR_SHAPE;
+  if (!aligned16(w->w13_q) || !aligned16(w->w13_s) || !aligned16(w->w2_q) || !aligned16(w->w2_s) ||
+      ((uintptr_t)expert_ids & 3u) || ((uintptr_t)num_live & 3u) || ((uintptr_t)checksums & 3u))
+    return MOE_ERR_ALIGN;
+  if (max_ids == 0) return MOE_OK;
+  const int64_t H = w->hidden, I = w->inter;
+  // bytes per expert of each array (multiples of 32 for H, I % 32 == 0)
+  const int64_t n13q = 2 * I * (H / 2), n13s = 2 * I * (H / 32);
+  const int64_t n2q = H * (I / 2), n2s = H * (I / 32);
+  PrefetchArgs a{};
+  int q = 0;
+  auto add = [&](const uint8_t* p, int64_t n) {
+    a.base[q] = p;
+    a.bytes[q++] = n;
+  };
+  if (parts & 1) { add(w->w13_q, n13q); add(w->w13_s, n13s); }
+  if (parts & 2) { add(w->w2_q, n2q); add(w->w2_s, n2s); }
+  a.nreg = q;
+  a.nbank = w->num_experts + w->has_shared;
+  a.ids = expert_ids;
+  a.num_live = num_live;
+  a.max_ids = max_ids;
+  a.checksums = checksums;
+  return hip_status(launch_prefetch(a, (hipStream_t)stream));
+}
+
 moe_status moe_lmhead_fp8_quantize(const uint16_t* w_bf16, int32_t V, int32_t H, uint8_t* codes, float* scales,
                                    void* stream) {
   if (!w_bf16 || !codes || !scales) return MOE_ERR_NULL;

@@ -212,6 +212,28 @@ hipError_t launch_mxfp8_quantize(const uint16_t* src, int64_t rows, int K, uint8
 // of the h rows of one path's experts (path 0: GEMV, 1: few-token) in place.
 hipError_t launch_mxfp8_round_trip_rows(uint16_t* p, int64_t rows, int K, hipStream_t s);
 hipError_t launch_h_round_trip(const ForwardArgs& a, int path, hipStream_t s);
+// Expert prefetch (prefetch.hip).  The chosen arrays of one expert (gate/up
+// codes, gate/up scales, down codes, down scales: those whose part is
+// chosen) are its regions; region q of expert e is the bytes[q] bytes at
+// base[q] + e * bytes[q].  The launcher fills per_block and blk_end.
+struct PrefetchArgs {
+  const uint8_t* base[4];
+  int64_t bytes[4];         // bytes per expert (a multiple of 4)
+  int blk_end[4];           // cumulative blocks per list entry, by region
+  int per_block;            // 64-byte lines per block (a multiple of 1024)
+  int nreg;                 // regions in use (2 or 4)
+  int nbank;                // bank entries (E + shared)
+  const int* ids;           // [max_ids] list entries
+  const int* num_live;      // live entries (device), or null: all max_ids
+  int max_ids;
+  uint32_t* checksums;      // [max_ids], each entry's line-word sum is added
+};
+// Draft heat map -> prefetch list (one workgroup); keys need heat < 2^20.
+constexpr int kPrefetchMaxIds = MOE_PREFETCH_MAX_DRAFT_IDS;
+constexpr int kPrefetchMaxList = MOE_PREFETCH_MAX_LIST;    // list entries: one grid row each
+hipError_t launch_prefetch_select(const int* ids, int n_ids, int E, int has_shared, int max_n, int* out,
+                                  int* num_out, hipStream_t s);
+hipError_t launch_prefetch(PrefetchArgs a, hipStream_t s);
 // FP8 LM head (lmhead.hip).
 hipError_t launch_lmhead_quantize(const uint16_t* w, int V, int H, uint8_t* codes, float* scales, hipStream_t s);
 hipError_t launch_lmhead_fp8(const uint16_t* x, const uint8_t* codes, const float* scales, int M, int V, int H,

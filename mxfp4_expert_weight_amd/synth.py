@@ -205,3 +205,26 @@ def lmhead_set(M: int, V: int, H: int, seed: int) -> LmHeadSet:
     codes = np.where((codes & 0x7F) == 0x7F, codes ^ 0x01, codes).astype(np.uint8)   # no NaN codes
     scales = (2.0 ** rng.uniform(-13, -12, V)).astype(np.float32)
     return LmHeadSet(x, w, codes, scales)
+
+
+def draft_ids(true_ids: np.ndarray, E: int, accuracy: float, rng: np.random.Generator) -> np.ndarray:
+    """A synthetic draft pass's routing for a layer (int32 [T][k]), standing in
+    for the draft model of speculative decoding (MoE-SpeQ article, 4.1): each
+    (token, slot) keeps the layer's true expert with probability `accuracy`,
+    else takes a uniformly random expert outside that token's true set and not
+    yet in its draft set.  `true_ids` [T][k] are the layer's own routed ids."""
+    true_ids = np.asarray(true_ids).reshape(-1, np.asarray(true_ids).shape[-1])
+    out = np.empty_like(true_ids, dtype=np.int32)
+    for t, row in enumerate(true_ids):
+        taken = set(int(e) for e in row)
+        for s, e in enumerate(row):
+            if rng.random() < accuracy:
+                out[t, s] = e
+                continue
+            while True:
+                c = int(rng.integers(0, E))
+                if c not in taken:
+                    break
+            taken.add(c)
+            out[t, s] = c
+    return out

@@ -151,3 +151,30 @@ def test_mxfp8_quantize_host_checks(lib):
     assert _status(f, A, 4, 0, A, A, A, 0) == B.MOE_ERR_SHAPE
     assert _status(f, MIS, 4, 64, A, A, A, 0) == B.MOE_ERR_ALIGN
     assert _status(f, A, 4, 64, MIS, A, A, 0) == B.MOE_ERR_ALIGN
+
+
+def test_prefetch_host_checks(lib):
+    s = B.moe_prefetch_select
+    assert _status(s, None, 4, 512, 1, 9, A, A, 0) == B.MOE_ERR_NULL           # ids with n_ids > 0
+    assert _status(s, A, 4, 512, 1, 9, None, A, 0) == B.MOE_ERR_NULL
+    assert _status(s, A, 4, 512, 1, 9, A, None, 0) == B.MOE_ERR_NULL
+    assert _status(s, A, 1 << 20, 512, 1, 9, A, A, 0) == B.MOE_ERR_SHAPE      # n_ids > limit
+    assert _status(s, A, 4, 1025, 1, 9, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(s, A, 4, 512, 2, 9, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(s, A, 4, 512, 1, 65536, A, A, 0) == B.MOE_ERR_SHAPE        # list > limit
+    assert _status(s, A, 4, 512, 1, -1, A, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(s, A + 2, 4, 512, 1, 9, A, A, 0) == B.MOE_ERR_ALIGN
+    p = B.moe_prefetch_experts
+    w = B.make_weights(A, A, A, A, 512, 2560, 768, 1)
+    assert _status(p, None, A, A, 9, 3, A, 0) == B.MOE_ERR_NULL
+    assert _status(p, B.make_weights(A, A, None, A, 512, 2560, 768, 1), A, A, 9, 3, A, 0) == B.MOE_ERR_NULL
+    assert _status(p, w, None, A, 9, 3, A, 0) == B.MOE_ERR_NULL
+    assert _status(p, w, A, A, 9, 3, None, 0) == B.MOE_ERR_NULL
+    assert _status(p, w, A, A, 9, 0, A, 0) == B.MOE_ERR_SHAPE                # parts
+    assert _status(p, w, A, A, 9, 4, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(p, w, A, A, 65536, 3, A, 0) == B.MOE_ERR_SHAPE            # list > limit
+    assert _status(p, w, A, A, -1, 3, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(p, B.make_weights(A, A, A, A, 512, 2560, 770, 1), A, A, 9, 3, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(p, B.make_weights(A, A, A, A, 512, 2560, 768, 3), A, A, 9, 3, A, 0) == B.MOE_ERR_SHAPE
+    assert _status(p, B.make_weights(A, MIS, A, A, 512, 2560, 768, 1), A, A, 9, 3, A, 0) == B.MOE_ERR_ALIGN
+    assert _status(p, w, A + 2, A, 9, 3, A, 0) == B.MOE_ERR_ALIGN
