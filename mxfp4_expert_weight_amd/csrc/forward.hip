@@ -160,9 +160,12 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
   const int wave = threadIdx.x / kWave;
   const int jp0 = (blockIdx.x * GU_WPB + wave) * 2 * GU_NP;
   if constexpr (C > 0) {
-    // routed: rows 0 .. gridDim.y-2 loop over the slots (each workgroup routes
-    // once, however many slots it takes); the last row is the writer
+    // routed: rows 0 .. gridDim.y-3 loop over the slots (each workgroup routes
+    // once, however many slots it takes); with a shared expert, the row before
+    // last streams it without waiting for the routing (it needs none); the
+    // last row is the writer
     const bool writer = blockIdx.y == gridDim.y - 1;
+    const bool shared_row = a.has_shared && blockIdx.y == gridDim.y - 2;
     if (writer && blockIdx.x != 0) return;
     // short rows: every token's activations are staged in LDS for the GEMVs;
     // the loads are issued before the top-k, whose logits wait covers them
@@ -186,28 +189,51 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
         }
       }
     };
-    RouteState rs;
-    if (!route_prepare<C>(a, r, rs, writer, stage_x)) return;     // uniform over the block
     // this block's slots: blockIdx.y, + rows, + 2 rows, ...  Their records are
     // looked up first (one wave per slot) and parked in LDS, so no routing
-    // state stays live in registers through the GEMVs.
+    // state stays live in registers through the GEMVs.  The shared row parks
+    // the shared expert's record and skips the routing.
     __shared__ SlotRec s_rec[kRoutedMaxPairs + 1];
-    const int slots = max_slots(a.M, a.k, a.E) - 1 + a.has_shared;
-    const int rows = gridDim.y - 1;
-    const int mine = (slots - (int)blockIdx.y + rows - 1) / rows;
-    const int lane = threadIdx.x & (kWave - 1);
-    for (int i = wave; i < mine; i += GU_WPB) {
-      const int slot = blockIdx.y + i * rows;
-      const SlotRec rec = route_slot(a, rs, slot);
-      if (lane == 0) {
-        s_rec[i] = rec;
-        if (blockIdx.x == 0) r.rec[slot] = rec;
+    int mine = 1;
+    if (shared_row) {
+      if constexpr (SHORT) {
+#pragma unroll
+        for (int q = 0; q < kXPer; ++q) {
+          const int i = threadIdx.x + q * GU_WPB * kWave;
+          uint4 v = xs[q];
+          if constexpr (A8) mxfp8_round_trip8_quad(v);
+          if (i < nxv) s_x[i] = v;
+        }
+      }
+      if (threadIdx.x == 0) {
+        SlotRec rec;
+        rec.e = a.E; rec.n = a.M; rec.pbeg = -1; rec.hrow0 = a.M * a.k;
+        rec.pad[0] = rec.pad[1] = rec.pad[2] = rec.pad[3] = 0;
+#pragma unroll
+        for (int q = 0; q < kRecTokens; ++q) { rec.tok[q] = q < a.M ? q : 0; rec.w[q] = 1.f; }
+        s_rec[0] = rec;
+      }
+    } else {
+      RouteState rs;
+      if (!route_prepare<C>(a, r, rs, writer, stage_x)) return;     // uniform over the block
+      const int slots = max_slots(a.M, a.k, a.E) - 1 + a.has_shared;
+      const int rows = gridDim.y - 1 - a.has_shared;
+      mine = (slots - (int)blockIdx.y + rows - 1) / rows;
+      const int lane = threadIdx.x & (kWave - 1);
+      for (int i = wave; i < mine; i += GU_WPB) {
+        const int slot = blockIdx.y + i * rows;
+        const SlotRec rec = route_slot(a, rs, slot);
+        if (lane == 0) {
+          s_rec[i] = rec;
+          if (blockIdx.x == 0) r.rec[slot] = rec;
+        }
       }
     }
     __syncthreads();
     for (int i = 0; i < mine; ++i) {
       const SlotRec& rec = s_rec[i];
-      if (rec.e < 0) break;                              // later slots are empty too
+      // later slots are empty; the shared row streams the shared expert
+      if (rec.e < 0 || (rec.e == a.E && a.has_shared && !shared_row)) break;
       s.e = rec.e; s.n = rec.n; s.pbeg = rec.pbeg; s.hrow0 = rec.hrow0;
 #pragma unroll
       for (int q = 0; q < kRecTokens; ++q) { s.tok[q] = rec.tok[q]; s.w[q] = rec.w[q]; }
@@ -318,15 +344,18 @@ int device_cus() {
   return cus[dev];
 }
 
-// routed: the gate/up grid has one more row (the routing writer).
+// routed: the gate/up grid has one more row (the routing writer), and one more
+// for the shared expert when the bank has one.
 hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, const RouteOut& r,
                        bool routed, hipStream_t s, hipEvent_t start, hipEvent_t stop, hipEvent_t mid = nullptr) {
   const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
   const int gx = (a.I + GU_PAIRS_PER_BLOCK - 1) / GU_PAIRS_PER_BLOCK;
   int gy = slots;
-  if (routed) {   // as many rows of slots as stay resident with the writer row; blocks loop over the rest
-    const int fit = kGateupBlocksPerCu * device_cus() / gx - 1;
-    gy = (slots < fit ? slots : (fit > 1 ? fit : 1)) + 1;
+  if (routed) {   // as many rows of slots as stay resident with the shared and writer rows; blocks loop
+                  // over the rest
+    const int extra = 1 + (a.has_shared ? 1 : 0);
+    const int fit = kGateupBlocksPerCu * device_cus() / gx - extra;
+    gy = (slots < fit ? slots : (fit > 1 ? fit : 1)) + extra;
   }
   dim3 ggu(gx, gy);
   dim3 bgu(GU_WPB * kWave);
