@@ -67,6 +67,8 @@ def test_tiny_config_every_element(fused):
     (8, 64, 32, 600, 9, False, "plain"),     # 72 pairs: block sort; E > 512 top-k
     (2, 64, 32, 1024, 32, True, "plain"),    # largest E and k
     (4, 64, 32, 1024, 32, True, "plain"),    # 128 pairs routed inside the gate/up blocks
+    (4, 8192, 64, 16, 8, True, "plain"),     # decode: 17 slots of 128 down workgroups, long gate/up rows
+    (3, 4096, 128, 40, 8, True, "overlap"),  # decode: overlapping token sets, long gate/up rows
     (40, 256, 128, 4, 2, True, "plain"),     # matrix-core path: every expert has >= 16 tokens
     (130, 384, 256, 3, 2, True, "plain"),    # matrix-core path: ragged 64-token tiles
     (24, 256, 128, 12, 2, True, "zipf"),     # both paths in one layer

@@ -177,6 +177,7 @@ def test_tiny_config_every_element():
     (1, 32, 32, 1, 1, False, "plain"),       # smallest layer
     (2, 64, 4096, 3, 1, True, "plain"),      # largest intermediate size
     (2, 8192, 64, 3, 2, True, "plain"),      # largest hidden size
+    (4, 8192, 64, 16, 8, True, "plain"),     # decode: 17 slots of 128 down workgroups, long gate/up rows
     (40, 256, 128, 4, 2, True, "plain"),     # every expert on the scaled MFMA path (one term)
     (130, 384, 256, 3, 2, True, "plain"),    # ragged 64-token MFMA tiles
     (12, 256, 256, 6, 4, True, "plain"),     # few-token matrix cores
