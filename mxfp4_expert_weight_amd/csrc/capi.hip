@@ -51,6 +51,7 @@ ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
   a.hdr = reinterpret_cast<WorkspaceHeader*>(workspace);
   a.rec = reinterpret_cast<const SlotRec*>(ws + L.rec);
   a.h = reinterpret_cast<uint16_t*>(ws + L.h);
+  a.hlo = reinterpret_cast<uint16_t*>(ws + L.hlo);
   a.M = M; a.k = top_k; a.E = w->num_experts; a.H = w->hidden; a.I = w->inter;
   a.has_shared = w->has_shared;
   const bool mt = mt_path(M, a.H, a.I);

@@ -38,6 +38,22 @@ __device__ __forceinline__ float dot8_mxfp4_bf16(uint32_t codes, float scale, co
   return acc;
 }
 
+// The same against activations carried as two bf16 terms (v = hi + lo, ~16
+// significant bits): the codes are decoded once; both products are exact in
+// fp32 and go into the one accumulator.
+__device__ __forceinline__ float dot8_mxfp4_bf16_2t(uint32_t codes, float scale, const uint32_t hi[4],
+                                                    const uint32_t lo[4], float acc) {
+#define MOE_DOT2_2T(sel)                                                                           \
+  {                                                                                                \
+    const bf16x2 w = mxfp4_pair_bf16<sel>(codes, scale);                                           \
+    acc = __builtin_amdgcn_fdot2_f32_bf16(w, __builtin_bit_cast(bf16x2, hi[sel]), acc, false);    \
+    acc = __builtin_amdgcn_fdot2_f32_bf16(w, __builtin_bit_cast(bf16x2, lo[sel]), acc, false);    \
+  }
+  MOE_DOT2_2T(0) MOE_DOT2_2T(1) MOE_DOT2_2T(2) MOE_DOT2_2T(3)
+#undef MOE_DOT2_2T
+  return acc;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

@@ -275,7 +275,9 @@ __global__ __launch_bounds__(DN_WPB * kWave) void down_kernel(ForwardArgs a) {
   if (a.lists) {     // grid row y takes the y-th GEMV expert (rows past them exit)
     if ((int)blockIdx.y >= a.hdr->gemv_experts) return;
     resolve_slot(a.lists[blockIdx.y], a, s);
-  } else if (!resolve_slot(blockIdx.y, a, s)) {
+  } else if (!resolve_slot(gridDim.y - 1 - blockIdx.y, a, s)) {
+    // decode: slots in reverse, so the shared expert (every token, the most
+    // work; the last working slot) is dispatched before the routed ones
     return;
   }
   if (r0 >= a.H) return;

@@ -247,8 +247,13 @@ __device__ __forceinline__ void gateup_short(const ForwardArgs& a, const ExpertS
     for (int p = 0; p < NP; ++p) {
       const float g = group_sum<32>(accg[p]);
       const float u = group_sum<32>(accu[p]);
-      if (j32 == 0)
-        a.h[(size_t)hrow * I + jp0 + 2 * p + grp] = (uint16_t)f32_to_bf16_bits(silu(g) * u);
+      if (j32 == 0) {   // h = hi + lo, two bf16 terms (the down kernels read both)
+        const float v = silu(g) * u;
+        const uint32_t hi = f32_to_bf16_bits(v);
+        const size_t o = (size_t)hrow * I + jp0 + 2 * p + grp;
+        a.h[o] = (uint16_t)hi;
+        a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+      }
     }
   }
 }
@@ -301,8 +306,13 @@ __device__ __forceinline__ void gateup_long(const ForwardArgs& a, const ExpertSl
     for (int p = 0; p < NP; ++p) {
       const float g = group_sum<32>(accg[p]);
       const float u = group_sum<32>(accu[p]);
-      if (j32 == 0)
-        a.h[(size_t)hrow * I + jp0 + 2 * p + grp] = (uint16_t)f32_to_bf16_bits(silu(g) * u);
+      if (j32 == 0) {   // h = hi + lo, two bf16 terms (the down kernels read both)
+        const float v = silu(g) * u;
+        const uint32_t hi = f32_to_bf16_bits(v);
+        const size_t o = (size_t)hrow * I + jp0 + 2 * p + grp;
+        a.h[o] = (uint16_t)hi;
+        a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+      }
     }
   }
 }
@@ -329,11 +339,19 @@ __device__ __forceinline__ void down_short(const ForwardArgs& a, const ExpertSlo
 #pragma unroll
   for (int i = 0; i < HC; ++i) hcc[i] = min(j16 + 16 * i, KH - 1);
 
-  uint4 hv[HC][2];
+  // h = hi + lo (two bf16 terms); W4A8 layers carry their MXFP8 h in hi alone
+  const bool two = !a.act8;
+  uint4 hv[HC][2], hl[HC][2];
   {
     const uint4* hr = reinterpret_cast<const uint4*>(a.h + (size_t)s.hrow0 * I);
+    const uint4* lr = reinterpret_cast<const uint4*>(a.hlo + (size_t)s.hrow0 * I);
 #pragma unroll
     for (int i = 0; i < HC; ++i) { hv[i][0] = hr[2 * hcc[i]]; hv[i][1] = hr[2 * hcc[i] + 1]; }
+#pragma unroll
+    for (int i = 0; i < HC; ++i) {
+      hl[i][0] = two ? lr[2 * hcc[i]] : make_uint4(0, 0, 0, 0);
+      hl[i][1] = two ? lr[2 * hcc[i] + 1] : make_uint4(0, 0, 0, 0);
+    }
   }
   const int sbytes = nrows * row_s;
   const bool svec = (sbytes & 15) == 0 && sbytes <= 16 * kWave;
@@ -366,21 +384,29 @@ __device__ __forceinline__ void down_short(const ForwardArgs& a, const ExpertSlo
     token_of(a, s, m, t, wgt, hrow);
     if (m > 0) {
       const uint4* hr = reinterpret_cast<const uint4*>(a.h + (size_t)hrow * I);
+      const uint4* lr = reinterpret_cast<const uint4*>(a.hlo + (size_t)hrow * I);
 #pragma unroll
       for (int i = 0; i < HC; ++i) { hv[i][0] = hr[2 * hcc[i]]; hv[i][1] = hr[2 * hcc[i] + 1]; }
+#pragma unroll
+      for (int i = 0; i < HC; ++i) {
+        hl[i][0] = two ? lr[2 * hcc[i]] : make_uint4(0, 0, 0, 0);
+        hl[i][1] = two ? lr[2 * hcc[i] + 1] : make_uint4(0, 0, 0, 0);
+      }
     }
     float acc[NR];
 #pragma unroll
     for (int q = 0; q < NR; ++q) acc[q] = 0.f;
 #pragma unroll
     for (int i = 0; i < HC; ++i) {
-      uint32_t ha[8];
+      uint32_t ha[8], hb[8];
       unpack8(hv[i][0], ha);
       unpack8(hv[i][1], ha + 4);
+      unpack8(hl[i][0], hb);
+      unpack8(hl[i][1], hb + 4);
 #pragma unroll
       for (int q = 0; q < NR; ++q) {
-        acc[q] = dot8_mxfp4_bf16(c[q][i].x, sc[q][i], ha, acc[q]);
-        acc[q] = dot8_mxfp4_bf16(c[q][i].y, sc[q][i], ha + 4, acc[q]);
+        acc[q] = dot8_mxfp4_bf16_2t(c[q][i].x, sc[q][i], ha, hb, acc[q]);
+        acc[q] = dot8_mxfp4_bf16_2t(c[q][i].y, sc[q][i], ha + 4, hb + 4, acc[q]);
       }
     }
 #pragma unroll
@@ -413,6 +439,7 @@ __device__ __forceinline__ void down_long(const ForwardArgs& a, const ExpertSlot
     int t, hrow; float wgt;
     token_of(a, s, m, t, wgt, hrow);
     const uint4* hr = reinterpret_cast<const uint4*>(a.h + (size_t)hrow * I);
+    const uint4* lr = reinterpret_cast<const uint4*>(a.hlo + (size_t)hrow * I);
     float acc[NR];
 #pragma unroll
     for (int q = 0; q < NR; ++q) acc[q] = 0.f;
@@ -421,15 +448,16 @@ __device__ __forceinline__ void down_long(const ForwardArgs& a, const ExpertSlot
       for (int i = 0; i < HC; ++i) {
         const int hc = kb + j16 + 16 * i;
         if (hc < KH) {
-          uint32_t ha[8];
+          uint32_t ha[8], hb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
           act_from(hr, hc, ha);
+          if (!a.act8) act_from(lr, hc, hb);     // h = hi + lo; W4A8: hi alone
 #pragma unroll
           for (int q = 0; q < NR; ++q) {
             const int r = 4 * q + grp;
             const uint2 c2 = *reinterpret_cast<const uint2*>(wq + (size_t)(r0 + r) * row_q + hc * 8);
             const float scv = e8m0_to_f32(s_lds[r * row_s + (hc >> 1)]);
-            acc[q] = dot8_mxfp4_bf16(c2.x, scv, ha, acc[q]);
-            acc[q] = dot8_mxfp4_bf16(c2.y, scv, ha + 4, acc[q]);
+            acc[q] = dot8_mxfp4_bf16_2t(c2.x, scv, ha, hb, acc[q]);
+            acc[q] = dot8_mxfp4_bf16_2t(c2.y, scv, ha + 4, hb + 4, acc[q]);
           }
         }
       }

@@ -36,6 +36,7 @@ struct ForwardArgs {
   const int* num_active;      // [1]
   float* y;                   // [M][H]
   uint16_t* h;                // [M*k + M][I] bf16 (workspace)
+  uint16_t* hlo;              // [M*k + M][I] bf16 residual of the GEMV path's h (h = hi + lo)
   WorkspaceHeader* hdr;       // workspace header
   const SlotRec* rec;         // slot records, or null (then resolved from the sort outputs)
   int M, k, E, H, I, has_shared;
@@ -102,7 +103,7 @@ inline bool combine_rows(int M, int k, int H) {
   return M >= kCombineRowsMinTokens && ((size_t)M * k + M) * H * sizeof(float) <= kCombineRowsMaxBytes;
 }
 struct WorkspaceLayout {
-  size_t rec, h, xq_hi, xq_lo, xq_shi, xq_slo, hq_hi, hq_lo, hq_shi, hq_slo, items, yp, inv, lists, xdq, total;
+  size_t rec, h, hlo, xq_hi, xq_lo, xq_shi, xq_slo, hq_hi, hq_lo, hq_shi, hq_slo, items, yp, inv, lists, xdq, total;
 };
 inline WorkspaceLayout workspace_layout(int M, int k, int E, int H, int I) {
   WorkspaceLayout w{};
@@ -111,6 +112,7 @@ inline WorkspaceLayout workspace_layout(int M, int k, int E, int H, int I) {
   auto take = [&o](size_t bytes) { const size_t at = o; o += align_up(bytes, 256); return at; };
   w.rec = take((size_t)max_slots(M, k, E) * sizeof(SlotRec));
   w.h = take(pairs * I * sizeof(uint16_t));
+  w.hlo = take(pairs * I * sizeof(uint16_t));
   if (mfma_path(M, H, I)) {
     w.xq_hi = take((size_t)M * H);
     w.xq_lo = take((size_t)M * H);

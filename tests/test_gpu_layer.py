@@ -69,6 +69,8 @@ def test_tiny_config_every_element(fused):
     (4, 64, 32, 1024, 32, True, "plain"),    # 128 pairs routed inside the gate/up blocks
     (4, 8192, 64, 16, 8, True, "plain"),     # decode: 17 slots of 128 down workgroups, long gate/up rows
     (3, 4096, 128, 40, 8, True, "overlap"),  # decode: overlapping token sets, long gate/up rows
+    (3, 4096, 96, 40, 8, True, "overlap"),   # short down reduction: one bf16 h term would pass the bar
+    (3, 2560, 160, 40, 8, True, "overlap"),  # the same at the Ling hidden size (bf16 h: 1.06x the bar)
     (40, 256, 128, 4, 2, True, "plain"),     # matrix-core path: every expert has >= 16 tokens
     (130, 384, 256, 3, 2, True, "plain"),    # matrix-core path: ragged 64-token tiles
     (24, 256, 128, 12, 2, True, "zipf"),     # both paths in one layer
