@@ -160,22 +160,30 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
     wu = nu;
   }
   // lane (g, j): indices jw + 4g + r of token j
-  if (j < rec.n) {
-    uint32_t hb[4];
+  if (j < rec.n) {   // h = hi + lo, two bf16 terms
+    uint32_t hb[4], lb[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) hb[r] = f32_to_bf16_bits(silu(accg[r]) * accu[r]);
-    *reinterpret_cast<uint2*>(a.h + ((int64_t)rec.hrow0 + j) * I + jw + 4 * g) =
-        make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+    for (int r = 0; r < 4; ++r) {
+      const float v = silu(accg[r]) * accu[r];
+      hb[r] = f32_to_bf16_bits(v);
+      lb[r] = f32_to_bf16_bits(v - bf16_bits_to_f32(hb[r]));
+    }
+    const int64_t o = ((int64_t)rec.hrow0 + j) * I + jw + 4 * g;
+    *reinterpret_cast<uint2*>(a.h + o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+    *reinterpret_cast<uint2*>(a.hlo + o) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
   }
 }
 
 // ---------------------------------------------------------------- down --
 // Workgroup (128 output rows, slot): wave w takes rows r0 + 32w .. + 31 as two
 // 16-row tiles over the expert's tokens; y[t][r] += w_t * (h_t . Wd[r]).
+// h = hi + lo (two bf16 terms, each staged and multiplied); W4A8 layers carry
+// their MXFP8 h in hi alone.
 __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a) {
   SlotRec rec;
   if (!mt_slot(a, blockIdx.y, rec)) return;
-  __shared__ MtStage st;
+  __shared__ MtStage st, stl;
+  const bool two = !a.act8;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int g = lane >> 4, j = lane & 15;
   const int rw = blockIdx.x * MT_DN_R + 32 * wave;
@@ -188,10 +196,13 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
   const int srow = threadIdx.x >> 4, part = threadIdx.x & 15;
   const bool sv = srow < rec.n;
   const uint16_t* hsrc = a.h + ((int64_t)rec.hrow0 + (sv ? srow : 0)) * I;
+  const uint16_t* lsrc = a.hlo + ((int64_t)rec.hrow0 + (sv ? srow : 0)) * I;
   const int nk = I / MT_KC;
-  uint4 x0, x1;
+  uint4 x0, x1, l0, l1;
   mt_stage_load(x0, x1, hsrc, sv, 0, part);
+  mt_stage_load(l0, l1, lsrc, sv && two, 0, part);
   mt_stage_store(st.rows[0], srow, part, x0, x1);
+  mt_stage_store(stl.rows[0], srow, part, l0, l1);
   MtRowChunk w0 = mt_load_row(q0, s0, 0, g), w1 = mt_load_row(q1, s1, 0, g);
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
@@ -201,16 +212,24 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
     MtRowChunk n0 = w0, n1 = w1;
     if (more) {
       mt_stage_load(x0, x1, hsrc, sv, kc + 1, part);
+      mt_stage_load(l0, l1, lsrc, sv && two, kc + 1, part);
       n0 = mt_load_row(q0, s0, kc + 1, g);
       n1 = mt_load_row(q1, s1, kc + 1, g);
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const v8bf b = mt_frag_b(st.rows[cur], s, g, j);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(w0, s), b, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(w1, s), b, acc1, 0, 0, 0);
+      const v8bf bl = mt_frag_b(stl.rows[cur], s, g, j);
+      const v8bf a0 = mt_frag_a(w0, s), a1 = mt_frag_a(w1, s);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc1, 0, 0, 0);
     }
-    if (more) mt_stage_store(st.rows[cur ^ 1], srow, part, x0, x1);
+    if (more) {
+      mt_stage_store(st.rows[cur ^ 1], srow, part, x0, x1);
+      mt_stage_store(stl.rows[cur ^ 1], srow, part, l0, l1);
+    }
     block_barrier_lds();
     w0 = n0;
     w1 = n1;

@@ -76,6 +76,7 @@ def test_tiny_config_every_element(fused):
     (24, 256, 128, 12, 2, True, "zipf"),     # both paths in one layer
     (6, 256, 256, 3, 2, False, "plain"),     # few-token matrix cores after the fused top-k + sort
     (12, 256, 256, 6, 4, True, "plain"),     # few-token matrix cores, shared expert included
+    (12, 8192, 256, 8, 4, True, "plain"),    # few-token matrix cores, long rows (bf16 h: 1.26x the bar)
     (24, 512, 512, 10, 3, True, "zipf"),     # GEMV, few-token and scaled-MFMA experts in one layer
 ])
 def test_edge_shapes_every_element(M, H, I, E, k, shared, routing):
