@@ -12,7 +12,7 @@ What it computes, and where it is stated:
     built, halving the bytes each decode step reads (digest, section 4; the
     Vietnamese rewrite, section 2).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   FP8 is OCP E4M3 (the "FN" variant: bias 7, no infinities, 0x7F/0xFF are
   NaN, largest finite 448); one fp32 scale per vocabulary row,
   s = amax(row) / 448 computed in fp32 (s = 1 for an all-zero row); a code is

@@ -27,7 +27,7 @@ What the layer computes, and where it is stated:
     shared expert is added with weight 1.  (The pages do not spell out the
     expert MLP; this is the plainest reading for a gate/up/down expert.)
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   element 2j of a code byte is its low nibble; scale blocks run along K of a
   row-major [N][K] weight; gate rows are stacked before up rows in w13;
   top-k is chosen on logits (softmax is monotone) with ties to the lower

@@ -15,7 +15,7 @@ What it computes, and where it is stated (MoE-SpeQ article):
   * 1.1 / 1.2: prefetching hides the cost of bringing the predicted experts
     to where the computation reads them.
 
-Readings taken where the article is silent (each listed in the design doc):
+Readings taken where the article is silent:
   * heat[e] is the number of (draft token, slot) pairs whose routed id is e;
     ids outside [0, E) count for nothing.
   * size and transfer time enter the priority divided by the bank's largest;

@@ -10,7 +10,7 @@ What it computes, and where it is stated:
     moe_oracle (router, top-k, renormalised softmax, SwiGLU experts, shared
     expert, weighted combine).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * The 8-bit activations are MXFP8 in the OCP microscaling sense: blocks of
     32 consecutive elements along the reduction axis share one E8M0 scale
     X = 2^(floor(log2 amax) - 8), where 8 is the exponent of E4M3's largest
