@@ -181,3 +181,65 @@ def test_select_then_prefetch_then_layer():
                              wl.k, wl.shared)
         assert np.array_equal(ids_plain, r["ids"])
         assert_layer_close(b.y.cpu().numpy(), r["y"], what=f"{name} after prefetch")
+
+
+def test_prefetch_in_graph_replays():
+    """Select + prefetch on a side stream, captured with the layer into one HIP
+    graph (fork and join by events, as the bench runs them): each replay adds
+    the oracle's checksums once more and leaves the layer output the oracle's.
+    Eager work (refilling y) runs between the replays."""
+    torch = need_gpu()
+    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer
+    ls = synth.layer_set("tiny")
+    wl = ls.wl
+    say("prefetch captured in a graph with the tiny layer")
+    d = DeviceLayerSet.from_host(ls)
+    b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
+    run_layer(d, b)
+    torch.cuda.synchronize()
+    draft = synth.draft_ids(b.ids.cpu().numpy(), wl.E, 0.5, np.random.default_rng(9))
+    max_n = wl.M * wl.k + 1
+    lst = torch.zeros(max_n, dtype=torch.int32, device="cuda")
+    num = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cs = torch.zeros(max_n, dtype=torch.int32, device="cuda")
+    d_draft = _i32(torch, draft)
+    w = d.weights()
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+
+    def step():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            B.moe_prefetch_select(d_draft, draft.size, wl.E, 1, max_n, lst, num)
+            B.moe_prefetch_experts(w, lst, num, max_n, 3, cs)
+        done.record(side)
+        cur.wait_event(done)
+        run_layer(d, b)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    cs.zero_()
+    torch.cuda.synchronize()
+    want_list = oracle.select_experts(draft, wl.E, True, max_n)
+    want_cs = oracle.prefetch_checksums(ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s, want_list, want_list.size, 3)
+    r = oracle.moe_layer(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s, wl.k, wl.shared)
+    n = want_list.size
+    for rep in range(1, 4):
+        b.y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(num.item()) == n
+        assert lst.cpu().numpy()[:n].tolist() == want_list.tolist()
+        got = cs.cpu().numpy().view(np.uint32)[:n].astype(np.uint64)
+        assert got.tolist() == ((want_cs.astype(np.uint64) * rep) % (1 << 32)).tolist(), rep
+        assert_layer_close(b.y.cpu().numpy(), r["y"], what=f"graph replay {rep}")
