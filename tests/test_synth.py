@@ -98,3 +98,23 @@ def test_m512_has_mfma_sized_experts():
 def test_set_index_checked():
     with pytest.raises(ValueError):
         synth.layer_set("tiny", 1)
+
+
+def test_draft_ids():
+    """The synthetic draft routing: accuracy 1 keeps every true expert,
+    accuracy 0 keeps none, and a token's drafted experts are distinct."""
+    rng = np.random.default_rng(0)
+    true = np.stack([rng.choice(512, size=8, replace=False) for _ in range(4)]).astype(np.int32)
+    assert np.array_equal(synth.draft_ids(true, 512, 1.0, np.random.default_rng(1)), true)
+    d0 = synth.draft_ids(true, 512, 0.0, np.random.default_rng(2))
+    for t in range(4):
+        assert len(set(d0[t])) == 8
+        assert not set(d0[t]) & set(true[t])
+        assert d0[t].min() >= 0 and d0[t].max() < 512
+    # about half kept at accuracy 0.5 (4,000 slots: 5 sigma is 160)
+    big = np.stack([rng.choice(512, size=8, replace=False) for _ in range(500)]).astype(np.int32)
+    dh = synth.draft_ids(big, 512, 0.5, np.random.default_rng(3))
+    kept = int((dh == big).sum())
+    assert abs(kept - 2000) < 160
+    for t in range(500):
+        assert len(set(dh[t])) == 8
