@@ -252,7 +252,7 @@ __device__ __forceinline__ void gateup_short(const ForwardArgs& a, const ExpertS
         const uint32_t hi = f32_to_bf16_bits(v);
         const size_t o = (size_t)hrow * I + jp0 + 2 * p + grp;
         a.h[o] = (uint16_t)hi;
-        a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+        if (!a.act8) a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));   // W4A8: hi alone
       }
     }
   }
@@ -311,7 +311,7 @@ __device__ __forceinline__ void gateup_long(const ForwardArgs& a, const ExpertSl
         const uint32_t hi = f32_to_bf16_bits(v);
         const size_t o = (size_t)hrow * I + jp0 + 2 * p + grp;
         a.h[o] = (uint16_t)hi;
-        a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+        if (!a.act8) a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));   // W4A8: hi alone
       }
     }
   }

@@ -170,7 +170,8 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
     }
     const int64_t o = ((int64_t)rec.hrow0 + j) * I + jw + 4 * g;
     *reinterpret_cast<uint2*>(a.h + o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-    *reinterpret_cast<uint2*>(a.hlo + o) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+    if (!a.act8)   // W4A8 layers carry their MXFP8 h in hi alone
+      *reinterpret_cast<uint2*>(a.hlo + o) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
   }
 }
 
@@ -198,11 +199,11 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
   const uint16_t* hsrc = a.h + ((int64_t)rec.hrow0 + (sv ? srow : 0)) * I;
   const uint16_t* lsrc = a.hlo + ((int64_t)rec.hrow0 + (sv ? srow : 0)) * I;
   const int nk = I / MT_KC;
-  uint4 x0, x1, l0, l1;
+  uint4 x0, x1, l0 = make_uint4(0, 0, 0, 0), l1 = l0;
   mt_stage_load(x0, x1, hsrc, sv, 0, part);
-  mt_stage_load(l0, l1, lsrc, sv && two, 0, part);
+  if (two) mt_stage_load(l0, l1, lsrc, sv, 0, part);
   mt_stage_store(st.rows[0], srow, part, x0, x1);
-  mt_stage_store(stl.rows[0], srow, part, l0, l1);
+  if (two) mt_stage_store(stl.rows[0], srow, part, l0, l1);
   MtRowChunk w0 = mt_load_row(q0, s0, 0, g), w1 = mt_load_row(q1, s1, 0, g);
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
@@ -212,23 +213,32 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
     MtRowChunk n0 = w0, n1 = w1;
     if (more) {
       mt_stage_load(x0, x1, hsrc, sv, kc + 1, part);
-      mt_stage_load(l0, l1, lsrc, sv && two, kc + 1, part);
+      if (two) mt_stage_load(l0, l1, lsrc, sv, kc + 1, part);
       n0 = mt_load_row(q0, s0, kc + 1, g);
       n1 = mt_load_row(q1, s1, kc + 1, g);
     }
+    if (two) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const v8bf b = mt_frag_b(st.rows[cur], s, g, j);
-      const v8bf bl = mt_frag_b(stl.rows[cur], s, g, j);
-      const v8bf a0 = mt_frag_a(w0, s), a1 = mt_frag_a(w1, s);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc1, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc1, 0, 0, 0);
+      for (int s = 0; s < 8; ++s) {
+        const v8bf b = mt_frag_b(st.rows[cur], s, g, j);
+        const v8bf bl = mt_frag_b(stl.rows[cur], s, g, j);
+        const v8bf a0 = mt_frag_a(w0, s), a1 = mt_frag_a(w1, s);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc1, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const v8bf b = mt_frag_b(st.rows[cur], s, g, j);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(w0, s), b, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(w1, s), b, acc1, 0, 0, 0);
+      }
     }
     if (more) {
       mt_stage_store(st.rows[cur ^ 1], srow, part, x0, x1);
-      mt_stage_store(stl.rows[cur ^ 1], srow, part, l0, l1);
+      if (two) mt_stage_store(stl.rows[cur ^ 1], srow, part, l0, l1);
     }
     block_barrier_lds();
     w0 = n0;
