@@ -132,6 +132,9 @@ moe_status moe_sort_by_expert(const int32_t* topk_ids, int32_t M, int32_t top_k,
  * p = t*k + s, h = SiLU(x_t Wg_e^T) * (x_t Wu_e^T) and
  *   y_t = sum_s topk_weights[t][s] * (h Wd_e^T) + (shared expert of x_t, weight 1).
  * Reads the sort outputs on the device (num_active is never copied to the host).
+ * Arithmetic: MXFP4 weights decode exactly; products accumulate in fp32; h is
+ * carried between the projections as two terms (bf16 hi + lo, or two MXFP8
+ * terms for experts with >= 16 tokens), about 16 significant bits.
  *   x                      device bf16 [M][H], 16-byte aligned
  *   w                      host pointer to the expert bank descriptor
  *   topk_weights           device fp32 [M][k]

@@ -3,7 +3,8 @@
 // (and the shared expert) exit at once -- the grid is sized for the worst case
 // because the number of active experts is only known on the device.
 //
-//   gateup_kernel:  h[p][j] = SiLU(x_t . Wg[j]) * (x_t . Wu[j])   (bf16 h)
+//   gateup_kernel:  h[p][j] = SiLU(x_t . Wg[j]) * (x_t . Wu[j])   (h = hi + lo,
+//                   two bf16 terms)
 //   down_kernel:    y[t][r] += w_p * (h[p] . Wd[r])               (fp32 atomics;
 //                   gateup_kernel zeroes y first)
 #include "gemv_dev.h"
