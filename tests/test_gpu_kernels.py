@@ -130,6 +130,9 @@ def test_sort_by_expert_exact(M, k, E, dist):
 @pytest.mark.parametrize("M,H,E,k,bias", [
     (1, 2560, 512, 8, None),        # one wave per expert row, one token
     (4, 2560, 512, 8, "rows"),      # up to 4 tokens per pass, per-token bias
+    (3, 96, 77, 5, "experts"),      # odd E (the last workgroup's second wave has no row), short rows
+    (1, 2592, 33, 4, None),         # rows past 2560: the long-row variant
+    (2, 32, 1, 1, None),            # one expert, one vector per row
     (15, 224, 77, 3, None),         # ragged E
     (63, 2560, 512, 8, "experts"),  # largest batch of the wave kernel
     (64, 2560, 512, 8, "experts"),  # smallest batch of the tiled GEMM, 16-expert tiles
