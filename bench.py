@@ -565,6 +565,10 @@ def main():
         "us_per_layer": ms_per_step * 1e3,
         "layer_bytes": sum(lay_b) / len(lay_b),
         "layer_frac_of_hbm_peak": layer_gbs / HBM_PEAK_GBS,
+        # the routed and shared experts' MXFP4 bytes over the whole layer time
+        "expert_bytes_per_layer": sum(exp_b) / len(exp_b),
+        "expert_gbs": sum(exp_b) / (ms_total * 1e-3) / 1e9,
+        "expert_frac_of_hbm_peak": sum(exp_b) / (ms_total * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "mean_distinct_experts": sum(D[l] for l in step_sets) / len(step_sets),
         "roofline": {"bound": "hbm", "kernel": "gateup_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
