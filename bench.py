@@ -386,6 +386,10 @@ def main():
     ap.add_argument("--prefetch-window", type=int, default=4, metavar="W",
                     help="with --prefetch: layers prefetched per fork of the side stream; the layers "
                          "W..2W-1 ahead are read while the next W run")
+    ap.add_argument("--gap-kernels", type=int, default=0, metavar="N",
+                    help="before each layer, N small elementwise kernels on a 256 KB tensor that stays in "
+                         "L2: a stand-in for the non-MoE work between two layers that leaves HBM idle "
+                         "(with --prefetch, each layer's own experts are prefetched during it)")
     ap.add_argument("--three-calls", action="store_true",
                     help="time moe_route + moe_sort_by_expert + moe_mxfp4_forward instead of moe_layer")
     ap.add_argument("--copy-probe", action="store_true",
@@ -452,19 +456,36 @@ def main():
             "the prefetch window must divide the number of layer sets"
         pf = Prefetcher(torch, binding, synth, wl, sets, weights, true_ids, args.prefetch, args.prefetch_window)
 
-    def capture(n, prefetch):
+    gap = torch.zeros(1 << 16, device="cuda") if args.gap_kernels else None
+
+    def run_gap():
+        for _ in range(args.gap_kernels):
+            gap.add_(1.0)
+
+    def capture(n, prefetch, layers=True):
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
 
         def steps():
             W = args.prefetch_window
             for i in range(n):
+                if gap is not None:
+                    # the stand-in gap; with the prefetch, this layer's experts are read during it
+                    if prefetch:
+                        pf.fork([i % nsets])
+                    run_gap()
+                    if prefetch:
+                        pf.join()
+                    if layers:
+                        run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls,
+                                  w4a8=args.w4a8)
+                    continue
                 if prefetch and i % W == 0:
                     if i:
                         pf.join()
                     pf.fork([(i + W + j) % nsets for j in range(W)])
                 run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls, w4a8=args.w4a8)
-            if prefetch:
+            if prefetch and gap is None:
                 pf.join()
 
         s.wait_stream(torch.cuda.current_stream())
@@ -475,10 +496,10 @@ def main():
             steps()
         return g
 
-    def timed_replays(prefetch):
-        g_full = capture(nsets, prefetch)
+    def timed_replays(prefetch, layers=True):
+        g_full = capture(nsets, prefetch, layers)
         rem = args.steps % nsets
-        g_rem = capture(rem, prefetch) if rem else None
+        g_rem = capture(rem, prefetch, layers) if rem else None
         reps = args.steps // nsets
         for _ in range(math.ceil(args.warmup / nsets)):
             g_full.replay()
@@ -495,11 +516,19 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1), time.perf_counter() - w0
 
-    plain_ms = None
+    plain_ms = gap_ms = None
+    if gap is not None:
+        gap_ms, _ = timed_replays(False, layers=False)
+        log(f"[bench] the gap alone ({args.gap_kernels} kernels): {gap_ms / args.steps * 1e3:.2f} us per step")
     if pf is not None:
         plain_ms, _ = timed_replays(False)
-        log(f"[bench] without prefetch: {plain_ms / args.steps * 1e3:.2f} us/layer")
+        log(f"[bench] without prefetch: {plain_ms / args.steps * 1e3:.2f} us per step")
     ms_total, wall = timed_replays(pf is not None)
+    if gap is not None:                  # the layer's share of each step
+        log(f"[bench] gap + layer: {ms_total / args.steps * 1e3:.2f} us per step")
+        ms_total -= gap_ms
+        if plain_ms is not None:
+            plain_ms -= gap_ms
     ms_per_step = ms_total / args.steps
     step_sets = [i % nsets for i in range(args.steps)]
     exp_b = [layer_bytes(wl, D[l])[0] for l in step_sets]
@@ -520,18 +549,24 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
     W = args.prefetch_window
-    if pf is not None:           # the first window's experts, as the replays leave them
+    if pf is not None and gap is None:   # the first window's experts, as the replays leave them
         pf.fork([step_sets[j % len(step_sets)] for j in range(W)])
     for i in range(n_ev):
         d, w = sets[step_sets[i]], weights[step_sets[i]]
-        if pf is not None and i % W == 0:
+        if gap is not None:
+            if pf is not None:
+                pf.fork([step_sets[i]])
+            run_gap()
+            if pf is not None:
+                pf.join()
+        elif pf is not None and i % W == 0:
             pf.join()
             pf.fork([(step_sets[i] + W + j) % nsets for j in range(W)])
         timed = binding.moe_layer_w4a8_timed if args.w4a8 else binding.moe_layer_timed
         timed(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits, buf.ids, buf.weights,
               buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y, buf.ws, buf.ws_bytes, starts[i], stops[i],
               stream)
-    if pf is not None:
+    if pf is not None and gap is None:
         pf.join()
     torch.cuda.synchronize()
     spans = [hev.elapsed_ms(starts[i], stops[i]) for i in range(n_ev)]
@@ -576,8 +611,14 @@ def main():
                      "traffic": recorded_traffic(wl.name + ("_w4a8" if args.w4a8 else "")),
                      "us_per_launch": gu_ms * 1e3, "bytes_per_launch": gu_bytes},
     }
+    if gap is not None:
+        out["config"]["gap_kernels"] = args.gap_kernels
+        out["us_gap_per_step"] = gap_ms / args.steps * 1e3
     if pf is not None:
         out["config"]["prefetch"] = pf.describe()
+        if gap is not None:
+            out["config"]["prefetch"]["window"] = 1
+            out["config"]["prefetch"]["when"] = "during the gap before the layer, on a side stream"
         out["us_per_layer_without_prefetch"] = plain_ms / args.steps * 1e3
         out["roofline"]["traffic"] = None     # counters were taken without the prefetch beside the layer
     if not args.no_cpu_baseline:
