@@ -386,6 +386,9 @@ def main():
     ap.add_argument("--prefetch-window", type=int, default=4, metavar="W",
                     help="with --prefetch: layers prefetched per fork of the side stream; the layers "
                          "W..2W-1 ahead are read while the next W run")
+    ap.add_argument("--hint", type=float, default=None, metavar="ACC",
+                    help="moe_layer_hinted: each layer gets the experts a synthetic draft predicts (each true "
+                         "expert kept with probability ACC), sorted by moe_sort_by_expert before timing")
     ap.add_argument("--gap-kernels", type=int, default=0, metavar="N",
                     help="before each layer, N small elementwise kernels on a 256 KB tensor that stays in "
                          "L2: a stand-in for the non-MoE work between two layers that leaves HBM idle "
@@ -450,6 +453,36 @@ def main():
         true_ids.append(buf.ids.cpu().numpy())
     log(f"[bench] distinct routed experts per set: min {min(D)} max {max(D)} mean {sum(D) / len(D):.2f}")
 
+    hints = None
+    if args.hint is not None:             # the draft's predicted experts of every set, ascending, on the device
+        import numpy as np
+        rng = np.random.default_rng(2000 + wl.seed)
+        hints = []
+        offs = torch.empty(wl.E + 1, dtype=torch.int32, device="cuda")
+        prs = torch.empty(wl.M * wl.k, dtype=torch.int32, device="cuda")
+        hit = need = 0
+        for t in true_ids:
+            dr = synth.draft_ids(t, wl.E, args.hint, rng)
+            hit += len(set(dr.ravel()) & set(t.ravel()))
+            need += len(set(t.ravel()))
+            act = torch.full((wl.E,), -1, dtype=torch.int32, device="cuda")
+            num = torch.zeros(1, dtype=torch.int32, device="cuda")
+            binding.moe_sort_by_expert(torch.tensor(dr.reshape(-1), dtype=torch.int32, device="cuda"), wl.M, wl.k,
+                                       wl.E, offs, prs, act, num)
+            hints.append((act, num))
+        torch.cuda.synchronize()
+        hint_frac = hit / max(need, 1)
+
+    def run_step(i):
+        l = i % nsets
+        if hints is not None:
+            d = sets[l]
+            binding.moe_layer_hinted(d.x, d.w_router, d.bias, d.bias_row_stride, weights[l], d.M, d.k, buf.logits,
+                                     buf.ids, buf.weights, buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y,
+                                     buf.ws, buf.ws_bytes, hints[l][0], hints[l][1])
+        else:
+            run_layer(sets[l], buf, weights[l], fused=not args.three_calls, w4a8=args.w4a8)
+
     pf = None
     if args.prefetch is not None:
         assert args.prefetch_window >= 1 and nsets % args.prefetch_window == 0, \
@@ -477,14 +510,13 @@ def main():
                     if prefetch:
                         pf.join()
                     if layers:
-                        run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls,
-                                  w4a8=args.w4a8)
+                        run_step(i)
                     continue
                 if prefetch and i % W == 0:
                     if i:
                         pf.join()
                     pf.fork([(i + W + j) % nsets for j in range(W)])
-                run_layer(sets[i % nsets], buf, weights[i % nsets], fused=not args.three_calls, w4a8=args.w4a8)
+                run_step(i)
             if prefetch and gap is None:
                 pf.join()
 
@@ -562,10 +594,16 @@ def main():
         elif pf is not None and i % W == 0:
             pf.join()
             pf.fork([(step_sets[i] + W + j) % nsets for j in range(W)])
-        timed = binding.moe_layer_w4a8_timed if args.w4a8 else binding.moe_layer_timed
-        timed(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits, buf.ids, buf.weights,
-              buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y, buf.ws, buf.ws_bytes, starts[i], stops[i],
-              stream)
+        if hints is not None:
+            hs = hints[step_sets[i]]
+            binding.moe_layer_hinted(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits, buf.ids,
+                                     buf.weights, buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y, buf.ws,
+                                     buf.ws_bytes, hs[0], hs[1], starts[i], stops[i], stream)
+        else:
+            timed = binding.moe_layer_w4a8_timed if args.w4a8 else binding.moe_layer_timed
+            timed(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits, buf.ids, buf.weights,
+                  buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y, buf.ws, buf.ws_bytes, starts[i],
+                  stops[i], stream)
     if pf is not None and gap is None:
         pf.join()
     torch.cuda.synchronize()
@@ -611,6 +649,11 @@ def main():
                      "traffic": recorded_traffic(wl.name + ("_w4a8" if args.w4a8 else "")),
                      "us_per_launch": gu_ms * 1e3, "bytes_per_launch": gu_bytes},
     }
+    if hints is not None:
+        out["roofline"]["traffic"] = None     # counters were taken without hints (wrong hints fetch more)
+        out["config"]["entry"] = "moe_layer_hinted"
+        out["config"]["hint"] = {"accuracy": args.hint, "predicted_fraction_of_needed_experts": round(hint_frac, 4),
+                                 "list": "the draft's routed experts, ascending (moe_sort_by_expert)"}
     if gap is not None:
         out["config"]["gap_kernels"] = args.gap_kernels
         out["us_gap_per_step"] = gap_ms / args.steps * 1e3

@@ -176,6 +176,25 @@ moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float
                            void* workspace, size_t workspace_bytes, void* start_event, void* stop_event,
                            void* stream);
 
+/* moe_layer with a hint from a draft pass (speculative decoding predicts the
+ * experts of the coming tokens: MoE-SpeQ article, 4.1).  Same arguments,
+ * outputs and limits as moe_layer_timed (the events may be NULL), plus:
+ *   hint_experts device int32 [*num_hint]: the routed experts the draft
+ *                predicts for this layer, ascending (e.g. moe_sort_by_expert's
+ *                active_experts of the draft's ids); entries outside [0, E)
+ *                are ignored
+ *   num_hint     device int32 [1]: their count
+ * Both NULL: moe_layer_timed.  Only one NULL: MOE_ERR_NULL.  For M <= 4 the
+ * gate/up workgroups whose waves are idle during the routing read one word
+ * of every 64-byte line of their rows of hint_experts[slot], so a right guess
+ * finds the stream in L2; the results never depend on the hint. */
+moe_status moe_layer_hinted(const uint16_t* x, const float* w_router, const float* logit_bias,
+                            int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                            float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                            int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                            void* workspace, size_t workspace_bytes, const int32_t* hint_experts,
+                            const int32_t* num_hint, void* start_event, void* stop_event, void* stream);
+
 /* ------------------------------------------------------------------- W4A8
  * The baseline deployment of the Ling model runs the MXFP4 experts with 8-bit
  * activations, W4A8 (digest, section 2).  Here the 8-bit format is MXFP8 in

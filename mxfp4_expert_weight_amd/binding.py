@@ -57,6 +57,8 @@ _SIGNATURES = {
                                  _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_timed": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32,
                                        _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
+    "moe_layer_hinted": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32,
+                                        _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
     "moe_layer_w4a8": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P,
                                       _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_w4a8_timed": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32,
@@ -184,6 +186,18 @@ def moe_layer_timed(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weigh
                                  _ptr(sorted_pairs), _ptr(active_experts), _ptr(num_active), _ptr(y),
                                  _ptr(workspace), workspace_bytes, start_event, stop_event,
                                  _stream(stream)), "moe_layer_timed")
+
+
+def moe_layer_hinted(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weights, M, top_k, logits,
+                     topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
+                     workspace, workspace_bytes, hint_experts, num_hint, start_event=None, stop_event=None,
+                     stream=None):
+    _check(lib().moe_layer_hinted(_ptr(x), _ptr(w_router), _ptr(logit_bias), bias_row_stride,
+                                  ctypes.byref(w) if w is not None else None, M, top_k, _ptr(logits),
+                                  _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_offsets), _ptr(sorted_pairs),
+                                  _ptr(active_experts), _ptr(num_active), _ptr(y), _ptr(workspace),
+                                  workspace_bytes, _ptr(hint_experts), _ptr(num_hint), start_event, stop_event,
+                                  _stream(stream)), "moe_layer_hinted")
 
 
 def moe_layer_w4a8(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weights, M, top_k, logits,

@@ -180,7 +180,8 @@ moe_status layer_impl(const uint16_t* x, const float* w_router, const float* log
                            float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
                            int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                            void* workspace, size_t workspace_bytes_, void* start_event, void* stop_event,
-                           void* stream, bool act8) {
+                           void* stream, bool act8, const int32_t* hint = nullptr,
+                           const int32_t* num_hint = nullptr) {
   if (!x || !w_router || !w || !logits || !topk_ids || !topk_weights || !expert_offsets ||
       !sorted_pairs || !active_experts || !num_active || !y || !workspace)
     return MOE_ERR_NULL;
@@ -202,6 +203,8 @@ moe_status layer_impl(const uint16_t* x, const float* w_router, const float* log
     return MOE_ERR_HIP;
   ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
                              num_active, y, workspace, act8);
+  a.hint = hint;
+  a.num_hint = num_hint;
   if (act8) {
     if (M <= kRoutedMaxTokens && routed_stages_x(H)) {
       a.x = x;                       // the decode gate/up kernel rounds x to MXFP8 as it stages it
@@ -351,6 +354,19 @@ moe_status moe_layer_w4a8_timed(const uint16_t* x, const float* w_router, const 
   return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
                     expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
                     start_event, stop_event, stream, true);
+}
+
+moe_status moe_layer_hinted(const uint16_t* x, const float* w_router, const float* logit_bias,
+                            int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                            float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                            int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                            void* workspace, size_t workspace_bytes_, const int32_t* hint_experts,
+                            const int32_t* num_hint, void* start_event, void* stop_event, void* stream) {
+  if ((hint_experts == nullptr) != (num_hint == nullptr)) return MOE_ERR_NULL;
+  if (((uintptr_t)hint_experts & 3u) || ((uintptr_t)num_hint & 3u)) return MOE_ERR_ALIGN;
+  return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
+                    expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
+                    start_event, stop_event, stream, false, hint_experts, num_hint);
 }
 
 moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logit_bias,

@@ -25,6 +25,11 @@ constexpr int GU_SHORT_H = 32 * GU_HC * 16;         // longest row the single-pa
 constexpr int DN_SHORT_I = 16 * DN_HC * 16;         // (768)
 // Gate/up workgroups resident per CU (3 waves per SIMD, 4 waves a workgroup).
 constexpr int kGateupBlocksPerCu = 3;
+// Hinted line touches of a decode gate/up workgroup: its 2 * 16 rows of H/2
+// code bytes in 64-byte lines, kGuTouchLoads per lane of each idle wave
+// (three idle waves at M = 1 cover the 640 lines of H = 2560).
+constexpr int kGuLineBytes = 64;
+constexpr int kGuTouchLoads = 4;
 
 // Routing inside a gate/up block (decode batches, M <= kRoutedMaxTokens, so
 // at most 128 pairs: two per lane).  route_prepare: every workgroup takes the
@@ -180,6 +185,36 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
 #pragma unroll
       for (int q = 0; q < kXPer; ++q) xs[q] = x4[min((int)threadIdx.x + q * GU_WPB * kWave, nxv - 1)];
     }
+    // With a hint, the waves that take no part in the top-k (wave >= M) touch
+    // this workgroup's code lines of the hinted expert of its first slot (one
+    // word per 64-byte line), so the stream after the routing finds them in
+    // this XCD's L2.  The routing barrier is their only wait on these loads,
+    // and it waits for the top-k anyway.
+    uint32_t tw[kGuTouchLoads];
+    bool touch = false;
+    if constexpr (SHORT) {
+      const int row_q = a.H / 2;
+      const int lpr = row_q / kGuLineBytes;
+      const int jbase = blockIdx.x * GU_PAIRS_PER_BLOCK;
+      if (a.hint && !writer && !shared_row && wave >= a.M && row_q % kGuLineBytes == 0 && jbase < a.I) {
+        const int y = blockIdx.y;
+        const int eh = (y < *a.num_hint) ? a.hint[y] : -1;
+        if ((unsigned)eh < (unsigned)a.E) {
+          touch = true;
+          const uint8_t* base = a.w13_q + (size_t)eh * 2 * a.I * row_q;
+          const int nl = 2 * GU_PAIRS_PER_BLOCK * lpr;            // gate rows, then up rows
+          const int nlanes = (GU_WPB - a.M) * kWave;
+          const int l0 = (wave - a.M) * kWave + (threadIdx.x & (kWave - 1));
+#pragma unroll
+          for (int q = 0; q < kGuTouchLoads; ++q) {
+            const int l = min(q * nlanes + l0, nl - 1);
+            const int r = l / lpr, c = l - r * lpr;
+            const int row = (r < GU_PAIRS_PER_BLOCK) ? jbase + r : a.I + jbase + (r - GU_PAIRS_PER_BLOCK);
+            tw[q] = *reinterpret_cast<const uint32_t*>(base + (size_t)row * row_q + c * kGuLineBytes);
+          }
+        }
+      }
+    }
     auto stage_x = [&]() {
       if constexpr (SHORT) {
 #pragma unroll
@@ -244,6 +279,12 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
         else
           gateup_long<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
       }
+    }
+    if (touch) {
+      uint32_t t = 0u;
+#pragma unroll
+      for (int q = 0; q < kGuTouchLoads; ++q) t += tw[q];
+      if (t == 0x9E3779B9u && a.M < 0) a.y[0] = 0.f;   // never true (M >= 1): keeps the touches live
     }
     return;
   } else {

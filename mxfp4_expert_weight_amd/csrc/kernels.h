@@ -65,6 +65,11 @@ struct ForwardArgs {
   // carries x and h as one MXFP8 term (codes in xq_hi/hq_hi, scales in
   // xq_shi/hq_shi; the _lo terms are unused).
   int act8;
+  // Decode hint (moe_layer_hinted): the routed experts a draft pass predicts,
+  // ascending, hint[0 .. *num_hint); null: none.  Only read by the decode
+  // gate/up kernel, whose idle waves touch the hinted rows during the routing.
+  const int* hint;
+  const int* num_hint;
 };
 
 // The few-token matrix-core path (mt.hip): batches of more than

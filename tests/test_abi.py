@@ -178,3 +178,15 @@ def test_prefetch_host_checks(lib):
     assert _status(p, B.make_weights(A, A, A, A, 512, 2560, 768, 3), A, A, 9, 3, A, 0) == B.MOE_ERR_SHAPE
     assert _status(p, B.make_weights(A, MIS, A, A, 512, 2560, 768, 1), A, A, 9, 3, A, 0) == B.MOE_ERR_ALIGN
     assert _status(p, w, A + 2, A, 9, 3, A, 0) == B.MOE_ERR_ALIGN
+
+
+def test_hinted_layer_host_checks(lib):
+    w = B.make_weights(A, A, A, A, 512, 2560, 768, 1)
+    ws = B.moe_workspace_bytes(1, 8, 512, 2560, 768)
+    f = B.moe_layer_hinted
+    args = [A, A, None, 0, w, 1, 8, A, A, A, A, A, A, A, A, A, ws]
+    assert _status(f, *(args + [A, None])) == B.MOE_ERR_NULL          # hint without its count
+    assert _status(f, *(args + [None, A])) == B.MOE_ERR_NULL
+    assert _status(f, *(args + [A + 2, A])) == B.MOE_ERR_ALIGN
+    assert _status(f, *([None] + args[1:] + [A, A])) == B.MOE_ERR_NULL
+    assert _status(f, *(args[:5] + [0] + args[6:] + [A, A])) == B.MOE_ERR_SHAPE

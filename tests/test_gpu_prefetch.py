@@ -243,3 +243,44 @@ def test_prefetch_in_graph_replays():
         got = cs.cpu().numpy().view(np.uint32)[:n].astype(np.uint64)
         assert got.tolist() == ((want_cs.astype(np.uint64) * rep) % (1 << 32)).tolist(), rep
         assert_layer_close(b.y.cpu().numpy(), r["y"], what=f"graph replay {rep}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "ling_m1", "ling_m4_mtp"])
+def test_hinted_layer_equals_plain(name):
+    """moe_layer_hinted with right, half-right, invalid and empty hints gives
+    moe_layer's routing bit for bit and its output (fp32 atomics may reorder
+    the sum); the tiny and M = 1 layers also against the float64 oracle."""
+    torch = need_gpu()
+    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer
+    ls = synth.layer_set(name)
+    wl = ls.wl
+    d = DeviceLayerSet.from_host(ls)
+    b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
+    run_layer(d, b)
+    torch.cuda.synchronize()
+    ref = dict(ids=b.ids.cpu().numpy(), w=b.weights.cpu().numpy(), y=b.y.cpu().numpy().astype(np.float64))
+    true_active = np.unique(ref["ids"])
+    draft = synth.draft_ids(ref["ids"], wl.E, 0.5, np.random.default_rng(3))
+    cases = {
+        "right": true_active,
+        "half": np.unique(draft),
+        "invalid": np.array([-1] + true_active.tolist()[:-1] + [wl.E, 1 << 20]),
+        "empty": np.array([], dtype=np.int64),
+    }
+    rms = float(np.sqrt(np.mean(ref["y"] ** 2)))
+    for what, hint in cases.items():
+        say(f"moe_layer_hinted {name}: {what} hint {hint.tolist()[:10]}")
+        h = torch.tensor(np.concatenate([hint, [0]]).astype(np.int32), device="cuda")
+        nh = torch.tensor([hint.size], dtype=torch.int32, device="cuda")
+        b.y.fill_(float("nan"))
+        B.moe_layer_hinted(d.x, d.w_router, d.bias, d.bias_row_stride, d.weights(), d.M, d.k, b.logits, b.ids,
+                           b.weights, b.offsets, b.pairs, b.active, b.num_active, b.y, b.ws, b.ws_bytes, h, nh)
+        torch.cuda.synchronize()
+        assert np.array_equal(b.ids.cpu().numpy(), ref["ids"]), what
+        assert np.array_equal(b.weights.cpu().numpy(), ref["w"]), what
+        y = b.y.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(y - ref["y"]) <= 1e-5 * (np.abs(ref["y"]) + rms)), what
+    if wl.M == 1:
+        r = oracle.moe_layer(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s, wl.k, wl.shared)
+        assert np.array_equal(ref["ids"], r["ids"])
+        assert_layer_close(b.y.cpu().numpy(), r["y"], what=f"{name} hinted")
