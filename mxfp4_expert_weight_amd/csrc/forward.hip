@@ -151,7 +151,9 @@ __device__ __forceinline__ SlotRec route_slot(const ForwardArgs& a, const RouteS
 // C > 0: the block routes itself (C = experts per lane of the top-k).
 // A8 (W4A8 decode, short rows): x goes through the MXFP8 round trip as it is
 // staged (the four threads of a DPP quad hold one 32-element block).
-template <bool SHORT, int C, bool A8 = false>
+// HINT (moe_layer_hinted): idle waves touch the hinted expert's rows during the
+// routing; a separate instance, so the plain kernel carries none of it.
+template <bool SHORT, int C, bool A8 = false, bool HINT = false>
 __global__ __launch_bounds__(GU_WPB * kWave) __attribute__((amdgpu_waves_per_eu(1, 3)))
 void gateup_kernel(ForwardArgs a, RouteOut r) {
   if (C > 0 || !a.yp) {   // every block zeroes a share of y for the down kernel's scatter-add
@@ -192,7 +194,7 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
     // and it waits for the top-k anyway.
     uint32_t tw[kGuTouchLoads];
     bool touch = false;
-    if constexpr (SHORT) {
+    if constexpr (SHORT && HINT) {
       const int row_q = a.H / 2;
       const int lpr = row_q / kGuLineBytes;
       const int jbase = blockIdx.x * GU_PAIRS_PER_BLOCK;
@@ -280,7 +282,7 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
           gateup_long<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
       }
     }
-    if (touch) {
+    if (HINT && touch) {
       uint32_t t = 0u;
 #pragma unroll
       for (int q = 0; q < kGuTouchLoads; ++q) t += tw[q];
@@ -438,10 +440,15 @@ hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStr
   const bool short_h = a.H <= GU_SHORT_H;
   const bool a8x = a.act8 && short_h;                // x rounded while staged (else a.x is already MXFP8)
   void (*gu)(ForwardArgs, RouteOut);
+  const bool hint = a.hint != nullptr && short_h && !a.act8;
   if (topk_lane_experts(a.E) == 8)
-    gu = short_h ? (a8x ? gateup_kernel<true, 8, true> : gateup_kernel<true, 8>) : gateup_kernel<false, 8>;
+    gu = short_h ? (a8x ? gateup_kernel<true, 8, true>
+                        : (hint ? gateup_kernel<true, 8, false, true> : gateup_kernel<true, 8>))
+                 : gateup_kernel<false, 8>;
   else
-    gu = short_h ? (a8x ? gateup_kernel<true, 16, true> : gateup_kernel<true, 16>) : gateup_kernel<false, 16>;
+    gu = short_h ? (a8x ? gateup_kernel<true, 16, true>
+                        : (hint ? gateup_kernel<true, 16, false, true> : gateup_kernel<true, 16>))
+                 : gateup_kernel<false, 16>;
   return launch_pair(gu, a, r, true, s, start, stop);
 }
 
