@@ -245,14 +245,27 @@ def test_prefetch_in_graph_replays():
         assert_layer_close(b.y.cpu().numpy(), r["y"], what=f"graph replay {rep}")
 
 
-@pytest.mark.parametrize("name", ["tiny", "ling_m1", "ling_m4_mtp"])
+# Banks above 512 experts take the 16-experts-per-lane top-k and its own
+# hinting kernel: 1,024 experts with k = 8 at M = 1, and a ragged 600 at M = 3
+# (one idle wave per workgroup), without a shared expert.
+HINT_CUSTOM = {
+    "e1024_m1": (1, 256, 128, 1024, 8, True),
+    "e600_m3": (3, 512, 96, 600, 8, False),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny", "ling_m1", "ling_m4_mtp", *HINT_CUSTOM])
 def test_hinted_layer_equals_plain(name):
     """moe_layer_hinted with right, half-right, invalid and empty hints gives
     moe_layer's routing bit for bit and its output (fp32 atomics may reorder
-    the sum); the tiny and M = 1 layers also against the float64 oracle."""
+    the sum); the M = 1 layers also against the float64 oracle."""
     torch = need_gpu()
     from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer
-    ls = synth.layer_set(name)
+    if name in HINT_CUSTOM:
+        M, H, I, E, k, shared = HINT_CUSTOM[name]
+        ls = synth.layer_set(synth.custom(name, M, H, I, E, k, shared, "plain", seed=M + E))
+    else:
+        ls = synth.layer_set(name)
     wl = ls.wl
     d = DeviceLayerSet.from_host(ls)
     b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
