@@ -19,8 +19,8 @@ Readings taken where the pages are silent:
     v / X (ties to the even mantissa), the quotient first clamped to +-448.
   * Quantised are the experts' inputs: x for the routed and shared experts
     (the router keeps the bf16 x, as the gate stays at high precision), and
-    h = SiLU(g) * u for the down projection, after h is rounded to bf16 (the
-    precision h is stored in between the two projections).
+    h = SiLU(g) * u for the down projection, quantised straight from its
+    value (the pages say only "W4A8": no other rounding of h is implied).
   * Products and sums are then exact float64 arithmetic on the dequantised
     values.
 """
@@ -97,9 +97,9 @@ def expert_hidden(xq: np.ndarray, w13_q, w13_s) -> np.ndarray:
 
 def expert_mlp_w4a8(xq: np.ndarray, w13_q, w13_s, w2_q, w2_s) -> np.ndarray:
     """One expert over already quantised input rows xq [n][H] (float64):
-    h rounded to bf16 and quantised to MXFP8 along I, then the down
+    h quantised to MXFP8 along I from its float64 value, then the down
     projection."""
-    h = mxfp8_fake_quant(bf16_round(expert_hidden(xq, w13_q, w13_s)))
+    h = mxfp8_fake_quant(expert_hidden(xq, w13_q, w13_s))
     W2 = dequant_mxfp4(w2_q, w2_s)
     return h @ W2.T
 

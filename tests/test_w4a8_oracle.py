@@ -135,11 +135,14 @@ def _mxfp4_rows(rows, exp):
 def test_layer_quantisation_points_handbuilt():
     """One expert, k = 1, no shared expert, H = I = 32.  Gate rows read
     x[0] = 1 with weight 48, so g = 48 and SiLU(g) = 48 exactly in float64;
-    up row i = x[i] + 0.5 x[i+1]; down = identity.  Then
-    y = q(bf16(48 * (q(x)_i + 0.5 q(x)_{i+1}))) where q is the MXFP8 round
-    trip: x quantised before the experts, h rounded to bf16 then quantised."""
+    up row i = 6 x[i] + 0.5 x[i+1]; down = identity.  Then
+    y = q(48 * (6 q(x)_i + 0.5 q(x)_{i+1})) where q is the MXFP8 round trip:
+    x quantised before the experts, h quantised from its exact value.  The
+    input is chosen so that h has more significant bits than bf16 keeps and
+    rounding h to bf16 first would move three of its codes: the pin tells the
+    two readings apart."""
     H = I = 32
-    rng = np.random.default_rng(5)
+    rng = np.random.default_rng(13)
     x = np.round(rng.standard_normal(H) * 64) / 64 * 2.0 ** rng.integers(-3, 3, H)
     x[0] = 1.0
     x_bits = synth.f32_to_bf16_bits(x.astype(np.float32))[None]
@@ -147,7 +150,7 @@ def test_layer_quantisation_points_handbuilt():
     gate = np.zeros((I, H)); gate[:, 0] = 48.0
     up = np.zeros((I, H))
     for i in range(I):
-        up[i, i] = 1.0
+        up[i, i] = 6.0
         up[i, (i + 1) % I] = 0.5
     down = np.eye(H)
     qg, sg = _mxfp4_rows(gate, 3)                    # 48 = 6 * 2^3
@@ -160,11 +163,28 @@ def test_layer_quantisation_points_handbuilt():
                                 k=1, shared=False)
     xq = oracle.mxfp8_fake_quant(xb[None])[0]
     assert xq[0] == 1.0
-    u = xq + 0.5 * np.roll(xq, -1)
-    want = oracle.mxfp8_fake_quant(oracle.bf16_round(48.0 * u)[None])[0]
+    h = 48.0 * (6.0 * xq + 0.5 * np.roll(xq, -1))
+    want = oracle.mxfp8_fake_quant(h[None])[0]
     assert np.array_equal(out["y"][0], want)
     # and the quantisations are visible: neither x nor h is left unquantised
-    assert not np.array_equal(want, 48.0 * (xb + 0.5 * np.roll(xb, -1)))
+    assert not np.array_equal(want, 48.0 * (6.0 * xb + 0.5 * np.roll(xb, -1)))
+    assert not np.array_equal(want, h)
+    # h quantised from bf16(h) instead would differ in three elements
+    via_bf16 = oracle.mxfp8_fake_quant(oracle.bf16_round(h)[None])[0]
+    assert int(np.sum(via_bf16 != want)) == 3
+
+
+def test_mxfp8_of_h_is_not_mxfp8_of_bf16_h():
+    """A value one part in 2^12 above an E4M3 midpoint rounds up directly, but
+    to the midpoint (then down, to the even code) through bf16's 8 bits: in a
+    block whose largest element is 256 (X = 1), 136 + 1/32 -> code 144 direct,
+    136 -> 128 through bf16."""
+    v = np.zeros((1, 32))
+    v[0, 0] = 256.0
+    v[0, 1] = 136.0 + 1.0 / 32
+    assert oracle.bf16_round(v[0, 1:2])[0] == 136.0
+    assert oracle.mxfp8_fake_quant(v)[0, 1] == 144.0
+    assert oracle.mxfp8_fake_quant(oracle.bf16_round(v))[0, 1] == 128.0
 
 
 def _tiny():
@@ -182,8 +202,8 @@ def test_layer_routing_is_the_bf16_layers():
 
 
 def test_layer_scale_metamorphics():
-    """+1 on every down scale doubles y; +1 on every up scale doubles u, so h,
-    its bf16 rounding and its MXFP8 round trip double, and so does y."""
+    """+1 on every down scale doubles y; +1 on every up scale doubles u, so h
+    and its MXFP8 round trip double, and so does y."""
     wl, ls = _tiny()
     args = (ls.x_bits, ls.w_router, ls.bias)
     base = oracle.moe_layer_w4a8(*args, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s, wl.k)["y"]
