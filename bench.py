@@ -4,19 +4,23 @@
 A step is one whole layer -- one moe_layer call (router GEMV + top-k, the sort
 by expert, every active expert's fused dequant GEMVs and the weighted combine
 plus the shared expert; --three-calls times moe_route, moe_sort_by_expert and
-moe_mxfp4_forward instead) -- on the next of
-`--sets` distinct layer weight sets, so consecutive steps never reuse expert
-weights and the 256 MB Infinity Cache cannot serve them.  Steps are replayed
-from a HIP graph of one pass over all sets; inputs are resident in HBM before
-the timed region starts.
+moe_mxfp4_forward instead) -- on the next of `--sets` distinct layer weight
+sets, so consecutive steps never reuse expert weights and the 256 MB Infinity
+Cache cannot serve them.  The K timed steps are replayed from HIP graphs
+(every graph is replayed once before timing); the timed pass runs five times
+and the median is reported.  Inputs are resident in HBM before the timed
+region starts.
 
-Prints one JSON line:
-  value        layer GB/s: algorithmic bytes of a layer / time per layer
-  ms_per_step  time per layer
-  roofline     the dominant kernel (gate/up: two thirds of the expert bytes):
-               its weight bytes per launch / mean launch duration, from HIP
-               events bound to that kernel's own begin/end timestamps
-  cpu_baseline the float64 oracle on a bounded sample of the same workload
+The default run (ling_m1) prints one JSON line for M = 1 with the M = 4
+verify workload (ling_m4_mtp) nested under "ling_m4_mtp":
+  value         layer GB/s: algorithmic bytes of a layer / time per layer
+  ms_per_step   time per layer
+  expert_rate   the experts' MXFP4 bytes / (gate/up + down kernel time), the
+                kernels timed with HIP events bound to their own begin/end
+  roofline      the dominant kernel (gate/up: two thirds of the expert bytes):
+                its weight bytes per launch / mean launch duration
+  cpu_baseline  the float64 oracle on a bounded sample of the same workload
+                (all host threads, and one thread)
 """
 from __future__ import annotations
 
@@ -57,28 +61,6 @@ def layer_bytes(wl, D):
         bias = wl.E * 4
     expert = (D + int(wl.shared)) * expert_bytes_per_expert(wl.H, wl.I)
     return expert, wl.E * wl.H * 4 + wl.M * wl.H * 2 + wl.M * wl.H * 4 + bias + expert
-
-
-class HipEvents:
-    """hipEvent_t handles from the HIP runtime torch already loaded."""
-
-    def __init__(self):
-        self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-
-    def create(self):
-        ev = ctypes.c_void_p()
-        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
-        return ev.value
-
-    def elapsed_ms(self, a, b):
-        ms = ctypes.c_float()
-        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
-        return ms.value
-
-    def destroy(self, ev):
-        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
 
 
 class Prefetcher:
@@ -244,14 +226,34 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline(wl, seconds_budget=20.0, w4a8=False):
-    """The oracle as it stands, on host-generated sets of the same workload."""
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_layers(wl, seconds_budget, w4a8):
+    """Time the oracle as it stands on host-generated sets of the workload,
+    set after set, until the budget is spent: whole layers for M <= 8, else 4
+    sampled tokens per set with the time scaled to the M tokens."""
     import numpy as np
 
     import oracle
     from mxfp4_expert_weight_amd import synth
-    threads = blas_threads()
-    times, nbytes, tokens = [], [], 0
+    times, nbytes = [], []
     start = time.time()
     l = 0
     while l < wl.sets and (time.time() - start) < seconds_budget:
@@ -270,17 +272,32 @@ def cpu_baseline(wl, seconds_budget=20.0, w4a8=False):
             D = int(np.unique(oracle.topk_softmax(oracle.router_logits(
                 oracle.bf16_bits_to_f64(ls.x_bits), ls.w_router, ls.bias), wl.k)[0]).size)
             frac = len(sample) / wl.M
-        dt = time.perf_counter() - t0
-        times.append(dt / frac)
+        times.append((time.perf_counter() - t0) / frac)
         nbytes.append(layer_bytes(wl, D)[1])
-        tokens += wl.M if frac == 1.0 else len(sample)
         l += 1
     sec = sum(times) / len(times)
-    gbs = sum(nbytes) / len(nbytes) / sec / 1e9
+    return sec, sum(nbytes) / len(nbytes) / sec / 1e9, len(times)
+
+
+def cpu_baseline(wl, seconds_budget=10.0, w4a8=False, one_thread=True):
+    """The oracle as it stands, on host-generated sets of the same workload:
+    once with the BLAS's own thread count, once on one thread."""
+    threads = blas_threads()
+    sec, gbs, n = _oracle_layers(wl, seconds_budget, w4a8)
     kind = "whole layers" if wl.M <= 8 else "4 tokens per layer, time scaled to M tokens"
-    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(times)} layer sets of {wl.name} ({kind}); {sec * 1e3:.1f} ms per layer",
-            "us_per_layer": sec * 1e6}
+    out = {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} layer sets of {wl.name} ({kind}); {sec * 1e3:.1f} ms per layer",
+           "us_per_layer": sec * 1e6, "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    if one_thread:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                sec1, gbs1, n1 = _oracle_layers(wl, seconds_budget, w4a8)
+            out["one_thread"] = {"value": gbs1, "unit": "GB/s", "cores": 1, "us_per_layer": sec1 * 1e6,
+                                 "sample": f"{n1} layer sets of {wl.name} ({kind})"}
+        except ImportError:
+            out["one_thread"] = None
+    return out
 
 
 def bench_lmhead(torch, binding, synth, args):
@@ -393,6 +410,8 @@ def main():
                     help="before each layer, N small elementwise kernels on a 256 KB tensor that stays in "
                          "L2: a stand-in for the non-MoE work between two layers that leaves HBM idle "
                          "(with --prefetch, each layer's own experts are prefetched during it)")
+    ap.add_argument("--single", action="store_true",
+                    help="ling_m1 alone (the default run also measures ling_m4_mtp into the same line)")
     ap.add_argument("--three-calls", action="store_true",
                     help="time moe_route + moe_sort_by_expert + moe_mxfp4_forward instead of moe_layer")
     ap.add_argument("--copy-probe", action="store_true",
@@ -417,7 +436,6 @@ def main():
 
     import torch
     from mxfp4_expert_weight_amd import binding, synth
-    from mxfp4_expert_weight_amd.layer import LayerBuffers, run_layer
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.lib()
@@ -436,6 +454,26 @@ def main():
         return
 
     wl = synth.WORKLOADS[args.workload]
+    out = bench_moe(torch, binding, synth, args, wl, cpu=not args.no_cpu_baseline)
+    if args.workload == "ling_m1" and not args.single and not (args.hint is not None or args.prefetch is not None
+                                                              or args.gap_kernels or args.three_calls):
+        # the M = 4 verify workload of the same metric, nested in the same line
+        torch.cuda.empty_cache()
+        m4 = bench_moe(torch, binding, synth, args, synth.WORKLOADS["ling_m4_mtp"], cpu=not args.no_cpu_baseline,
+                       cpu_budget=5.0, one_thread=False)
+        keep = ("us_per_layer", "value", "unit", "ms_per_step", "layer_frac_of_hbm_peak", "expert_bytes_per_layer",
+                "expert_rate", "roofline", "mean_distinct_experts", "config", "timed_passes_us_per_layer",
+                "cpu_baseline")
+        out["ling_m4_mtp"] = {k: m4[k] for k in keep if k in m4}
+        out["t_m4_over_t_m1"] = m4["us_per_layer"] / out["us_per_layer"]
+    print(json.dumps(out), flush=True)
+
+
+def bench_moe(torch, binding, synth, args, wl, cpu=True, cpu_budget=10.0, one_thread=True):
+    """Measure one MoE workload; returns the bench line's fields."""
+    import statistics
+
+    from mxfp4_expert_weight_amd.layer import HelperStreams, HipEvents, LayerBuffers, run_layer
     nsets = args.sets or wl.sets
     t0 = time.time()
     sets = device_sets(torch, wl, nsets)
@@ -443,13 +481,15 @@ def main():
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB)")
     buf = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
     weights = [d.weights() for d in sets]
+    # batches run their matrix-core experts on two helper streams of ours
+    helpers = HelperStreams() if wl.M > 4 else None
 
     # one eager pass: loads the kernels and records each set's distinct-expert count
     D, G, true_ids = [], [], []
     for d, w in zip(sets, weights):
-        run_layer(d, buf, w, w4a8=args.w4a8)
+        run_layer(d, buf, w, w4a8=args.w4a8, helpers=helpers)
         D.append(int(buf.num_active.item()))
-        G.append(buf.header()["gemv_experts"])   # experts on the GEMV path (the timed kernel)
+        G.append(buf.header()["gemv_experts"])   # experts on the GEMV path (the timed kernels)
         true_ids.append(buf.ids.cpu().numpy())
     log(f"[bench] distinct routed experts per set: min {min(D)} max {max(D)} mean {sum(D) / len(D):.2f}")
 
@@ -473,15 +513,17 @@ def main():
         torch.cuda.synchronize()
         hint_frac = hit / max(need, 1)
 
-    def run_step(i):
+    def run_step(i, gu_ev=None, dn_ev=None):
         l = i % nsets
         if hints is not None:
             d = sets[l]
             binding.moe_layer_hinted(d.x, d.w_router, d.bias, d.bias_row_stride, weights[l], d.M, d.k, buf.logits,
                                      buf.ids, buf.weights, buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y,
-                                     buf.ws, buf.ws_bytes, hints[l][0], hints[l][1])
+                                     buf.ws, buf.ws_bytes, hints[l][0], hints[l][1],
+                                     *(gu_ev if gu_ev is not None else (None, None)))
         else:
-            run_layer(sets[l], buf, weights[l], fused=not args.three_calls, w4a8=args.w4a8)
+            run_layer(sets[l], buf, weights[l], fused=not args.three_calls, w4a8=args.w4a8, helpers=helpers,
+                      gateup_events=gu_ev, down_events=dn_ev)
 
     pf = None
     if args.prefetch is not None:
@@ -495,13 +537,14 @@ def main():
         for _ in range(args.gap_kernels):
             gap.add_(1.0)
 
-    def capture(n, prefetch, layers=True):
+    def capture(first, n, prefetch, layers=True):
+        """A graph of steps first .. first+n-1 (layer set = step mod nsets)."""
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
 
         def steps():
             W = args.prefetch_window
-            for i in range(n):
+            for i in range(first, first + n):
                 if gap is not None:
                     # the stand-in gap; with the prefetch, this layer's experts are read during it
                     if prefetch:
@@ -512,8 +555,8 @@ def main():
                     if layers:
                         run_step(i)
                     continue
-                if prefetch and i % W == 0:
-                    if i:
+                if prefetch and (i - first) % W == 0:
+                    if i != first:
                         pf.join()
                     pf.fork([(i + W + j) % nsets for j in range(W)])
                 run_step(i)
@@ -528,37 +571,50 @@ def main():
             steps()
         return g
 
-    def timed_replays(prefetch, layers=True):
-        g_full = capture(nsets, prefetch, layers)
-        rem = args.steps % nsets
-        g_rem = capture(rem, prefetch, layers) if rem else None
-        reps = args.steps // nsets
-        for _ in range(math.ceil(args.warmup / nsets)):
-            g_full.replay()
+    def timed_replays(prefetch, layers=True, passes=5):
+        """K = args.steps steps: a graph per pass over the sets plus one for the
+        remainder, each replayed once before timing (and --warmup steps of
+        replays in all); then `passes` timed passes of exactly K steps, each
+        bracketed by synchronisations.  Returns the per-pass times (ms)."""
+        K = args.steps
+        reps, rem = K // nsets, K % nsets
+        g_full = capture(0, nsets, prefetch, layers) if reps else None
+        g_rem = capture(reps * nsets, rem, prefetch, layers) if rem else None
+
+        def one_pass():
+            for _ in range(reps):
+                g_full.replay()
+            if g_rem is not None:
+                g_rem.replay()
+
+        one_pass()                                   # every graph replayed once before timing
+        for _ in range(math.ceil(max(args.warmup - K, 0) / max(K, 1))):
+            one_pass()
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        ev0.record()
-        for _ in range(reps):
-            g_full.replay()
-        if g_rem is not None:
-            g_rem.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1), time.perf_counter() - w0
+        ms = []
+        for _ in range(passes):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ev0.record()
+            one_pass()
+            ev1.record()
+            torch.cuda.synchronize()
+            ms.append(ev0.elapsed_time(ev1))
+        return ms
 
     plain_ms = gap_ms = None
     if gap is not None:
-        gap_ms, _ = timed_replays(False, layers=False)
+        gap_ms = statistics.median(timed_replays(False, layers=False))
         log(f"[bench] the gap alone ({args.gap_kernels} kernels): {gap_ms / args.steps * 1e3:.2f} us per step")
     if pf is not None:
-        plain_ms, _ = timed_replays(False)
+        plain_ms = statistics.median(timed_replays(False))
         log(f"[bench] without prefetch: {plain_ms / args.steps * 1e3:.2f} us per step")
-    ms_total, wall = timed_replays(pf is not None)
+    passes = timed_replays(pf is not None)
+    ms_total = statistics.median(passes)
     if gap is not None:                  # the layer's share of each step
         log(f"[bench] gap + layer: {ms_total / args.steps * 1e3:.2f} us per step")
         ms_total -= gap_ms
+        passes = [p - gap_ms for p in passes]
         if plain_ms is not None:
             plain_ms -= gap_ms
     ms_per_step = ms_total / args.steps
@@ -566,25 +622,23 @@ def main():
     exp_b = [layer_bytes(wl, D[l])[0] for l in step_sets]
     lay_b = [layer_bytes(wl, D[l])[1] for l in step_sets]
     layer_gbs = sum(lay_b) / (ms_total * 1e-3) / 1e9
-    log(f"[bench] {args.steps} steps in {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms): "
+    log(f"[bench] {wl.name}: {args.steps} steps, median of {len(passes)} passes {ms_total:.3f} ms "
+        f"({', '.join(f'{p / args.steps * 1e3:.2f}' for p in passes)} us/layer): "
         f"{ms_per_step * 1e3:.2f} us/layer, {layer_gbs:.0f} GB/s")
 
-    # Roofline of the GEMV gate/up kernel (the dominant kernel of the decode
-    # batches: 2/3 of the expert bytes): per-launch durations from HIP events
-    # bound to that kernel's own begin/end timestamps, over the same K steps run
-    # eagerly on the stream the kernels use.  Its bytes are those of the experts
-    # the header reports on the GEMV path (all of them for M <= 4).
+    # The GEMV gate/up and down kernels (for M <= 4 every expert runs on them;
+    # gate/up is the dominant kernel, two thirds of the expert bytes): per-launch
+    # durations from HIP events bound to each kernel's own begin/end timestamps,
+    # over the same K steps run eagerly on the stream the kernels use.  Their
+    # bytes are those of the experts the header reports on the GEMV path.
     hev = HipEvents()
-    n_ev = min(args.steps, 4000)
-    starts = [hev.create() for _ in range(n_ev)]
-    stops = [hev.create() for _ in range(n_ev)]
-    stream = torch.cuda.current_stream().cuda_stream
+    n_ev = min(args.steps, 2000)
+    evs = [[hev.create() for _ in range(4)] for _ in range(n_ev)]
     torch.cuda.synchronize()
     W = args.prefetch_window
     if pf is not None and gap is None:   # the first window's experts, as the replays leave them
         pf.fork([step_sets[j % len(step_sets)] for j in range(W)])
     for i in range(n_ev):
-        d, w = sets[step_sets[i]], weights[step_sets[i]]
         if gap is not None:
             if pf is not None:
                 pf.fork([step_sets[i]])
@@ -594,27 +648,28 @@ def main():
         elif pf is not None and i % W == 0:
             pf.join()
             pf.fork([(step_sets[i] + W + j) % nsets for j in range(W)])
-        if hints is not None:
-            hs = hints[step_sets[i]]
-            binding.moe_layer_hinted(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits, buf.ids,
-                                     buf.weights, buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y, buf.ws,
-                                     buf.ws_bytes, hs[0], hs[1], starts[i], stops[i], stream)
-        else:
-            timed = binding.moe_layer_w4a8_timed if args.w4a8 else binding.moe_layer_timed
-            timed(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, buf.logits, buf.ids, buf.weights,
-                  buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y, buf.ws, buf.ws_bytes, starts[i],
-                  stops[i], stream)
+        run_step(i, evs[i][:2], evs[i][2:])
     if pf is not None and gap is None:
         pf.join()
     torch.cuda.synchronize()
-    spans = [hev.elapsed_ms(starts[i], stops[i]) for i in range(n_ev)]
-    for e in starts + stops:
-        hev.destroy(e)
-    gu_ms = sum(spans) / n_ev
+    gu_ms = sum(hev.elapsed_ms(e[0], e[1]) for e in evs) / n_ev
+    dn_ms = None if hints is not None else sum(hev.elapsed_ms(e[2], e[3]) for e in evs) / n_ev
+    for e in evs:
+        for h in e:
+            hev.destroy(h)
     gu_bytes = sum(G[step_sets[i]] * gateup_bytes_per_expert(wl.H, wl.I) for i in range(n_ev)) / n_ev
+    gemv_exp_bytes = sum(G[step_sets[i]] * expert_bytes_per_expert(wl.H, wl.I) for i in range(n_ev)) / n_ev
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
     log(f"[bench] gate/up kernel: {gu_ms * 1e3:.2f} us per launch, {gu_bytes / 1e6:.2f} MB, "
         f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+    expert_rate = None
+    if dn_ms is not None:
+        rate = gemv_exp_bytes / ((gu_ms + dn_ms) * 1e-3) / 1e9
+        expert_rate = {"value": round(rate, 2), "unit": "GB/s", "frac_of_hbm_peak": rate / HBM_PEAK_GBS,
+                       "gateup_us": gu_ms * 1e3, "down_us": dn_ms * 1e3, "bytes": gemv_exp_bytes,
+                       "what": "(experts on the GEMV path) x 3,133,440 B / (gate/up + down kernel time)"}
+        log(f"[bench] down kernel: {dn_ms * 1e3:.2f} us per launch; expert rate {rate:.0f} GB/s "
+            f"({rate / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
     out = {
         "metric": METRIC,
@@ -630,18 +685,21 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name,
-                   "entry": "moe_layer_w4a8" if args.w4a8 else ("three calls" if args.three_calls else "moe_layer"),
+                   "entry": "moe_layer_ex (W4A8)" if args.w4a8 else ("three calls" if args.three_calls else "moe_layer"),
                    "M": wl.M, "hidden": wl.H, "inter": wl.I, "experts": wl.E,
                    "top_k": wl.k, "shared_expert": wl.shared, "routing": wl.routing,
                    "layer_sets_rotated": nsets, "weights": "MXFP4 (E2M1 + E8M0/32)",
-                   "activations": "MXFP8 (E4M3 + E8M0/32) into the experts" if args.w4a8 else "bf16"},
+                   "activations": "MXFP8 (E4M3 + E8M0/32) into the experts" if args.w4a8 else "bf16",
+                   "helper_streams": helpers is not None},
         "us_per_layer": ms_per_step * 1e3,
+        "timed_passes_us_per_layer": [p / args.steps * 1e3 for p in passes],
         "layer_bytes": sum(lay_b) / len(lay_b),
         "layer_frac_of_hbm_peak": layer_gbs / HBM_PEAK_GBS,
         # the routed and shared experts' MXFP4 bytes over the whole layer time
         "expert_bytes_per_layer": sum(exp_b) / len(exp_b),
         "expert_gbs": sum(exp_b) / (ms_total * 1e-3) / 1e9,
         "expert_frac_of_hbm_peak": sum(exp_b) / (ms_total * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "expert_rate": expert_rate,
         "mean_distinct_experts": sum(D[l] for l in step_sets) / len(step_sets),
         "roofline": {"bound": "hbm", "kernel": "gateup_kernel",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -664,11 +722,12 @@ def main():
             out["config"]["prefetch"]["when"] = "during the gap before the layer, on a side stream"
         out["us_per_layer_without_prefetch"] = plain_ms / args.steps * 1e3
         out["roofline"]["traffic"] = None     # counters were taken without the prefetch beside the layer
-    if not args.no_cpu_baseline:
-        del sets
-        torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(wl, w4a8=args.w4a8)
-    print(json.dumps(out), flush=True)
+    del sets, weights, buf, pf
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, seconds_budget=cpu_budget, w4a8=args.w4a8, one_thread=one_thread)
+    return out
 
 
 if __name__ == "__main__":

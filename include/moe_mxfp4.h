@@ -11,16 +11,12 @@
  *
  * Conventions shared by every call
  *  - Pointers marked "device" are HIP device pointers owned by the caller; the
- *    library allocates no device memory and never copies device data to the
- *    host.  All work is enqueued on `stream` (a hipStream_t; NULL = the default
- *    stream) and is asynchronous; no call synchronises.  The one piece of state:
- *    for batches of more than 4 tokens, moe_layer and moe_mxfp4_forward run the
- *    matrix-core expert kernels on two helper streams of their own (made on the
- *    first such call on a device, default priority), forked from and joined back
- *    to `stream` with events, so the work stays ordered on `stream` and can be
- *    captured into a HIP graph (if that first call is itself being captured,
- *    every kernel is enqueued on `stream`).  Host threads enqueueing such calls
- *    at the same time are serialised around the fork and join.
+ *    library allocates no device memory, never copies device data to the host
+ *    and keeps no state between calls (so calls from several host threads are
+ *    safe as long as they share no buffer, stream or event).  All work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream) and is
+ *    asynchronous; no call synchronises.  The _ex calls can also take helper
+ *    streams and events from the caller (moe_exec_opts).
  *  - Argument checks run on the host before anything is enqueued and return a
  *    status; nothing is launched when a check fails.  MOE_ERR_HIP means a launch
  *    was rejected by the HIP runtime (e.g. no gfx950 device).  No call aborts,
@@ -81,6 +77,35 @@ typedef struct {
   int32_t has_shared;   /* S: 0 or 1 */
 } moe_mxfp4_weights;
 
+/* Execution options of moe_layer_ex and moe_mxfp4_forward_ex.  Zero-initialise
+ * it; every field is optional, and a NULL options pointer means all zeros.
+ *   act8            0: bf16 activations into the experts (W4A16, as moe_layer);
+ *                   1: the W4A8 variant (as moe_layer_w4a8, see below)
+ *   helper_streams  two hipStream_t of the caller (default priority), or both
+ *                   NULL.  For batches of more than 4 tokens the few-token and
+ *                   scaled-MFMA expert kernels then run on them beside the GEMV
+ *                   kernels on `stream`; they are forked from `stream` and joined
+ *                   back to it with helper_events, so the call stays ordered on
+ *                   `stream` and can be captured into a HIP graph.  NULL: every
+ *                   kernel runs on `stream`, in order.  Calls enqueued at the
+ *                   same time must not share helper streams or events.
+ *   helper_events   four hipEvent_t of the caller (timing may be disabled);
+ *                   required when helper_streams are given, else ignored
+ *   gateup_events   two hipEvent_t, or NULL: they take the begin and end
+ *                   timestamps of the GEMV gate/up kernel (for M <= 4 it
+ *                   includes the in-block routing), so hipEventElapsedTime gives
+ *                   that kernel's own execution time (for measurement)
+ *   down_events     the same for the GEMV down kernel
+ * Status: MOE_ERR_SHAPE for act8 outside {0, 1}; MOE_ERR_NULL for one helper
+ * stream without the other, or helper streams with a NULL event. */
+typedef struct {
+  int32_t act8;
+  void* helper_streams[2];
+  void* helper_events[4];
+  void* gateup_events[2];
+  void* down_events[2];
+} moe_exec_opts;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(moe_status st);
 
@@ -128,8 +153,11 @@ moe_status moe_sort_by_expert(const int32_t* topk_ids, int32_t M, int32_t top_k,
                               int32_t* expert_offsets, int32_t* sorted_pairs,
                               int32_t* active_experts, int32_t* num_active, void* stream);
 
-/* The experts and the combine: for every active expert e and each of its pairs
- * p = t*k + s, h = SiLU(x_t Wg_e^T) * (x_t Wu_e^T) and
+/* The experts and the combine (digest "3 Ways to Improve MoE Inference on
+ * NVIDIA DGX Spark", sections 2-3: MXFP4 experts plus one shared expert;
+ * MoE-SpeQ article, 3.2 and 4.2: each expert runs once over its sorted pairs
+ * and the expert outputs are reduced across experts): for every active expert
+ * e and each of its pairs p = t*k + s, h = SiLU(x_t Wg_e^T) * (x_t Wu_e^T) and
  *   y_t = sum_s topk_weights[t][s] * (h Wd_e^T) + (shared expert of x_t, weight 1).
  * Reads the sort outputs on the device (num_active is never copied to the host).
  * Arithmetic: MXFP4 weights decode exactly; products accumulate in fp32; h is
@@ -149,6 +177,14 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int3
                              const int32_t* num_active, float* y, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* moe_mxfp4_forward with execution options (helper streams, timing events,
+ * W4A8 activations: moe_exec_opts).  opts may be NULL. */
+moe_status moe_mxfp4_forward_ex(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                                const float* topk_weights, const int32_t* expert_offsets,
+                                const int32_t* sorted_pairs, const int32_t* active_experts,
+                                const int32_t* num_active, float* y, void* workspace, size_t workspace_bytes,
+                                const moe_exec_opts* opts, void* stream);
+
 /* The whole layer in one call: moe_route, moe_sort_by_expert and
  * moe_mxfp4_forward with the same arguments and outputs, fused into fewer
  * launches.  For M <= 4 (decode, speculative verify) there are three: the
@@ -165,26 +201,25 @@ moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logi
                      int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* moe_layer, plus timing of its dominant kernel: `start_event` / `stop_event`
- * (hipEvent_t, may be NULL) take the begin and end timestamps of the gate/up
- * kernel (hipExtLaunchKernelGGL; for M <= 4 it includes the in-block routing),
- * so hipEventElapsedTime gives that kernel's own execution time.  For measurement; results are those of moe_layer. */
-moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float* logit_bias,
-                           int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
-                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
-                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
-                           void* workspace, size_t workspace_bytes, void* start_event, void* stop_event,
-                           void* stream);
+/* moe_layer with execution options (moe_exec_opts: the W4A8 variant, helper
+ * streams for batches, timing events of the gate/up and down kernels).  Same
+ * arguments, outputs and limits as moe_layer; opts may be NULL (= moe_layer). */
+moe_status moe_layer_ex(const uint16_t* x, const float* w_router, const float* logit_bias,
+                        int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                        float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                        int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                        void* workspace, size_t workspace_bytes, const moe_exec_opts* opts, void* stream);
 
 /* moe_layer with a hint from a draft pass (speculative decoding predicts the
  * experts of the coming tokens: MoE-SpeQ article, 4.1).  Same arguments,
- * outputs and limits as moe_layer_timed (the events may be NULL), plus:
+ * outputs and limits as moe_layer, plus two timing events of the gate/up
+ * kernel (as moe_exec_opts.gateup_events; may be NULL) and:
  *   hint_experts device int32 [*num_hint]: the routed experts the draft
  *                predicts for this layer, ascending (e.g. moe_sort_by_expert's
  *                active_experts of the draft's ids); entries outside [0, E)
  *                are ignored
  *   num_hint     device int32 [1]: their count
- * Both NULL: moe_layer_timed.  Only one NULL: MOE_ERR_NULL.  For M <= 4 the
+ * Both NULL: moe_layer.  Only one NULL: MOE_ERR_NULL.  For M <= 4 the
  * gate/up workgroups whose waves are idle during the routing read one word
  * of every 64-byte line of their rows of hint_experts[slot], so a right guess
  * finds the stream in L2; the results never depend on the hint. */
@@ -217,22 +252,15 @@ moe_status moe_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t K, uint8_
 /* moe_layer in the W4A8 variant.  Same arguments, outputs and limits; the
  * routing (logits, ids, weights, sort outputs) is moe_layer's, on the bf16 x.
  * The experts (routed and shared) take x as MXFP8 (each element replaced by
- * its code's value), and the down projection takes h as MXFP8 along I after h
- * is rounded to bf16.  Experts with >= 16 tokens run on the scaled MXFP4
+ * its code's value), and the down projection takes h as MXFP8 along I,
+ * quantised from h as computed (fp32 sums, carried between the kernels as two
+ * bf16 terms, about 16 significant bits).  Experts with >= 16 tokens run on the scaled MXFP4
  * matrix cores with one MXFP8 activation term. */
 moe_status moe_layer_w4a8(const uint16_t* x, const float* w_router, const float* logit_bias,
                           int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                           void* workspace, size_t workspace_bytes, void* stream);
-
-/* moe_layer_w4a8 with the gate/up kernel's timestamps (as moe_layer_timed). */
-moe_status moe_layer_w4a8_timed(const uint16_t* x, const float* w_router, const float* logit_bias,
-                                int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
-                                float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
-                                int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
-                                void* workspace, size_t workspace_bytes, void* start_event, void* stop_event,
-                                void* stream);
 
 /* Dequantise an MXFP4 tensor [rows][cols] (layout above) to fp32 with the same
  * device routine the expert kernels use (exposes it for exact checks).

@@ -39,6 +39,32 @@ class moe_mxfp4_weights(ctypes.Structure):
     ]
 
 
+class moe_exec_opts(ctypes.Structure):
+    _fields_ = [
+        ("act8", ctypes.c_int32),
+        ("helper_streams", ctypes.c_void_p * 2),
+        ("helper_events", ctypes.c_void_p * 4),
+        ("gateup_events", ctypes.c_void_p * 2),
+        ("down_events", ctypes.c_void_p * 2),
+    ]
+
+
+def make_opts(act8=False, helper_streams=None, helper_events=None, gateup_events=None,
+              down_events=None) -> moe_exec_opts:
+    """moe_exec_opts from plain handles (ints or None); unset fields are NULL."""
+    o = moe_exec_opts()
+    o.act8 = int(act8)
+    for field, vals, n in (("helper_streams", helper_streams, 2), ("helper_events", helper_events, 4),
+                           ("gateup_events", gateup_events, 2), ("down_events", down_events, 2)):
+        if vals is not None:
+            if len(vals) != n:
+                raise ValueError(f"{field} takes {n} handles")
+            arr = getattr(o, field)
+            for i, v in enumerate(vals):
+                arr[i] = v
+    return o
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -55,14 +81,14 @@ _SIGNATURES = {
                                          _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P, _P,
                                  _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "moe_layer_timed": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32,
-                                       _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
+    "moe_mxfp4_forward_ex": (ctypes.c_int, [_P, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P, _P,
+                                            _P, _P, _P, _P, _P, _SZ, ctypes.POINTER(moe_exec_opts), _P]),
+    "moe_layer_ex": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P, _P,
+                                    _P, _P, _P, _P, _P, _P, _P, _SZ, ctypes.POINTER(moe_exec_opts), _P]),
     "moe_layer_hinted": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32,
                                         _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P]),
     "moe_layer_w4a8": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P,
                                       _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "moe_layer_w4a8_timed": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32,
-                                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
     "moe_mxfp8_quantize": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
     "moe_mxfp4_dequantize": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     "moe_prefetch_select": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
@@ -177,15 +203,24 @@ def moe_layer(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weights, M,
                            workspace_bytes, _stream(stream)), "moe_layer")
 
 
-def moe_layer_timed(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weights, M, top_k, logits,
-                    topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
-                    workspace, workspace_bytes, start_event, stop_event, stream=None):
-    _check(lib().moe_layer_timed(_ptr(x), _ptr(w_router), _ptr(logit_bias), bias_row_stride,
-                                 ctypes.byref(w) if w is not None else None, M, top_k, _ptr(logits),
-                                 _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_offsets),
-                                 _ptr(sorted_pairs), _ptr(active_experts), _ptr(num_active), _ptr(y),
-                                 _ptr(workspace), workspace_bytes, start_event, stop_event,
-                                 _stream(stream)), "moe_layer_timed")
+def moe_layer_ex(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weights, M, top_k, logits,
+                 topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
+                 workspace, workspace_bytes, opts: moe_exec_opts | None = None, stream=None):
+    _check(lib().moe_layer_ex(_ptr(x), _ptr(w_router), _ptr(logit_bias), bias_row_stride,
+                              ctypes.byref(w) if w is not None else None, M, top_k, _ptr(logits),
+                              _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_offsets), _ptr(sorted_pairs),
+                              _ptr(active_experts), _ptr(num_active), _ptr(y), _ptr(workspace), workspace_bytes,
+                              ctypes.byref(opts) if opts is not None else None, _stream(stream)), "moe_layer_ex")
+
+
+def moe_mxfp4_forward_ex(x, w: moe_mxfp4_weights, M, top_k, topk_weights, expert_offsets, sorted_pairs,
+                         active_experts, num_active, y, workspace, workspace_bytes,
+                         opts: moe_exec_opts | None = None, stream=None):
+    _check(lib().moe_mxfp4_forward_ex(_ptr(x), ctypes.byref(w) if w is not None else None, M, top_k,
+                                      _ptr(topk_weights), _ptr(expert_offsets), _ptr(sorted_pairs),
+                                      _ptr(active_experts), _ptr(num_active), _ptr(y), _ptr(workspace),
+                                      workspace_bytes, ctypes.byref(opts) if opts is not None else None,
+                                      _stream(stream)), "moe_mxfp4_forward_ex")
 
 
 def moe_layer_hinted(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weights, M, top_k, logits,
@@ -208,17 +243,6 @@ def moe_layer_w4a8(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weight
                                 _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_offsets), _ptr(sorted_pairs),
                                 _ptr(active_experts), _ptr(num_active), _ptr(y), _ptr(workspace),
                                 workspace_bytes, _stream(stream)), "moe_layer_w4a8")
-
-
-def moe_layer_w4a8_timed(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weights, M, top_k, logits,
-                         topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
-                         workspace, workspace_bytes, start_event, stop_event, stream=None):
-    _check(lib().moe_layer_w4a8_timed(_ptr(x), _ptr(w_router), _ptr(logit_bias), bias_row_stride,
-                                      ctypes.byref(w) if w is not None else None, M, top_k, _ptr(logits),
-                                      _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_offsets),
-                                      _ptr(sorted_pairs), _ptr(active_experts), _ptr(num_active), _ptr(y),
-                                      _ptr(workspace), workspace_bytes, start_event, stop_event,
-                                      _stream(stream)), "moe_layer_w4a8_timed")
 
 
 def moe_mxfp8_quantize(x, rows, K, codes, scales, values, stream=None):

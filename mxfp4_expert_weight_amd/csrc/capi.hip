@@ -1,9 +1,8 @@
 // C ABI of the MXFP4 MoE layer: host-side argument checks, then launches.
-// Nothing here allocates device memory or synchronises.  The only state is a
-// pair of helper streams per device (with their events), made on first use,
-// on which batches run their matrix-core expert kernels beside the GEMV ones.
+// Nothing here allocates device memory, synchronises or keeps state between
+// calls; streams and events other than the caller's `stream` come from the
+// caller (moe_exec_opts).
 #include <climits>
-#include <mutex>
 
 #include "kernels.h"
 
@@ -88,53 +87,57 @@ RecOut layer_recout(const ForwardArgs& a, void* workspace) {
                 const_cast<int*>(a.inv), const_cast<int*>(a.lists)};
 }
 
-// Two helper streams per device (default priority) and the events that fork
-// them from, and join them back to, the caller's stream.  Made on the first
-// call that needs them, unless that call's stream is being captured into a
-// graph (then the kernels go on the caller's stream in order).
-struct SideStreams {
+// The caller's helper streams and events (moe_exec_opts), if any: batches fork
+// the matrix-core expert kernels onto them and join them back to `stream`.
+// The library keeps none of its own.
+struct Helpers {
   hipStream_t mt, mfma;
   hipEvent_t fork, zeroed, mt_done, mfma_done;
 };
-std::mutex g_side_mu;                // one fork/join sequence is enqueued at a time
 
-SideStreams* side_streams(hipStream_t s) {
-  constexpr int kMaxDevices = 64;
-  static SideStreams side[kMaxDevices];
-  static bool made[kMaxDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  if (made[dev]) return &side[dev];
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-  SideStreams& q = side[dev];
-  if (hipStreamCreateWithFlags(&q.mt, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  if (hipStreamCreateWithFlags(&q.mfma, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  for (hipEvent_t* ev : {&q.fork, &q.zeroed, &q.mt_done, &q.mfma_done})
-    if (hipEventCreateWithFlags(ev, hipEventDisableTiming) != hipSuccess) return nullptr;
-  made[dev] = true;
-  return &q;
+bool helpers_of(const moe_exec_opts* o, Helpers& h) {
+  if (!o || !o->helper_streams[0]) return false;
+  h.mt = (hipStream_t)o->helper_streams[0];
+  h.mfma = (hipStream_t)o->helper_streams[1];
+  h.fork = (hipEvent_t)o->helper_events[0];
+  h.zeroed = (hipEvent_t)o->helper_events[1];
+  h.mt_done = (hipEvent_t)o->helper_events[2];
+  h.mfma_done = (hipEvent_t)o->helper_events[3];
+  return true;
+}
+
+// Host check of the options: helper streams come as a pair with all four events.
+moe_status check_opts(const moe_exec_opts* o) {
+  if (!o) return MOE_OK;
+  if (o->act8 != 0 && o->act8 != 1) return MOE_ERR_SHAPE;
+  const bool any = o->helper_streams[0] || o->helper_streams[1];
+  if (any) {
+    if (!o->helper_streams[0] || !o->helper_streams[1]) return MOE_ERR_NULL;
+    for (void* e : o->helper_events)
+      if (!e) return MOE_ERR_NULL;
+  }
+  return MOE_OK;
 }
 
 // The expert stage: GEMV gate/up (zeroes y) and down for the experts with
 // one or two tokens; with the few-token path on, its kernels take experts of
 // kMtMinTokens..kMtMaxTokens tokens; with the MFMA path on, x is quantised
 // first and the dense kernels take the experts listed in the work items.
-// The three paths touch disjoint experts and h rows, so the matrix-core
-// kernels run on the helper streams beside the GEMV ones.  With atomics into
-// y, their down kernels wait for the GEMV gate/up kernel that zeroes y; when
-// combining by rows nothing waits, and the combine kernel runs after the join.
-hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+// The three paths touch disjoint experts and h rows, so with the caller's
+// helper streams the matrix-core kernels run beside the GEMV ones.  With
+// atomics into y, their down kernels wait for the GEMV gate/up kernel that
+// zeroes y; when combining by rows nothing waits, and the combine kernel runs
+// after the join.  Without helpers every kernel goes on `s` in order.
+hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, const moe_exec_opts* o) {
   const bool mfma = a.mfma_min == kMfmaMinTokens;
   const bool mt = a.mt_min == kMtMinTokens;
   const bool rows = a.yp != nullptr;
+  const Timing tm = timing_of(o);
   hipError_t e = hipSuccess;
-  std::unique_lock<std::mutex> lock(g_side_mu);
-  SideStreams* q = (mt || mfma) ? side_streams(s) : nullptr;
-  if (!q) {
-    lock.unlock();
+  Helpers q{};
+  if (!(mt || mfma) || !helpers_of(o, q)) {
     if (mfma && !a.act8 && (e = launch_forward_mfma_front(a, s)) != hipSuccess) return e;
-    if ((e = launch_forward(a, s, start, stop)) != hipSuccess) return e;
+    if ((e = launch_forward(a, s, tm)) != hipSuccess) return e;
     if (mt) {
       if ((e = launch_gateup_mt(a, s)) != hipSuccess) return e;
       if (a.act8 && (e = launch_h_round_trip(a, 1, s)) != hipSuccess) return e;
@@ -149,54 +152,75 @@ hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, hipEvent_t start,
   }
   // the GEMV kernels go first (their few workgroups are then not queued
   // behind the matrix-core paths' many); the fork point is before them
-  if ((e = hipEventRecord(q->fork, s)) != hipSuccess) return e;
-  if ((e = launch_forward(a, s, start, stop, q->zeroed)) != hipSuccess) return e;
-  if (mt && (e = hipStreamWaitEvent(q->mt, q->fork, 0)) != hipSuccess) return e;
-  if (mfma && (e = hipStreamWaitEvent(q->mfma, q->fork, 0)) != hipSuccess) return e;
-  if (mt && (e = launch_gateup_mt(a, q->mt)) != hipSuccess) return e;
-  if (mt && a.act8 && (e = launch_h_round_trip(a, 1, q->mt)) != hipSuccess) return e;
+  if ((e = hipEventRecord(q.fork, s)) != hipSuccess) return e;
+  if ((e = launch_forward(a, s, tm, q.zeroed)) != hipSuccess) return e;
+  if (mt && (e = hipStreamWaitEvent(q.mt, q.fork, 0)) != hipSuccess) return e;
+  if (mfma && (e = hipStreamWaitEvent(q.mfma, q.fork, 0)) != hipSuccess) return e;
+  if (mt && (e = launch_gateup_mt(a, q.mt)) != hipSuccess) return e;
+  if (mt && a.act8 && (e = launch_h_round_trip(a, 1, q.mt)) != hipSuccess) return e;
   if (mfma) {
-    if (!a.act8 && (e = launch_forward_mfma_front(a, q->mfma)) != hipSuccess) return e;
-    if ((e = launch_gateup_mfma(a, q->mfma)) != hipSuccess) return e;
+    if (!a.act8 && (e = launch_forward_mfma_front(a, q.mfma)) != hipSuccess) return e;
+    if ((e = launch_gateup_mfma(a, q.mfma)) != hipSuccess) return e;
   }
   if (mt) {
-    if (!rows && (e = hipStreamWaitEvent(q->mt, q->zeroed, 0)) != hipSuccess) return e;
-    if ((e = launch_down_mt(a, q->mt)) != hipSuccess) return e;
-    if ((e = hipEventRecord(q->mt_done, q->mt)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(s, q->mt_done, 0)) != hipSuccess) return e;
+    if (!rows && (e = hipStreamWaitEvent(q.mt, q.zeroed, 0)) != hipSuccess) return e;
+    if ((e = launch_down_mt(a, q.mt)) != hipSuccess) return e;
+    if ((e = hipEventRecord(q.mt_done, q.mt)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s, q.mt_done, 0)) != hipSuccess) return e;
   }
   if (mfma) {
-    if (!rows && (e = hipStreamWaitEvent(q->mfma, q->zeroed, 0)) != hipSuccess) return e;
-    if ((e = launch_down_mfma(a, q->mfma)) != hipSuccess) return e;
-    if ((e = hipEventRecord(q->mfma_done, q->mfma)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(s, q->mfma_done, 0)) != hipSuccess) return e;
+    if (!rows && (e = hipStreamWaitEvent(q.mfma, q.zeroed, 0)) != hipSuccess) return e;
+    if ((e = launch_down_mfma(a, q.mfma)) != hipSuccess) return e;
+    if ((e = hipEventRecord(q.mfma_done, q.mfma)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(s, q.mfma_done, 0)) != hipSuccess) return e;
   }
   if (rows) e = launch_combine_rows(a, s);
   return e;
 }
 
+// W4A8 (act8): the experts' x as MXFP8 values.  Decode batches with short
+// rows round x as the gate/up kernel stages it; otherwise x is quantised once
+// into the workspace (values for the GEMV and few-token paths, codes and
+// scales for the scaled-MFMA path, which takes one term).
+hipError_t prepare_act8(ForwardArgs& a, const uint16_t* x, int M, int H, hipStream_t s) {
+  if (M <= kRoutedMaxTokens && routed_stages_x(H)) {
+    a.x = x;
+    return hipSuccess;
+  }
+  const bool mfma = a.mfma_min == kMfmaMinTokens;
+  return launch_mxfp8_quantize(x, M, H, mfma ? a.xq_hi : nullptr, mfma ? a.xq_shi : nullptr,
+                               const_cast<uint16_t*>(a.x), s);
+}
+
+moe_status check_bank(const moe_mxfp4_weights* w) {
+  if (!w->w13_q || !w->w13_s || !w->w2_q || !w->w2_s) return MOE_ERR_NULL;
+  moe_status st;
+  if ((st = check_hidden(w->hidden)) != MOE_OK) return st;
+  if ((st = check_inter(w->inter)) != MOE_OK) return st;
+  if (w->has_shared != 0 && w->has_shared != 1) return MOE_ERR_SHAPE;
+  if (!aligned16(w->w13_q) || !aligned16(w->w13_s) || !aligned16(w->w2_q) || !aligned16(w->w2_s))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
 moe_status layer_impl(const uint16_t* x, const float* w_router, const float* logit_bias,
-                           int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
-                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
-                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
-                           void* workspace, size_t workspace_bytes_, void* start_event, void* stop_event,
-                           void* stream, bool act8, const int32_t* hint = nullptr,
-                           const int32_t* num_hint = nullptr) {
+                      int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                      float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                      int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                      void* workspace, size_t workspace_bytes_, const moe_exec_opts* opts, void* stream,
+                      const int32_t* hint = nullptr, const int32_t* num_hint = nullptr) {
   if (!x || !w_router || !w || !logits || !topk_ids || !topk_weights || !expert_offsets ||
       !sorted_pairs || !active_experts || !num_active || !y || !workspace)
     return MOE_ERR_NULL;
-  if (!w->w13_q || !w->w13_s || !w->w2_q || !w->w2_s) return MOE_ERR_NULL;
-  const int32_t E = w->num_experts, H = w->hidden;
-  moe_status st = check_route_sizes(M, E, top_k);
+  moe_status st = check_bank(w);
   if (st != MOE_OK) return st;
-  if ((st = check_hidden(H)) != MOE_OK) return st;
-  if ((st = check_inter(w->inter)) != MOE_OK) return st;
-  if (w->has_shared != 0 && w->has_shared != 1) return MOE_ERR_SHAPE;
+  const int32_t E = w->num_experts, H = w->hidden;
+  if ((st = check_route_sizes(M, E, top_k)) != MOE_OK) return st;
+  if ((st = check_opts(opts)) != MOE_OK) return st;
   if (logit_bias && bias_row_stride != 0 && bias_row_stride != E) return MOE_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w->w13_q) || !aligned16(w->w13_s) ||
-      !aligned16(w->w2_q) || !aligned16(w->w2_s) || ((uintptr_t)workspace & 255u))
-    return MOE_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(w_router) || ((uintptr_t)workspace & 255u)) return MOE_ERR_ALIGN;
   if (workspace_bytes_ < workspace_layout(M, top_k, E, H, w->inter).total) return MOE_ERR_WORKSPACE;
+  const bool act8 = opts && opts->act8;
   hipStream_t s = (hipStream_t)stream;
   if (launch_router_logits(x, w_router, logit_bias, logit_bias ? bias_row_stride : 0, M, H, E, logits,
                            s) != hipSuccess)
@@ -205,25 +229,13 @@ moe_status layer_impl(const uint16_t* x, const float* w_router, const float* log
                              num_active, y, workspace, act8);
   a.hint = hint;
   a.num_hint = num_hint;
-  if (act8) {
-    if (M <= kRoutedMaxTokens && routed_stages_x(H)) {
-      a.x = x;                       // the decode gate/up kernel rounds x to MXFP8 as it stages it
-    } else {
-      // the experts' input: x as MXFP8 values (bf16), and its codes and
-      // scales for the MFMA path, which takes them as one term
-      const bool mfma = a.mfma_min == kMfmaMinTokens;
-      if (launch_mxfp8_quantize(x, M, H, mfma ? a.xq_hi : nullptr, mfma ? a.xq_shi : nullptr,
-                                const_cast<uint16_t*>(a.x), s) != hipSuccess)
-        return MOE_ERR_HIP;
-    }
-  }
+  if (act8 && prepare_act8(a, x, M, H, s) != hipSuccess) return MOE_ERR_HIP;
   SlotRec* rec = const_cast<SlotRec*>(a.rec);
-  hipEvent_t start = (hipEvent_t)start_event, stop = (hipEvent_t)stop_event;
   if (M <= kRoutedMaxTokens) {
     // decode: every gate/up block routes itself from the logits
     const RouteOut r{logits, topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts,
                      num_active, rec, expert_bits(E)};
-    return hip_status(launch_forward_routed(a, r, s, start, stop));
+    return hip_status(launch_forward_routed(a, r, s, timing_of(opts)));
   }
   if (topk_sort_fits_one_block(M)) a.lists = nullptr;   // the one-workgroup sort writes records only
   const RecOut ro = layer_recout(a, workspace);
@@ -238,7 +250,44 @@ moe_status layer_impl(const uint16_t* x, const float* w_router, const float* log
                                 num_active, s, ro);
   }
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(launch_experts(a, s, start, stop));
+  return hip_status(launch_experts(a, s, opts));
+}
+
+moe_status forward_impl(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                        const float* topk_weights, const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                        const int32_t* active_experts, const int32_t* num_active, float* y, void* workspace,
+                        size_t workspace_bytes_, const moe_exec_opts* opts, void* stream) {
+  if (!x || !w || !topk_weights || !expert_offsets || !sorted_pairs || !active_experts || !num_active || !y ||
+      !workspace)
+    return MOE_ERR_NULL;
+  moe_status st = check_bank(w);
+  if (st != MOE_OK) return st;
+  if ((st = check_route_sizes(M, w->num_experts, top_k)) != MOE_OK) return st;
+  if ((st = check_opts(opts)) != MOE_OK) return st;
+  if (!aligned16(x) || ((uintptr_t)workspace & 255u)) return MOE_ERR_ALIGN;
+  if (workspace_bytes_ < workspace_layout(M, top_k, w->num_experts, w->hidden, w->inter).total)
+    return MOE_ERR_WORKSPACE;
+  const bool act8 = opts && opts->act8;
+  hipStream_t s = (hipStream_t)stream;
+  ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
+                             num_active, y, workspace, act8);
+  if (act8) {   // the sort-driven kernels take x as MXFP8 values from the workspace
+    const bool mfma = a.mfma_min == kMfmaMinTokens;
+    if (launch_mxfp8_quantize(x, M, w->hidden, mfma ? a.xq_hi : nullptr, mfma ? a.xq_shi : nullptr,
+                              const_cast<uint16_t*>(a.x), s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (a.mfma_min == kMfmaMinTokens || a.mt_min == kMtMinTokens || a.yp) {
+    // the path choice needs per-expert token counts, the combine the pairs'
+    // sorted positions: records (slot lists, MFMA items, positions) first
+    const RecOut ro = layer_recout(a, workspace);
+    if (launch_records(expert_offsets, sorted_pairs, active_experts, num_active, a.E, ro, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else {
+    a.rec = nullptr;                 // few tokens: resolved from the sort outputs directly
+    a.lists = nullptr;
+  }
+  return hip_status(launch_experts(a, s, opts));
 }
 
 }  // namespace
@@ -304,56 +353,27 @@ moe_status moe_mxfp4_forward(const uint16_t* x, const moe_mxfp4_weights* w, int3
                              const int32_t* sorted_pairs, const int32_t* active_experts,
                              const int32_t* num_active, float* y, void* workspace,
                              size_t workspace_bytes_, void* stream) {
-  if (!x || !w || !topk_weights || !expert_offsets || !sorted_pairs || !active_experts ||
-      !num_active || !y || !workspace)
-    return MOE_ERR_NULL;
-  if (!w->w13_q || !w->w13_s || !w->w2_q || !w->w2_s) return MOE_ERR_NULL;
-  moe_status st = check_route_sizes(M, w->num_experts, top_k);
-  if (st != MOE_OK) return st;
-  if ((st = check_hidden(w->hidden)) != MOE_OK) return st;
-  if ((st = check_inter(w->inter)) != MOE_OK) return st;
-  if (w->has_shared != 0 && w->has_shared != 1) return MOE_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(w->w13_q) || !aligned16(w->w13_s) || !aligned16(w->w2_q) ||
-      !aligned16(w->w2_s) || ((uintptr_t)workspace & 255u))
-    return MOE_ERR_ALIGN;
-  if (workspace_bytes_ < workspace_layout(M, top_k, w->num_experts, w->hidden, w->inter).total)
-    return MOE_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  ForwardArgs a = layer_args(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts,
-                             num_active, y, workspace);
-  if (a.mfma_min == kMfmaMinTokens || a.mt_min == kMtMinTokens || a.yp) {
-    // the path choice needs per-expert token counts, the combine the pairs'
-    // sorted positions: records (slot lists, MFMA items, positions) first
-    const RecOut ro = layer_recout(a, workspace);
-    if (launch_records(expert_offsets, sorted_pairs, active_experts, num_active, a.E, ro, s) != hipSuccess)
-      return MOE_ERR_HIP;
-  } else {
-    a.rec = nullptr;                 // few tokens: resolved from the sort outputs directly
-    a.lists = nullptr;
-  }
-  return hip_status(launch_experts(a, s, nullptr, nullptr));
+  return forward_impl(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
+                      workspace, workspace_bytes_, nullptr, stream);
 }
 
-moe_status moe_layer_timed(const uint16_t* x, const float* w_router, const float* logit_bias,
-                           int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
-                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
-                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
-                           void* workspace, size_t workspace_bytes_, void* start_event, void* stop_event,
-                           void* stream) {
-  return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
-                    expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
-                    start_event, stop_event, stream, false);
+moe_status moe_mxfp4_forward_ex(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                                const float* topk_weights, const int32_t* expert_offsets,
+                                const int32_t* sorted_pairs, const int32_t* active_experts,
+                                const int32_t* num_active, float* y, void* workspace, size_t workspace_bytes_,
+                                const moe_exec_opts* opts, void* stream) {
+  return forward_impl(x, w, M, top_k, topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
+                      workspace, workspace_bytes_, opts, stream);
 }
 
-moe_status moe_layer_w4a8_timed(const uint16_t* x, const float* w_router, const float* logit_bias,
-                                int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
-                                float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
-                                int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
-                                void* workspace, size_t workspace_bytes_, void* start_event, void* stop_event,
-                                void* stream) {
+moe_status moe_layer_ex(const uint16_t* x, const float* w_router, const float* logit_bias, int64_t bias_row_stride,
+                        const moe_mxfp4_weights* w, int32_t M, int32_t top_k, float* logits, int32_t* topk_ids,
+                        float* topk_weights, int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* active_experts,
+                        int32_t* num_active, float* y, void* workspace, size_t workspace_bytes_,
+                        const moe_exec_opts* opts, void* stream) {
   return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
                     expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
-                    start_event, stop_event, stream, true);
+                    opts, stream);
 }
 
 moe_status moe_layer_hinted(const uint16_t* x, const float* w_router, const float* logit_bias,
@@ -364,9 +384,12 @@ moe_status moe_layer_hinted(const uint16_t* x, const float* w_router, const floa
                             const int32_t* num_hint, void* start_event, void* stop_event, void* stream) {
   if ((hint_experts == nullptr) != (num_hint == nullptr)) return MOE_ERR_NULL;
   if (((uintptr_t)hint_experts & 3u) || ((uintptr_t)num_hint & 3u)) return MOE_ERR_ALIGN;
+  moe_exec_opts o{};
+  o.gateup_events[0] = start_event;
+  o.gateup_events[1] = stop_event;
   return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
                     expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
-                    start_event, stop_event, stream, false, hint_experts, num_hint);
+                    &o, stream, hint_experts, num_hint);
 }
 
 moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logit_bias,
@@ -374,9 +397,9 @@ moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logi
                      float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
                      int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                      void* workspace, size_t workspace_bytes_, void* stream) {
-  return moe_layer_timed(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids,
-                         topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
-                         workspace, workspace_bytes_, nullptr, nullptr, stream);
+  return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
+                    expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
+                    nullptr, stream);
 }
 
 moe_status moe_layer_w4a8(const uint16_t* x, const float* w_router, const float* logit_bias,
@@ -384,9 +407,11 @@ moe_status moe_layer_w4a8(const uint16_t* x, const float* w_router, const float*
                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                           void* workspace, size_t workspace_bytes_, void* stream) {
+  moe_exec_opts o{};
+  o.act8 = 1;
   return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
                     expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
-                    nullptr, nullptr, stream, true);
+                    &o, stream);
 }
 
 moe_status moe_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,

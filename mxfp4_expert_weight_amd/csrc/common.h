@@ -160,23 +160,27 @@ __device__ __forceinline__ float mxfp8_round_value(float v, int e) {
   const int qe = max(f, e - 6) - 3;
   return ldexpf(__builtin_rintf(ldexpf(c, -qe)), qe);
 }
-// MXFP8 round trip of 16 bf16 values (8 words, low half first) that are half
-// of a 32-element block whose other half lane ^ 1 holds and passes at the
-// same time (the exchange is a DPP quad swap, so lane ^ 1 must be active).
-// Each value becomes the value of its code, as bf16 (exact for blocks whose
-// largest magnitude is at least 2^-110).
-__device__ __forceinline__ void mxfp8_round_trip16(uint32_t (&w)[8]) {
-  uint32_t m = 0u;                                   // |v| as bf16 bits: ordered like the values
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = max(m, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-  m = max(m, dpp_quad_xor1(m));
-  const int e = mxfp8_exponent(__uint_as_float(m << 16));
+// MXFP8 round trip of 16 values carried as two bf16 terms, v = hi + lo (the
+// sum is exact in fp32: lo is the rounding residual of hi), quantised from
+// that value; the result (a code's value, exact in bf16) replaces hi.  The
+// 16 values are half of a 32-element block whose other half lane ^ 1 holds
+// and passes at the same time (DPP quad swap: lane ^ 1 must be active).
+__device__ __forceinline__ void mxfp8_round_trip16_2t(uint32_t (&hi)[8], const uint32_t (&lo)[8]) {
+  float v[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float lo = mxfp8_round_value(bf16_bits_to_f32(w[i] & 0xFFFFu), e);
-    const float hi = mxfp8_round_value(bf16_bits_to_f32(w[i] >> 16), e);
-    w[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    v[2 * i] = bf16_bits_to_f32(hi[i] & 0xFFFFu) + bf16_bits_to_f32(lo[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_bits_to_f32(hi[i] >> 16) + bf16_bits_to_f32(lo[i] >> 16);
   }
+  uint32_t m = 0u;                                   // |v| as fp32 bits: ordered like the values
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  m = max(m, dpp_quad_xor1(m));
+  const int e = mxfp8_exponent(__uint_as_float(m));
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    hi[i] = f32_to_bf16_bits(mxfp8_round_value(v[2 * i], e)) |
+            (f32_to_bf16_bits(mxfp8_round_value(v[2 * i + 1], e)) << 16);
 }
 
 // MXFP8 round trip of 8 bf16 values (one uint4) that are a quarter of a

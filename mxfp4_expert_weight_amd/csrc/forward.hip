@@ -377,23 +377,19 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 namespace {
 
-// Compute units of the current device (looked up once per device).
+// Compute units of the current device (queried per launch: no cached state).
 int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 // routed: the gate/up grid has one more row (the routing writer), and one more
 // for the shared expert when the bank has one.
 hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, const RouteOut& r,
-                       bool routed, hipStream_t s, hipEvent_t start, hipEvent_t stop, hipEvent_t mid = nullptr) {
+                       bool routed, hipStream_t s, const Timing& tm, hipEvent_t mid = nullptr) {
   const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
   const int gx = (a.I + GU_PAIRS_PER_BLOCK - 1) / GU_PAIRS_PER_BLOCK;
   int gy = slots;
@@ -409,34 +405,32 @@ hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, 
   auto dn = (a.I <= DN_SHORT_I) ? (a.yp ? down_kernel<true, true> : down_kernel<true, false>)
                                 : (a.yp ? down_kernel<false, true> : down_kernel<false, false>);
   // with events, they take the gate/up kernel's own begin/end timestamps
-  hipExtLaunchKernelGGL(gu, ggu, bgu, 0, s, start, stop, 0, a, r);
+  hipExtLaunchKernelGGL(gu, ggu, bgu, 0, s, tm.gu_start, tm.gu_stop, 0, a, r);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (mid && (err = hipEventRecord(mid, s)) != hipSuccess) return err;   // y is zeroed from here on
   // W4A8: h goes through the MXFP8 round trip once, in place, between the
   // two kernels (decode: every row; batches: the rows of this path's experts)
   if (a.act8) {
-    err = routed ? launch_mxfp8_round_trip_rows(a.h, (int64_t)a.M * a.k + a.M, a.I, s)
+    err = routed ? launch_mxfp8_round_trip_rows(a.h, a.hlo, (int64_t)a.M * a.k + a.M, a.I, s)
                  : launch_h_round_trip(a, 0, s);
     if (err != hipSuccess) return err;
   }
-  hipExtLaunchKernelGGL(dn, gdn, bdn, 0, s, nullptr, nullptr, 0, a);
+  hipExtLaunchKernelGGL(dn, gdn, bdn, 0, s, tm.dn_start, tm.dn_stop, 0, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start, hipEvent_t stop,
-                          hipEvent_t zeroed) {
+hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, const Timing& tm, hipEvent_t zeroed) {
   const RouteOut none{};
   return launch_pair(a.H <= GU_SHORT_H ? gateup_kernel<true, 0> : gateup_kernel<false, 0>, a, none, false, s,
-                     start, stop, zeroed);
+                     tm, zeroed);
 }
 
 bool routed_stages_x(int H) { return H <= GU_SHORT_H; }
 
-hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s, hipEvent_t start,
-                                 hipEvent_t stop) {
+hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s, const Timing& tm) {
   const bool short_h = a.H <= GU_SHORT_H;
   const bool a8x = a.act8 && short_h;                // x rounded while staged (else a.x is already MXFP8)
   void (*gu)(ForwardArgs, RouteOut);
@@ -449,7 +443,7 @@ hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStr
     gu = short_h ? (a8x ? gateup_kernel<true, 16, true>
                         : (hint ? gateup_kernel<true, 16, false, true> : gateup_kernel<true, 16>))
                  : gateup_kernel<false, 16>;
-  return launch_pair(gu, a, r, true, s, start, stop);
+  return launch_pair(gu, a, r, true, s, tm);
 }
 
 hipError_t launch_combine_rows(const ForwardArgs& a, hipStream_t s) {

@@ -247,12 +247,12 @@ __device__ __forceinline__ void gateup_short(const ForwardArgs& a, const ExpertS
     for (int p = 0; p < NP; ++p) {
       const float g = group_sum<32>(accg[p]);
       const float u = group_sum<32>(accu[p]);
-      if (j32 == 0) {   // h = hi + lo, two bf16 terms (the down kernels read both)
+      if (j32 == 0) {   // h = hi + lo, two bf16 terms (the down kernels, or W4A8's round trip, read both)
         const float v = silu(g) * u;
         const uint32_t hi = f32_to_bf16_bits(v);
         const size_t o = (size_t)hrow * I + jp0 + 2 * p + grp;
         a.h[o] = (uint16_t)hi;
-        if (!a.act8) a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));   // W4A8: hi alone
+        a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
       }
     }
   }
@@ -306,12 +306,12 @@ __device__ __forceinline__ void gateup_long(const ForwardArgs& a, const ExpertSl
     for (int p = 0; p < NP; ++p) {
       const float g = group_sum<32>(accg[p]);
       const float u = group_sum<32>(accu[p]);
-      if (j32 == 0) {   // h = hi + lo, two bf16 terms (the down kernels read both)
+      if (j32 == 0) {   // h = hi + lo, two bf16 terms (the down kernels, or W4A8's round trip, read both)
         const float v = silu(g) * u;
         const uint32_t hi = f32_to_bf16_bits(v);
         const size_t o = (size_t)hrow * I + jp0 + 2 * p + grp;
         a.h[o] = (uint16_t)hi;
-        if (!a.act8) a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));   // W4A8: hi alone
+        a.hlo[o] = (uint16_t)f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
       }
     }
   }

@@ -185,17 +185,27 @@ hipError_t launch_topk_softmax(const float* logits, int M, int E, int k, int* id
 hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int* sorted_pairs,
                                  int* active, int* num_active, hipStream_t s,
                                  RecOut ro = RecOut{nullptr, nullptr, 0, 0, 0, 0, nullptr, nullptr, 0, 0, nullptr, nullptr});
+// Timing events bound to the GEMV gate/up and down kernels' own begin and
+// end timestamps (hipExtLaunchKernelGGL); null: none.
+struct Timing {
+  hipEvent_t gu_start, gu_stop, dn_start, dn_stop;
+};
+inline Timing timing_of(const moe_exec_opts* o) {
+  if (!o) return Timing{};
+  return Timing{(hipEvent_t)o->gateup_events[0], (hipEvent_t)o->gateup_events[1], (hipEvent_t)o->down_events[0],
+                (hipEvent_t)o->down_events[1]};
+}
 // GEMV experts: gate/up (which zeroes y; `zeroed`, if given, is recorded on s
 // right after it), then down.
-hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, hipEvent_t start = nullptr,
-                          hipEvent_t stop = nullptr, hipEvent_t zeroed = nullptr);
+hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, const Timing& tm = Timing{},
+                          hipEvent_t zeroed = nullptr);
 // Gate/up with the top-k and the expert sort done in every block from the
 // logits (M <= kRoutedMaxTokens), then down.  W4A8 (act8): rows of at most
 // this many elements are rounded to MXFP8 as the kernel stages x (a.x is the
 // bf16 x); longer rows need a.x to hold the MXFP8 values already.
 bool routed_stages_x(int H);
 hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s,
-                                 hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+                                 const Timing& tm = Timing{});
 // MFMA path (mfma.hip): two-term MXFP8 quantisation of x, the dense gate/up
 // and down products of the experts listed in the work items.
 hipError_t launch_forward_mfma_front(const ForwardArgs& a, hipStream_t s);   // x quantisation
@@ -215,9 +225,10 @@ hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int64_t rows, int6
 // and the codes' values as bf16, each optional.
 hipError_t launch_mxfp8_quantize(const uint16_t* src, int64_t rows, int K, uint8_t* codes, uint8_t* scales,
                                  uint16_t* deq, hipStream_t s);
-// MXFP8 round trip (codes' values, as bf16) of rows [rows][K] in place; and
-// of the h rows of one path's experts (path 0: GEMV, 1: few-token) in place.
-hipError_t launch_mxfp8_round_trip_rows(uint16_t* p, int64_t rows, int K, hipStream_t s);
+// MXFP8 round trip (codes' values, as bf16) of h rows [rows][K] carried as
+// two bf16 terms, quantised from hi + lo, the result in hi; and of the h rows
+// of one path's experts (path 0: GEMV, 1: few-token) the same way.
+hipError_t launch_mxfp8_round_trip_rows(uint16_t* hi, const uint16_t* lo, int64_t rows, int K, hipStream_t s);
 hipError_t launch_h_round_trip(const ForwardArgs& a, int path, hipStream_t s);
 // Expert prefetch (prefetch.hip).  The chosen arrays of one expert (gate/up
 // codes, gate/up scales, down codes, down scales: those whose part is

@@ -321,9 +321,7 @@ __global__ __launch_bounds__(MF_WAVES * kWave) void gateup_mfma_kernel(ForwardAr
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] = ul[tc][i];
       const int64_t hrow = rec.hrow0 + t0 + tc;
-      if constexpr (ONE) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = bf16_bits_to_f32(f32_to_bf16_bits(v[i]));
+      if constexpr (ONE) {   // W4A8: one MXFP8 term, quantised from the fp32 h
         uint32_t h[8], sh;
         encode_one_term(v, h, sh);
         uint4* dh = reinterpret_cast<uint4*>(a.hq_hi + hrow * a.I + j0);

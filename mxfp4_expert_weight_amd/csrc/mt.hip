@@ -160,7 +160,7 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
     wu = nu;
   }
   // lane (g, j): indices jw + 4g + r of token j
-  if (j < rec.n) {   // h = hi + lo, two bf16 terms
+  if (j < rec.n) {   // h = hi + lo, two bf16 terms (W4A8: the MXFP8 round trip reads both)
     uint32_t hb[4], lb[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -170,8 +170,7 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
     }
     const int64_t o = ((int64_t)rec.hrow0 + j) * I + jw + 4 * g;
     *reinterpret_cast<uint2*>(a.h + o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-    if (!a.act8)   // W4A8 layers carry their MXFP8 h in hi alone
-      *reinterpret_cast<uint2*>(a.hlo + o) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+    *reinterpret_cast<uint2*>(a.hlo + o) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
   }
 }
 

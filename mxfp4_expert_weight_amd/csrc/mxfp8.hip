@@ -61,22 +61,31 @@ hipError_t launch_mxfp8_quantize(const uint16_t* src, int64_t rows, int K, uint8
   return hipGetLastError();
 }
 
-// MXFP8 round trip of bf16 elements in place, 16 per thread (threads 2b and
-// 2b + 1 share block b): rows [rows][K] from p.
-__global__ __launch_bounds__(256) void mxfp8_round_trip_kernel(uint16_t* __restrict__ p, int64_t nblocks) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if ((t >> 1) >= nblocks) return;                  // whole pairs exit together
-  uint4* q = reinterpret_cast<uint4*>(p + t * 16);
-  const uint4 u0 = q[0], u1 = q[1];
+// 16 elements of h (two bf16 terms, hi + lo) rounded to MXFP8 from their
+// value; the codes' values replace hi.  Threads 2b and 2b + 1 share block b.
+__device__ __forceinline__ void h_round_trip16(uint16_t* hi, const uint16_t* lo) {
+  uint4* q = reinterpret_cast<uint4*>(hi);
+  const uint4* l = reinterpret_cast<const uint4*>(lo);
+  const uint4 u0 = q[0], u1 = q[1], v0 = l[0], v1 = l[1];
   uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-  mxfp8_round_trip16(w);
+  const uint32_t r[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  mxfp8_round_trip16_2t(w, r);
   q[0] = make_uint4(w[0], w[1], w[2], w[3]);
   q[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }
 
-hipError_t launch_mxfp8_round_trip_rows(uint16_t* p, int64_t rows, int K, hipStream_t s) {
+// MXFP8 round trip of h rows [rows][K] (hi + lo) in place, 16 elements per
+// thread.
+__global__ __launch_bounds__(256) void mxfp8_round_trip_kernel(uint16_t* __restrict__ hi,
+                                                               const uint16_t* __restrict__ lo, int64_t nblocks) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if ((t >> 1) >= nblocks) return;                  // whole pairs exit together
+  h_round_trip16(hi + t * 16, lo + t * 16);
+}
+
+hipError_t launch_mxfp8_round_trip_rows(uint16_t* hi, const uint16_t* lo, int64_t rows, int K, hipStream_t s) {
   const int64_t nb = rows * (K / 32);
-  mxfp8_round_trip_kernel<<<dim3((unsigned)((2 * nb + 255) / 256)), dim3(256), 0, s>>>(p, nb);
+  mxfp8_round_trip_kernel<<<dim3((unsigned)((2 * nb + 255) / 256)), dim3(256), 0, s>>>(hi, lo, nb);
   return hipGetLastError();
 }
 
@@ -99,12 +108,8 @@ __global__ __launch_bounds__(256) void h_round_trip_kernel(ForwardArgs a) {
   const int64_t nb = (int64_t)r.n * (a.I / 32);
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if ((t >> 1) >= nb) return;                       // whole pairs exit together
-  uint4* q = reinterpret_cast<uint4*>(a.h + (int64_t)r.hrow0 * a.I + t * 16);
-  const uint4 u0 = q[0], u1 = q[1];
-  uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-  mxfp8_round_trip16(w);
-  q[0] = make_uint4(w[0], w[1], w[2], w[3]);
-  q[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  const int64_t o = (int64_t)r.hrow0 * a.I + t * 16;
+  h_round_trip16(a.h + o, a.hlo + o);
 }
 
 hipError_t launch_h_round_trip(const ForwardArgs& a, int path, hipStream_t s) {

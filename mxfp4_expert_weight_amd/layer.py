@@ -3,6 +3,7 @@ the C ABI only (``binding``).  torch is used for device memory and streams.
 """
 from __future__ import annotations
 
+import ctypes
 from dataclasses import dataclass
 from typing import Optional
 
@@ -78,25 +79,89 @@ class LayerBuffers:
         return dict(gemv_experts=h[0], mfma_experts=h[1], mfma_items=h[2], mt_experts=h[3])
 
 
+class HipEvents:
+    """hipEvent_t handles made through the HIP runtime torch already loaded
+    (torch's own events are created lazily, on their first record)."""
+
+    DISABLE_TIMING = 0x2
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, timing=True) -> int:
+        ev = ctypes.c_void_p()
+        flags = 0 if timing else self.DISABLE_TIMING
+        if self.hip.hipEventCreateWithFlags(ctypes.byref(ev), flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+class HelperStreams:
+    """The caller-owned helper streams (two torch streams, default priority) and
+    fork/join events (four, timing disabled) that let a batch's matrix-core
+    expert kernels run beside the GEMV ones (moe_exec_opts).  One set per
+    concurrently enqueued layer."""
+
+    def __init__(self):
+        self.streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        self._ev = HipEvents()
+        self.events = [self._ev.create(timing=False) for _ in range(4)]
+
+    def opts(self, **kw) -> binding.moe_exec_opts:
+        return binding.make_opts(helper_streams=[s.cuda_stream for s in self.streams], helper_events=self.events,
+                                 **kw)
+
+    def __del__(self):
+        for e in getattr(self, "events", []):
+            try:
+                self._ev.destroy(e)
+            except Exception:
+                pass
+
+
 def run_layer(d: DeviceLayerSet, b: LayerBuffers, w: Optional[binding.moe_mxfp4_weights] = None,
-              stream=None, fused: bool = True, w4a8: bool = False):
+              stream=None, fused: bool = True, w4a8: bool = False, helpers: Optional[HelperStreams] = None,
+              gateup_events=None, down_events=None):
     """One layer: moe_layer (fused=True) or moe_route -> moe_sort_by_expert ->
-    moe_mxfp4_forward (fused=False); same outputs, stream-ordered.  w4a8:
-    moe_layer_w4a8 (MXFP8 activations into the experts)."""
+    moe_mxfp4_forward (fused=False); same outputs, stream-ordered.  w4a8: the
+    W4A8 variant (MXFP8 activations into the experts).  helpers: the batch's
+    matrix-core kernels on helper streams; gateup_events / down_events: (begin,
+    end) event handles bound to the GEMV gate/up / down kernels."""
     if w is None:
         w = d.weights()
-    if w4a8:
-        binding.moe_layer_w4a8(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, b.logits, b.ids,
-                               b.weights, b.offsets, b.pairs, b.active, b.num_active, b.y, b.ws, b.ws_bytes,
-                               stream)
-        return
+    opts = None
+    if w4a8 or helpers is not None or gateup_events is not None or down_events is not None:
+        kw = dict(act8=w4a8, gateup_events=gateup_events, down_events=down_events)
+        opts = helpers.opts(**kw) if helpers is not None else binding.make_opts(**kw)
     if fused:
-        binding.moe_layer(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, b.logits, b.ids,
-                          b.weights, b.offsets, b.pairs, b.active, b.num_active, b.y, b.ws, b.ws_bytes,
-                          stream)
+        if opts is None:
+            binding.moe_layer(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, b.logits, b.ids,
+                              b.weights, b.offsets, b.pairs, b.active, b.num_active, b.y, b.ws, b.ws_bytes,
+                              stream)
+        else:
+            binding.moe_layer_ex(d.x, d.w_router, d.bias, d.bias_row_stride, w, d.M, d.k, b.logits, b.ids,
+                                 b.weights, b.offsets, b.pairs, b.active, b.num_active, b.y, b.ws, b.ws_bytes,
+                                 opts, stream)
         return
     binding.moe_route(d.x, d.w_router, d.bias, d.bias_row_stride, d.M, d.H, d.E, d.k, b.logits, b.ids,
                       b.weights, stream)
     binding.moe_sort_by_expert(b.ids, d.M, d.k, d.E, b.offsets, b.pairs, b.active, b.num_active, stream)
-    binding.moe_mxfp4_forward(d.x, w, d.M, d.k, b.weights, b.offsets, b.pairs, b.active, b.num_active,
-                              b.y, b.ws, b.ws_bytes, stream)
+    if opts is None:
+        binding.moe_mxfp4_forward(d.x, w, d.M, d.k, b.weights, b.offsets, b.pairs, b.active, b.num_active,
+                                  b.y, b.ws, b.ws_bytes, stream)
+    else:
+        binding.moe_mxfp4_forward_ex(d.x, w, d.M, d.k, b.weights, b.offsets, b.pairs, b.active, b.num_active,
+                                     b.y, b.ws, b.ws_bytes, opts, stream)

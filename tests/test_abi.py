@@ -96,11 +96,14 @@ def test_forward_host_checks(lib):
     assert _status(f, *(args[:11] + [ws - 1, 0])) == B.MOE_ERR_WORKSPACE
 
 
-@pytest.mark.parametrize("name", ["moe_layer", "moe_layer_w4a8"])
+@pytest.mark.parametrize("name", ["moe_layer", "moe_layer_w4a8", "moe_layer_ex"])
 def test_layer_host_checks(lib, name):
     w = B.make_weights(A, A, A, A, 512, 2560, 768, 1)
     ws = B.moe_workspace_bytes(1, 8, 512, 2560, 768)
     f = getattr(B, name)
+    if name == "moe_layer_ex":
+        ex = f
+        f = lambda *a: ex(*a[:-1], None, a[-1])      # noqa: E731  (NULL options)
     args = [A, A, None, 0, w, 1, 8, A, A, A, A, A, A, A, A, A, ws, 0]
     assert _status(f, *([None] + args[1:])) == B.MOE_ERR_NULL
     assert _status(f, *(args[:4] + [None] + args[5:])) == B.MOE_ERR_NULL
@@ -108,6 +111,27 @@ def test_layer_host_checks(lib, name):
     assert _status(f, *(args[:2] + [A, 3] + args[4:])) == B.MOE_ERR_SHAPE         # bias stride
     assert _status(f, *(args[:1] + [MIS] + args[2:])) == B.MOE_ERR_ALIGN
     assert _status(f, *(args[:16] + [ws - 1, 0])) == B.MOE_ERR_WORKSPACE
+
+
+def test_exec_opts_host_checks(lib):
+    """moe_exec_opts: act8 in {0, 1}; helper streams come as a pair, with all
+    four events (checked before anything is enqueued)."""
+    w = B.make_weights(A, A, A, A, 512, 2560, 768, 1)
+    ws = B.moe_workspace_bytes(24, 8, 512, 2560, 768)
+    args = [A, A, None, 0, w, 24, 8, A, A, A, A, A, A, A, A, A, ws]
+    fwd = [A, w, 24, 8, A, A, A, A, A, A, A, ws]
+    cases = [(B.make_opts(act8=2), B.MOE_ERR_SHAPE),
+             (B.make_opts(helper_streams=[A, None], helper_events=[A, A, A, A]), B.MOE_ERR_NULL),
+             (B.make_opts(helper_streams=[None, A], helper_events=[A, A, A, A]), B.MOE_ERR_NULL),
+             (B.make_opts(helper_streams=[A, A]), B.MOE_ERR_NULL),
+             (B.make_opts(helper_streams=[A, A], helper_events=[A, A, None, A]), B.MOE_ERR_NULL)]
+    for o, st in cases:
+        assert _status(B.moe_layer_ex, *args, o, 0) == st
+        assert _status(B.moe_mxfp4_forward_ex, *fwd, o, 0) == st
+    # a valid options struct still meets the other checks first
+    assert _status(B.moe_layer_ex, *args[:5], 0, *args[6:], B.make_opts(act8=1), 0) == B.MOE_ERR_SHAPE
+    with pytest.raises(ValueError):
+        B.make_opts(helper_events=[A])
 
 
 def test_dequant_host_checks(lib):

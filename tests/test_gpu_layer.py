@@ -25,8 +25,20 @@ def _run(torch, ls, fused=True):
     torch.cuda.synchronize()
     out = dict(y=b.y.cpu().numpy(), ids=b.ids.cpu().numpy(), w=b.weights.cpu().numpy(),
                logits=b.logits.cpu().numpy(), hdr=b.header(),
-               num_active=int(b.num_active.item()))
+               num_active=int(b.num_active.item()), offsets=b.offsets.cpu().numpy(),
+               pairs=b.pairs.cpu().numpy(), active=b.active.cpu().numpy())
     return out, d, b
+
+
+def assert_sort_outputs(g, E, what):
+    """The layer's sort outputs (expert_offsets, sorted_pairs, the first D
+    entries of active_experts, num_active) are exactly the stable sort of the
+    layer's own routing: the oracle's sort_by_expert of the ids it wrote."""
+    offsets, pairs, active, D = oracle.sort_by_expert(g["ids"], E)
+    assert g["num_active"] == D, f"{what}: num_active {g['num_active']} != {D}"
+    assert np.array_equal(g["offsets"], offsets), f"{what}: expert_offsets differ"
+    assert np.array_equal(g["pairs"], pairs), f"{what}: sorted_pairs differ"
+    assert np.array_equal(g["active"][:D], active), f"{what}: active_experts differ"
 
 
 def _check_full(torch, ls, what, fused=True):
@@ -42,8 +54,12 @@ def _check_full(torch, ls, what, fused=True):
     keep = np.setdiff1d(np.arange(wl.M), amb)
     rms = float(np.sqrt(np.mean(r["y"] ** 2)))
     assert_layer_close(g["y"][keep], r["y"][keep], rms, what)
+    assert_sort_outputs(g, wl.E, what)
     if not amb:
+        # the routing is the oracle's, so the sort outputs are the oracle's too
         assert g["num_active"] == r["num_active"]
+        assert np.array_equal(g["offsets"], r["offsets"]) and np.array_equal(g["pairs"], r["sorted_pairs"])
+        assert np.array_equal(g["active"][:r["num_active"]], r["active"])
         assert_paths(g["hdr"], wl, r["ids"], what)
     assert len(amb) <= max(1, wl.M // 50), f"{what}: {len(amb)} ambiguous tokens"
     return g, r
@@ -87,23 +103,105 @@ def test_edge_shapes_every_element(M, H, I, E, k, shared, routing):
     _check_full(torch, ls, wl.name, fused=False)
 
 
-@pytest.mark.parametrize("name,sets", [("ling_m1", [0, 17]), ("ling_m4_mtp", [0, 39])])
+@pytest.mark.parametrize("name,sets", [("ling_m1", [0, 13, 26, 39]), ("ling_m4_mtp", [0, 13, 26, 39])])
 def test_ling_decode_full_size(name, sets):
+    """Every element of y at full size on four layer sets, alternating the two
+    entry routes (moe_layer and the three calls)."""
     torch = need_gpu()
     for i, l in enumerate(sets):
-        _check_full(torch, synth.layer_set(name, l), f"{name}/set{l}", fused=(i == 0))
+        _check_full(torch, synth.layer_set(name, l), f"{name}/set{l}", fused=(i % 2 == 0))
 
 
-@pytest.mark.parametrize("name,tokens", [("ling_m32_zipf", [0, 5, 17, 31]),
-                                         ("ling_m512_prefill", [0, 101, 333, 511])])
-def test_ling_batch_sampled_tokens(name, tokens):
-    """Full-size batch on the GPU; the oracle recomputes sampled tokens one by
-    one (tokens do not interact).  rms(ref) is estimated on the sample."""
+@pytest.mark.parametrize("name", ["ling_m1", "ling_m4_mtp"])
+def test_ling_decode_routing_every_set(name):
+    """Routing and sort of moe_layer on all 40 layer sets of a decode workload:
+    ids, weights and logits by the oracle's rule, and expert_offsets,
+    sorted_pairs, active_experts and num_active exactly.  Routing does not
+    depend on the expert banks, so one random bank on the device serves all
+    sets (each set's x, router and bias are its own)."""
+    torch = need_gpu()
+    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer, to_device
+    wl = synth.WORKLOADS[name]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(97 + wl.M)
+    u8 = dict(dtype=torch.uint8, device="cuda", generator=g)
+    n, H, I = wl.E + 1, wl.H, wl.I
+    bank = (torch.randint(0, 256, (n, 2 * I, H // 2), **u8), torch.randint(120, 128, (n, 2 * I, H // 32), **u8),
+            torch.randint(0, 256, (n, H, I // 2), **u8), torch.randint(120, 128, (n, H, I // 32), **u8))
+    b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
+    amb_total = 0
+    for l in range(wl.sets):
+        ls = synth.layer_set(wl, l, banks=False)
+        say(f"routing {name}/set{l}")
+        d = DeviceLayerSet(to_device(ls.x_bits), to_device(ls.w_router), to_device(ls.bias), ls.bias_row_stride,
+                           *bank, wl.M, H, I, wl.E, wl.k, wl.shared)
+        run_layer(d, b)
+        torch.cuda.synchronize()
+        gout = dict(ids=b.ids.cpu().numpy(), w=b.weights.cpu().numpy(), logits=b.logits.cpu().numpy(),
+                    num_active=int(b.num_active.item()), offsets=b.offsets.cpu().numpy(),
+                    pairs=b.pairs.cpu().numpy(), active=b.active.cpu().numpy())
+        xf = oracle.bf16_bits_to_f64(ls.x_bits)
+        ref_logits = oracle.router_logits(xf, ls.w_router, ls.bias)
+        bound = logit_error_bound(xf, ls.w_router, ls.bias, H, wl.M)
+        amb = check_routing(gout["ids"], gout["w"], gout["logits"], ref_logits, bound, wl.k, f"{name}/set{l}")
+        amb_total += len(amb)
+        assert_sort_outputs(gout, wl.E, f"{name}/set{l}")
+        if not amb:
+            ref_ids, _ = oracle.topk_softmax(ref_logits, wl.k)
+            offsets, pairs, active, D = oracle.sort_by_expert(ref_ids, wl.E)
+            assert np.array_equal(gout["pairs"], pairs) and gout["num_active"] == D
+        assert_paths(b.header(), wl, gout["ids"], f"{name}/set{l}")
+    assert amb_total <= 2, f"{name}: {amb_total} ambiguous tokens over {wl.sets} sets"
+
+
+def _batch_sample(ids, wl):
+    """At least 32 tokens of a batch for the token-by-token oracle: for M <= 32
+    every token; otherwise four tokens from each 64-token tile of the batch,
+    chosen so that every tile has a token routed to an expert on each path the
+    layer runs (scaled MFMA: >= 16 tokens; few-token matrix cores: 3..15;
+    GEMV: 1..2), then the tile's first tokens."""
+    if wl.M <= 32:
+        return list(range(wl.M))
+    counts = np.bincount(ids.ravel(), minlength=wl.E)
+    cls = np.select([counts >= 16, counts >= 3, counts >= 1], [2, 1, 0], -1)
+    tokens = []
+    for t0 in range(0, wl.M, 64):
+        tile = list(range(t0, min(t0 + 64, wl.M)))
+        pick = []
+        for c in (2, 1, 0):
+            for t in tile:
+                if t not in pick and np.any(cls[ids[t]] == c):
+                    pick.append(t)
+                    break
+        for t in tile:
+            if len(pick) >= 4:
+                break
+            if t not in pick:
+                pick.append(t)
+        tokens += sorted(pick)
+    return tokens
+
+
+@pytest.mark.parametrize("name", ["ling_m32_zipf", "ling_m512_prefill"])
+def test_ling_batch_sampled_tokens(name):
+    """Full-size batch on the GPU; the oracle recomputes the sampled tokens one
+    by one (tokens do not interact): all 32 tokens of the M = 32 batch, and 32
+    tokens over all eight 64-token tiles of the M = 512 batch, covering tokens
+    routed to GEMV, few-token and scaled-MFMA experts.  rms(ref) is taken over
+    the sample."""
     torch = need_gpu()
     ls = synth.layer_set(name, 0)
     wl = ls.wl
-    say(f"layer {name}: M={wl.M} sampled {tokens}")
+    say(f"layer {name}: M={wl.M}")
     g, _, _ = _run(torch, ls)
+    tokens = _batch_sample(g["ids"], wl)
+    assert len(tokens) >= 32
+    if wl.M > 32:
+        counts = np.bincount(g["ids"].ravel(), minlength=wl.E)
+        per_path = [int(np.sum([np.any(np.isin(g["ids"][t], np.nonzero(sel)[0])) for t in tokens]))
+                    for sel in (counts >= 16, (counts >= 3) & (counts < 16), (counts >= 1) & (counts <= 2))]
+        assert all(c > 0 for c in per_path), f"{name}: sampled tokens per path {per_path}"
+    say(f"oracle over {len(tokens)} tokens of {name}")
     r = oracle.moe_layer_tokens(tokens, ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s,
                                 ls.w2_q, ls.w2_s, wl.k, wl.shared)
     xf = oracle.bf16_bits_to_f64(ls.x_bits[tokens])
@@ -116,8 +214,7 @@ def test_ling_batch_sampled_tokens(name, tokens):
     assert_layer_close(g["y"][tokens][keep], r["y"][keep], rms, name)
     # every token's output is finite and the dedup covers every routed pair
     assert np.all(np.isfinite(g["y"]))
-    D = len(np.unique(g["ids"]))
-    assert g["num_active"] == D
+    assert_sort_outputs(g, wl.E, name)
     assert_paths(g["hdr"], wl, g["ids"], name)
 
 
@@ -151,23 +248,27 @@ def test_down_scale_doubling_doubles_output():
     assert np.all(np.abs(g2["y"] - 2 * g["y"]) <= 1e-5 * (np.abs(2 * g["y"]) + 2 * rms))
 
 
+@pytest.mark.parametrize("helpers", [True, False])
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("M,E", [(24, 10), (96, 24)])
-def test_graph_replays_match_eager(fused, M, E):
+def test_graph_replays_match_eager(fused, M, E, helpers):
     """A HIP graph of the layer (as bench.py replays it) gives the eager result
     on every replay.  The layers have GEMV, few-token and scaled-MFMA experts, so
-    the graph holds the helper streams' fork and join (M = 96 also combines by
-    rows: partial rows per pair, then the combine kernel); eager work and host
-    synchronisations run between the replays."""
+    with the caller's helper streams (two torch streams and four events) the
+    graph holds their fork and join; without them every kernel is on the one
+    stream (M = 96 also combines by rows: partial rows per pair, then the
+    combine kernel); eager work and host synchronisations run between the
+    replays."""
     torch = need_gpu()
-    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, LayerBuffers, run_layer
+    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, HelperStreams, LayerBuffers, run_layer
     wl = synth.custom(f"graph{M}x512x512", M, 512, 512, E, 3, True, "zipf", seed=1048 + M)
     ls = synth.layer_set(wl)
-    say(f"graph replay {wl.name} {'moe_layer' if fused else 'three calls'}")
+    say(f"graph replay {wl.name} {'moe_layer' if fused else 'three calls'} helpers={helpers}")
     d = DeviceLayerSet.from_host(ls)
     b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
     w = d.weights()
-    run_layer(d, b, w, fused=fused)
+    hs = HelperStreams() if helpers else None
+    run_layer(d, b, w, fused=fused, helpers=hs)
     torch.cuda.synchronize()
     eager = b.y.clone()
     hdr = b.header()
@@ -175,12 +276,12 @@ def test_graph_replays_match_eager(fused, M, E):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        run_layer(d, b, w, fused=fused)
+        run_layer(d, b, w, fused=fused, helpers=hs)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        run_layer(d, b, w, fused=fused)
+        run_layer(d, b, w, fused=fused, helpers=hs)
     rms = float(eager.pow(2).mean().sqrt())
     for rep in range(4):
         b.y.fill_(float("nan"))
@@ -188,5 +289,5 @@ def test_graph_replays_match_eager(fused, M, E):
         torch.cuda.synchronize()
         diff = (b.y - eager).abs()
         assert bool(torch.all(diff <= 1e-5 * (eager.abs() + rms))), f"replay {rep}: max diff {float(diff.max())}"
-        run_layer(d, b, w, fused=fused)            # eager work between replays
+        run_layer(d, b, w, fused=fused, helpers=hs)            # eager work between replays
         torch.cuda.synchronize()
