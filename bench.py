@@ -410,6 +410,8 @@ def main():
                     help="before each layer, N small elementwise kernels on a 256 KB tensor that stays in "
                          "L2: a stand-in for the non-MoE work between two layers that leaves HBM idle "
                          "(with --prefetch, each layer's own experts are prefetched during it)")
+    ap.add_argument("--phases", action="store_true",
+                    help="the decode path's per-workgroup phase timestamps (moe_layer_probe) instead of the bench")
     ap.add_argument("--single", action="store_true",
                     help="ling_m1 alone (the default run also measures ling_m4_mtp into the same line)")
     ap.add_argument("--three-calls", action="store_true",
@@ -454,6 +456,9 @@ def main():
         return
 
     wl = synth.WORKLOADS[args.workload]
+    if args.phases:
+        phase_table(torch, binding, synth, args, wl)
+        return
     out = bench_moe(torch, binding, synth, args, wl, cpu=not args.no_cpu_baseline)
     if args.workload == "ling_m1" and not args.single and not (args.hint is not None or args.prefetch is not None
                                                               or args.gap_kernels or args.three_calls):
@@ -467,6 +472,55 @@ def main():
         out["ling_m4_mtp"] = {k: m4[k] for k in keep if k in m4}
         out["t_m4_over_t_m1"] = m4["us_per_layer"] / out["us_per_layer"]
     print(json.dumps(out), flush=True)
+
+
+def phase_table(torch, binding, synth, args, wl):
+    """Where a decode layer's time goes: moe_layer_probe's per-workgroup
+    timestamps (100 MHz) over --steps layers run back to back on the rotating
+    sets, each workgroup's phases in microseconds from its gate/up kernel's
+    first workgroup start.  Prints one JSON line."""
+    import statistics
+
+    from mxfp4_expert_weight_amd.layer import LayerBuffers
+    nsets = args.sets or wl.sets
+    sets = device_sets(torch, wl, nsets)
+    buf = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
+    n = binding.moe_layer_probe_stamps(wl.M, wl.k, wl.E, wl.H, wl.I)
+    assert n > 0, "the decode path does not cover this workload"
+    steps = max(args.steps, 1)
+    stamps = torch.zeros((steps, n), dtype=torch.int64, device="cuda")
+    for i in range(steps):
+        d = sets[i % nsets]
+        binding.moe_layer_probe(d.x, d.w_router, d.bias, d.bias_row_stride, d.weights(), d.M, d.k, buf.logits,
+                                buf.ids, buf.weights, buf.offsets, buf.pairs, buf.active, buf.num_active, buf.y,
+                                buf.ws, buf.ws_bytes, stamps[i], n)
+    torch.cuda.synchronize()
+    st = stamps.cpu().numpy().reshape(steps, -1, 16).astype("float64") / 100.0   # 100 MHz ticks -> us
+    names = ["gate/up start", "logits loaded", "top-k threshold", "top-k done", "routing barrier",
+             "slot known", "weights issued", "first weights used", "h written",
+             "down start", "record loaded", "down loads issued", "down first weights", "down done",
+             "unused 14", "unused 15"]
+    rows = {k: [] for k in names}
+    ends = {"gate/up last start": [], "gate/up end": [], "down first start": [], "down end": []}
+    for s_ in st:
+        t0 = s_[:, 0][s_[:, 0] > 0].min()
+        for j, k in enumerate(names):
+            v = s_[:, j][s_[:, j] > 0] - t0
+            rows[k].append((statistics.median(v), float(v.max())) if len(v) else (None, None))
+        gs = s_[:, 0][s_[:, 0] > 0] - t0
+        ends["gate/up last start"].append(float(gs.max()))
+        ends["gate/up end"].append(float((s_[:, 8][s_[:, 8] > 0] - t0).max()))
+        ends["down first start"].append(float((s_[:, 9][s_[:, 9] > 0] - t0).min()))
+        ends["down end"].append(float((s_[:, 13][s_[:, 13] > 0] - t0).max()))
+    table = {k: {"median_us": statistics.median([m for m, _ in v if m is not None]),
+                 "max_us": statistics.median([x for _, x in v if x is not None])}
+             for k, v in rows.items() if any(m is not None for m, _ in v)}
+    for k, v in ends.items():
+        table[k] = {"median_us": statistics.median(v)}
+    for k, v in table.items():
+        log(f"[phases] {wl.name} {k:20s} " + " ".join(f"{a}={b:.2f}" for a, b in v.items()))
+    print(json.dumps({"workload": wl.name, "layers": steps, "phases_from_gateup_start_us": table,
+                      "what": "median over layers of the median (max) over workgroups"}), flush=True)
 
 
 def bench_moe(torch, binding, synth, args, wl, cpu=True, cpu_budget=10.0, one_thread=True):

@@ -210,6 +210,30 @@ moe_status moe_layer_ex(const uint16_t* x, const float* w_router, const float* l
                         int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                         void* workspace, size_t workspace_bytes, const moe_exec_opts* opts, void* stream);
 
+/* Measurement hook of the decode path (M <= 4, H = 2560, I = 768): moe_layer
+ * with kernel instances that also write phase timestamps (the GPU's 100 MHz
+ * constant clock, s_memrealtime) of thread 0 of every workgroup: per
+ * workgroup index w = y * gridDim.x + x of each kernel's own grid,
+ *   stamps[16w + 0..8]:  gate/up kernel entry, token 0's logits loaded, its
+ *                        top-k threshold, its top-k done, the workgroup's
+ *                        routing barrier passed, slot known, weight loads
+ *                        issued, first weight block used, h written;
+ *   stamps[16w + 9..13]: down kernel entry, record loaded, loads issued,
+ *                        first weight block used, y added.
+ * Stamps a workgroup does not reach keep their prior value.  Results are those
+ * of moe_layer.
+ *   stamps      device uint64 [num_stamps], 8-byte aligned
+ *   num_stamps  >= moe_layer_probe_stamps(M, top_k, E, H, I)
+ * MOE_ERR_SHAPE for sizes the decode path does not cover (the helper returns 0
+ * for them) or a short buffer. */
+size_t moe_layer_probe_stamps(int32_t M, int32_t top_k, int32_t E, int32_t H, int32_t I);
+moe_status moe_layer_probe(const uint16_t* x, const float* w_router, const float* logit_bias,
+                           int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                           void* workspace, size_t workspace_bytes, unsigned long long* stamps,
+                           size_t num_stamps, void* stream);
+
 /* moe_layer with a hint from a draft pass (speculative decoding predicts the
  * experts of the coming tokens: MoE-SpeQ article, 4.1).  Same arguments,
  * outputs and limits as moe_layer, plus two timing events of the gate/up

@@ -208,7 +208,8 @@ moe_status layer_impl(const uint16_t* x, const float* w_router, const float* log
                       float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
                       int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                       void* workspace, size_t workspace_bytes_, const moe_exec_opts* opts, void* stream,
-                      const int32_t* hint = nullptr, const int32_t* num_hint = nullptr) {
+                      const int32_t* hint = nullptr, const int32_t* num_hint = nullptr,
+                      unsigned long long* probe = nullptr) {
   if (!x || !w_router || !w || !logits || !topk_ids || !topk_weights || !expert_offsets ||
       !sorted_pairs || !active_experts || !num_active || !y || !workspace)
     return MOE_ERR_NULL;
@@ -235,8 +236,14 @@ moe_status layer_impl(const uint16_t* x, const float* w_router, const float* log
     // decode: every gate/up block routes itself from the logits
     const RouteOut r{logits, topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts,
                      num_active, rec, expert_bits(E)};
+    if (!hint && decode_fast_fits(M, H, w->inter)) {
+      a.probe = probe;
+      return hip_status(launch_decode(a, r, s, timing_of(opts), probe != nullptr));
+    }
+    if (probe) return MOE_ERR_SHAPE;               // the stamping instances exist for the decode path only
     return hip_status(launch_forward_routed(a, r, s, timing_of(opts)));
   }
+  if (probe) return MOE_ERR_SHAPE;
   if (topk_sort_fits_one_block(M)) a.lists = nullptr;   // the one-workgroup sort writes records only
   const RecOut ro = layer_recout(a, workspace);
   hipError_t e;
@@ -390,6 +397,28 @@ moe_status moe_layer_hinted(const uint16_t* x, const float* w_router, const floa
   return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
                     expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
                     &o, stream, hint_experts, num_hint);
+}
+
+size_t moe_layer_probe_stamps(int32_t M, int32_t top_k, int32_t E, int32_t H, int32_t I) {
+  if (check_route_sizes(M, E, top_k) != MOE_OK || check_hidden(H) != MOE_OK || check_inter(I) != MOE_OK ||
+      M > kRoutedMaxTokens || !decode_fast_fits(M, H, I))
+    return 0;
+  return decode_probe_stamps(M, top_k, E, H, I, 1);
+}
+
+moe_status moe_layer_probe(const uint16_t* x, const float* w_router, const float* logit_bias,
+                           int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                           float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                           int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                           void* workspace, size_t workspace_bytes_, unsigned long long* stamps, size_t num_stamps,
+                           void* stream) {
+  if (!stamps || !w) return MOE_ERR_NULL;
+  if (((uintptr_t)stamps & 7u)) return MOE_ERR_ALIGN;
+  const size_t need = moe_layer_probe_stamps(M, top_k, w->num_experts, w->hidden, w->inter);
+  if (need == 0 || num_stamps < need) return MOE_ERR_SHAPE;
+  return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
+                    expert_offsets, sorted_pairs, active_experts, num_active, y, workspace, workspace_bytes_,
+                    nullptr, stream, nullptr, nullptr, stamps);
 }
 
 moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logit_bias,

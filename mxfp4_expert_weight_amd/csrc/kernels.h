@@ -70,6 +70,8 @@ struct ForwardArgs {
   // gate/up kernel, whose idle waves touch the hinted rows during the routing.
   const int* hint;
   const int* num_hint;
+  // Phase stamps of the decode kernels' measurement instances (null otherwise).
+  unsigned long long* probe;
 };
 
 // The few-token matrix-core path (mt.hip): batches of more than
@@ -204,6 +206,13 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, const Timing& tm 
 // this many elements are rounded to MXFP8 as the kernel stages x (a.x is the
 // bf16 x); longer rows need a.x to hold the MXFP8 values already.
 bool routed_stages_x(int H);
+// The decode path of decode.hip (M <= kRoutedMaxTokens, the shapes it is
+// built for): routed gate/up kernel with 128-bit loads, then down; with
+// `probe`, the instances that stamp each workgroup's phases into a.probe.
+bool decode_fast_fits(int M, int H, int I);
+// Stamps the measurement instances write: 8 per workgroup of the larger grid.
+size_t decode_probe_stamps(int M, int k, int E, int H, int I, int has_shared);
+hipError_t launch_decode(const ForwardArgs& a, const RouteOut& r, hipStream_t s, const Timing& tm, bool probe);
 hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s,
                                  const Timing& tm = Timing{});
 // MFMA path (mfma.hip): two-term MXFP8 quantisation of x, the dense gate/up

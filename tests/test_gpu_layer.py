@@ -291,3 +291,67 @@ def test_graph_replays_match_eager(fused, M, E, helpers):
         assert bool(torch.all(diff <= 1e-5 * (eager.abs() + rms))), f"replay {rep}: max diff {float(diff.max())}"
         run_layer(d, b, w, fused=fused, helpers=hs)            # eager work between replays
         torch.cuda.synchronize()
+
+
+# The decode path of moe_layer for the Ling expert shapes (H = 2560, I = 768,
+# M <= 4): in-block routing by threshold and rank, records in first-pair
+# order, 128-bit weight streams.  Edge cases of that path: E and k at their
+# extremes (two pairs per lane at 128 pairs, 16 experts per lane of the
+# top-k), no shared expert (record 0 empty), k = E with every token on every
+# expert, k = 1.
+@pytest.mark.parametrize("M,E,k,shared,routing", [
+    (1, 16, 2, True, "plain"),
+    (2, 40, 8, False, "overlap"),
+    (3, 600, 9, True, "plain"),
+    (4, 1024, 32, True, "plain"),
+    (4, 8, 8, True, "overlap"),
+    (2, 512, 1, True, "plain"),
+    (4, 512, 8, False, "overlap"),
+])
+def test_decode_path_edge_shapes(M, E, k, shared, routing):
+    torch = need_gpu()
+    wl = synth.custom(f"dec{M}x{E}x{k}", M, 2560, 768, E, k, shared, routing, seed=7 * M + E + k)
+    ls = synth.layer_set(wl)
+    _check_full(torch, ls, wl.name, fused=True)
+
+
+def _tied_router_layer(M, E, k, levels, seed):
+    """A decode layer whose logits are exact small integers with many ties:
+    x[t][0] = 1 and every other x 0 contributes nothing to the router (its
+    weights are 0 outside column 0), and expert e's column-0 weight is
+    levels(e).  All other inputs are the workload's random ones."""
+    wl = synth.custom(f"tied{M}x{E}x{k}", M, 2560, 768, E, k, True, "plain", seed=seed)
+    ls = synth.layer_set(wl)
+    x = oracle.bf16_bits_to_f64(ls.x_bits).astype(np.float32)
+    x[:, 0] = 1.0
+    ls.x_bits = synth.f32_to_bf16_bits(x)
+    w = np.zeros((E, 2560), np.float32)
+    w[:, 0] = [levels(e) for e in range(E)]
+    ls.w_router = w
+    return ls
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_decode_path_exact_ties(M):
+    """Exact logit ties inside the top-k: 16 experts share each integer level
+    (64 candidates reach the threshold and are ranked with the lower-index
+    rule), and a router of zeros (every logit 0: more than 64 candidates, so
+    the round-based top-k takes over), which picks experts 0..k-1 with weight
+    1/k.  The logits are exact in fp32 (integer products, zero elsewhere), so
+    they, the ids and the sort outputs must equal the oracle's exactly."""
+    torch = need_gpu()
+    for what, levels in (("tied levels", lambda e: float((e // 16) % 32)), ("zero router", lambda e: 0.0)):
+        ls = _tied_router_layer(M, 512, 8, levels, seed=11 + M)
+        wl = ls.wl
+        say(f"decode path {what} M={M}")
+        g, _, _ = _run(torch, ls)
+        r = oracle.moe_layer(ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s, ls.w2_q, ls.w2_s, wl.k, wl.shared)
+        assert np.array_equal(g["logits"].astype(np.float64), r["logits"]), what
+        assert np.array_equal(g["ids"], r["ids"]), (what, g["ids"], r["ids"])
+        assert np.allclose(g["w"], r["weights"], rtol=0, atol=1e-6), what
+        assert_sort_outputs(g, wl.E, what)
+        assert np.array_equal(g["pairs"], r["sorted_pairs"]) and g["num_active"] == r["num_active"]
+        rms = float(np.sqrt(np.mean(r["y"] ** 2)))
+        assert_layer_close(g["y"], r["y"], rms, what)
+        if what == "zero router":
+            assert np.array_equal(g["ids"], np.tile(np.arange(8, dtype=np.int32), (M, 1)))
