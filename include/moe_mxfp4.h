@@ -201,6 +201,26 @@ moe_status moe_layer(const uint16_t* x, const float* w_router, const float* logi
                      int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same call without the workspace arguments.  Its workspace is a static
+ * device array of MOE_NOALLOC_WORKSPACE_BYTES inside the library, one per GPU
+ * (held until the process ends), found with hipGetSymbolAddress on the first
+ * call on each device; the call allocates nothing.  Every call on a GPU shares
+ * that GPU's array, and it keeps the last call's contents (the layer ignores
+ * them on entry): calls that overlap on one GPU -- on different streams, or
+ * from different host threads -- race and must not be made.
+ * Same arguments, outputs and limits as moe_layer, plus:
+ * moe_workspace_bytes(M, k, E, H, I) <= MOE_NOALLOC_WORKSPACE_BYTES, else
+ * MOE_ERR_WORKSPACE (the Ling layer, H = 2560 and I = 768 with 512 experts
+ * top-8, fits up to M = 57). */
+#define MOE_NOALLOC_WORKSPACE_BYTES (8u << 20)
+moe_status moe_layer_noalloc(const uint16_t* x, const float* w_router, const float* logit_bias,
+                             int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                             float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                             int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                             void* stream);
+
 /* moe_layer with execution options (moe_exec_opts: the W4A8 variant, helper
  * streams for batches, timing events of the gate/up and down kernels).  Same
  * arguments, outputs and limits as moe_layer; opts may be NULL (= moe_layer). */

@@ -85,6 +85,8 @@ _SIGNATURES = {
                                             _P, _P, _P, _P, _P, _SZ, ctypes.POINTER(moe_exec_opts), _P]),
     "moe_layer_ex": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P, _P,
                                     _P, _P, _P, _P, _P, _P, _P, _SZ, ctypes.POINTER(moe_exec_opts), _P]),
+    "moe_layer_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P,
+                                         _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_layer_probe_stamps": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "moe_layer_probe": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P, _P,
                                        _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
@@ -224,6 +226,19 @@ def moe_mxfp4_forward_ex(x, w: moe_mxfp4_weights, M, top_k, topk_weights, expert
                                       _ptr(active_experts), _ptr(num_active), _ptr(y), _ptr(workspace),
                                       workspace_bytes, ctypes.byref(opts) if opts is not None else None,
                                       _stream(stream)), "moe_mxfp4_forward_ex")
+
+
+NOALLOC_WORKSPACE_BYTES = 8 << 20      # MOE_NOALLOC_WORKSPACE_BYTES
+
+
+def moe_layer_noalloc(x, w_router, logit_bias, bias_row_stride, w: moe_mxfp4_weights, M, top_k, logits,
+                      topk_ids, topk_weights, expert_offsets, sorted_pairs, active_experts, num_active, y,
+                      stream=None):
+    _check(lib().moe_layer_noalloc(_ptr(x), _ptr(w_router), _ptr(logit_bias), bias_row_stride,
+                                   ctypes.byref(w) if w is not None else None, M, top_k, _ptr(logits),
+                                   _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_offsets), _ptr(sorted_pairs),
+                                   _ptr(active_experts), _ptr(num_active), _ptr(y), _stream(stream)),
+           "moe_layer_noalloc")
 
 
 def moe_layer_probe_stamps(M, top_k, E, H, I) -> int:

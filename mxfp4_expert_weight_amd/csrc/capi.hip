@@ -2,11 +2,18 @@
 // Nothing here allocates device memory, synchronises or keeps state between
 // calls; streams and events other than the caller's `stream` come from the
 // caller (moe_exec_opts).
+#include <atomic>
 #include <climits>
 
 #include "kernels.h"
 
 using namespace moe;
+
+// Workspace of moe_layer_noalloc: one array per GPU, held until the process
+// ends.  On the host, `scratch` names a stand-in, not a device address: host
+// code only ever passes the address hipGetSymbolAddress returns for it.
+constexpr size_t kNoAllocScratchBytes = size_t(MOE_NOALLOC_WORKSPACE_BYTES);
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -297,9 +304,52 @@ moe_status forward_impl(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M
   return hip_status(launch_experts(a, s, opts));
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status moe_layer_noalloc(const uint16_t* x, const float* w_router, const float* logit_bias,
+                             int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
+                             float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                             int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
+                             void* stream) {
+  // every host check first (nothing touches the device for a rejected call)
+  if (!x || !w_router || !w || !logits || !topk_ids || !topk_weights || !expert_offsets || !sorted_pairs ||
+      !active_experts || !num_active || !y)
+    return MOE_ERR_NULL;
+  moe_status st = check_bank(w);
+  if (st != MOE_OK) return st;
+  if ((st = check_route_sizes(M, w->num_experts, top_k)) != MOE_OK) return st;
+  if (logit_bias && bias_row_stride != 0 && bias_row_stride != w->num_experts) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_ALIGN;
+  const size_t need = workspace_layout(M, top_k, w->num_experts, w->hidden, w->inter).total;
+  if (need > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return layer_impl(x, w_router, logit_bias, bias_row_stride, w, M, top_k, logits, topk_ids, topk_weights,
+                    expert_offsets, sorted_pairs, active_experts, num_active, y, ws, kNoAllocScratchBytes, nullptr,
+                    stream);
+}
 
 const char* moe_status_string(moe_status st) {
   switch (st) {

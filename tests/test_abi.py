@@ -113,6 +113,28 @@ def test_layer_host_checks(lib, name):
     assert _status(f, *(args[:16] + [ws - 1, 0])) == B.MOE_ERR_WORKSPACE
 
 
+def test_noalloc_layer_host_checks(lib):
+    """moe_layer_noalloc: the moe_layer checks, then the layer's workspace must
+    fit the library's static array (8 MiB: the Ling layer up to M = 57), else
+    MOE_ERR_WORKSPACE -- all before the device is touched."""
+    assert B.NOALLOC_WORKSPACE_BYTES == 8 << 20
+    w = B.make_weights(A, A, A, A, 512, 2560, 768, 1)
+    f = B.moe_layer_noalloc
+    args = [A, A, None, 0, w, 1, 8, A, A, A, A, A, A, A, A, 0]
+    assert _status(f, *([None] + args[1:])) == B.MOE_ERR_NULL
+    assert _status(f, *(args[:4] + [None] + args[5:])) == B.MOE_ERR_NULL
+    assert _status(f, *(args[:14] + [None, 0])) == B.MOE_ERR_NULL                 # y
+    assert _status(f, *(args[:5] + [0] + args[6:])) == B.MOE_ERR_SHAPE
+    assert _status(f, *(args[:2] + [A, 3] + args[4:])) == B.MOE_ERR_SHAPE         # bias stride
+    assert _status(f, *(args[:1] + [MIS] + args[2:])) == B.MOE_ERR_ALIGN
+    bad = B.make_weights(A, A, A, A, 512, 2560, 700, 1)
+    assert _status(f, *(args[:4] + [bad] + args[5:])) == B.MOE_ERR_SHAPE
+    assert B.moe_workspace_bytes(57, 8, 512, 2560, 768) <= B.NOALLOC_WORKSPACE_BYTES
+    assert B.moe_workspace_bytes(58, 8, 512, 2560, 768) > B.NOALLOC_WORKSPACE_BYTES
+    assert _status(f, *(args[:5] + [58] + args[6:])) == B.MOE_ERR_WORKSPACE
+    assert _status(f, *(args[:5] + [512] + args[6:])) == B.MOE_ERR_WORKSPACE
+
+
 def test_exec_opts_host_checks(lib):
     """moe_exec_opts: act8 in {0, 1}; helper streams come as a pair, with all
     four events (checked before anything is enqueued)."""
