@@ -34,6 +34,32 @@ namespace moe {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 ld128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Matrix-core operands (v_mfma_f32_16x16x32_bf16): lane l holds row (A) or
+// column (B) l % 16 and 8 consecutive K values of lane group l / 16; output
+// register i of lane l is D[4 (l / 16) + i][l % 16].  Only the pairing of A
+// and B values along K matters, so lane group kq of load i takes scale block
+// 4 i + kq of its row: one 16-byte load per lane is one whole MXFP4 block, a
+// row's four lanes read 64 contiguous bytes, and step m of the block is its
+// m-th 32-bit code word (8 elements).
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// One code word (8 E2M1 elements) times the block scale, as 8 bf16 (exact).
+__device__ __forceinline__ v8bf mxfp4_word_bf16x8(uint32_t w, float scale) {
+  const bf16x2 p0 = mxfp4_pair_bf16<0>(w, scale), p1 = mxfp4_pair_bf16<1>(w, scale);
+  const bf16x2 p2 = mxfp4_pair_bf16<2>(w, scale), p3 = mxfp4_pair_bf16<3>(w, scale);
+  v8bf v;
+  v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+  v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+  return v;
+}
+
+// The value a lane's partner in the other half of the wave (l ^ 32) holds.
+__device__ __forceinline__ float half_partner(float v) {
+  const Pair p = swap32(__float_as_uint(v));
+  return __uint_as_float(p.a == __float_as_uint(v) ? p.b : p.a);   // equal values: either copy
+}
+
 constexpr int DC_THREADS = 256;                 // 4 waves per workgroup (both kernels)
 constexpr int DC_WAVES = DC_THREADS / kWave;
 constexpr int DC_MAXP = kRoutedMaxTokens * MOE_MAX_TOPK;   // pairs of a decode batch (128)
@@ -317,15 +343,21 @@ __device__ __forceinline__ float dot_block(const u32x4& c, float scale, const u3
 // token loop, not hoisted out of it into many live registers.  No instruction.
 __device__ __forceinline__ void keep_in_loop(u32x4& v) { asm volatile("" : "+v"(v)); }
 
-// Roles of the gate/up grid rows: [shared row] [R routed rows] [writer row].
+// Roles of the gate/up grid rows: [shared row] [writer row] [R routed rows]
+// (the writer is dispatched early: its loads then go out before the weight
+// stream fills the memory queues).
 // C: experts per lane of the top-k; NB: H / 512; Q: quads of row pairs per
 // wave (a workgroup covers 16 Q intermediate indices); A8: W4A8 (x rounded to
-// MXFP8 as it is staged).
-template <int C, int NB, int Q, bool A8, bool PROBE>
+// MXFP8 as it is staged); MF: the products on the matrix cores (Q = 2: a
+// wave's 8 gate and 8 up rows are the 16 rows of one tile, the slot's tokens
+// its columns), each weight decoded once for all of the slot's tokens;
+// otherwise per-token v_dot2 products.
+template <int C, int NB, int Q, bool A8, bool PROBE, bool MF>
 __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(Q >= 2 ? 3 : 4, Q >= 2 ? 3 : 4)))
 void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
   constexpr int KB = NB * 16;                      // 32-element blocks per row
   static_assert(Q >= 1 && Q <= 4, "quads");
+  static_assert(!MF || Q == 2, "a matrix-core wave covers 8 row pairs");
   using Lds = GateupLds<NB, Q>;
   static_assert(sizeof(SmallSortLds<C, DC_MAXP>) <= sizeof(Lds::x), "the writer's sort state fits the x area");
   __shared__ __align__(16) Lds L;
@@ -333,7 +365,7 @@ void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int M = a.M, k = a.k, E = a.E, H = a.H, I = a.I;
   const int srow = a.has_shared ? 1 : 0;
-  const bool writer = blockIdx.y == gridDim.y - 1;
+  const bool writer = blockIdx.y == srow;
   const bool shared_row = a.has_shared && blockIdx.y == 0;
   {                                                // every workgroup zeroes a share of y (down adds into it)
     const size_t nblk = (size_t)gridDim.x * gridDim.y;
@@ -361,6 +393,7 @@ void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
       a.hdr->mt_experts = 0;
       if (!a.has_shared) recs[0].e = -1;            // record 0 is the shared expert's
     }
+    stamp<PROBE>(a.probe, kGuDone);
     return;
   }
 
@@ -375,9 +408,9 @@ void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
   if (shared_row)
     shared_record(M, k, E, rec);
   else
-    routed_record(L.ids, L.w, L.owner, M, k, E, (int)blockIdx.y - srow, rec);
-  // record 0: the shared expert; record 1 + s: routed slot s (grid row srow + s)
-  if (blockIdx.x == 0 && lane == 0 && wave == 0) prec_store(&recs[shared_row ? 0 : (int)blockIdx.y - srow + 1], rec);
+    routed_record(L.ids, L.w, L.owner, M, k, E, (int)blockIdx.y - srow - 1, rec);
+  // record 0: the shared expert; record 1 + s: routed slot s (grid row srow + 1 + s)
+  if (blockIdx.x == 0 && lane == 0 && wave == 0) prec_store(&recs[shared_row ? 0 : (int)blockIdx.y - srow], rec);
   stamp<PROBE>(a.probe, kGuSlot);
   const int rec_e = prec_e(rec), rec_n = prec_n(rec);
   if (rec_e < 0) return;                            // no expert in this slot (uniform over the block)
@@ -415,16 +448,32 @@ void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
     sv[i] = ld128(ws + (size_t)row * row_s + col);
   }
   __builtin_amdgcn_sched_barrier(0);                // the scale loads go out before the code stream
-  u32x4 cg[Q][NB], cu[Q][NB];
+  // per-token products: lane (g, j) takes rows jb + 4q + g, blocks c * 16 + j;
+  // matrix cores: lane (r, kq) takes row r of the tile (gate rows jb .. jb + 7,
+  // then the same up rows), blocks 4 i + kq
+  constexpr int kMfLoads = MF ? KB / 4 : 1;
+  constexpr int kDotQ = MF ? 1 : Q, kDotNB = MF ? 1 : NB;
+  u32x4 cg[kDotQ][kDotNB], cu[kDotQ][kDotNB], cm[kMfLoads];
+  const int mr = lane & 15, kq = lane >> 4;
+  if constexpr (MF) {
+    const int idx = min(jb + (mr & 7), I - 1);
+    const uint8_t* rq = wq + (size_t)((mr >> 3) * I + idx) * row_q + kq * 16;
 #pragma unroll
-  for (int c = 0; c < NB; ++c)
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int idx = min(jb + 4 * q + g, I - 1);
-      cg[q][c] = ld128(wq + (size_t)idx * row_q + c * 256 + j * 16);
-      cu[q][c] = ld128(wq + (size_t)(I + idx) * row_q + c * 256 + j * 16);
+    for (int i = 0; i < kMfLoads; ++i) {
+      cm[i] = ld128(rq + i * 64);
       __builtin_amdgcn_sched_barrier(0);            // issued in the order the products consume them
     }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NB; ++c)
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int idx = min(jb + 4 * q + g, I - 1);
+        cg[q][c] = ld128(wq + (size_t)idx * row_q + c * 256 + j * 16);
+        cu[q][c] = ld128(wq + (size_t)(I + idx) * row_q + c * 256 + j * 16);
+        __builtin_amdgcn_sched_barrier(0);          // issued in the order the products consume them
+      }
+  }
   stamp<PROBE>(a.probe, kGuIssued);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -444,6 +493,50 @@ void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
   for (int i = 0; i < (kSVec + kWave - 1) / kWave; ++i)
     reinterpret_cast<u32x4*>(sl)[min(lane + i * kWave, kSVec - 1)] = sv[i];
   block_barrier_lds();                              // x and the scales staged; the codes stay in flight
+  if constexpr (MF) {
+    if (jb >= I) return;
+    // column c of the tile: the record's token c (columns past its tokens
+    // repeat token 0 and are not stored)
+    const int c = lane & 15;
+    const u32x4* xb = L.x + (size_t)((c < rec_n ? c : 0) * 4) * KB + kq;
+    const uint8_t* sb = sl + mr * KB + kq;
+    v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kMfLoads; ++i) {
+      const float sc = e8m0_to_f32(sb[4 * i]);
+#pragma unroll
+      for (int m = 0; m < 4; m += 2) {               // two accumulators: no chain of dependent products
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mxfp4_word_bf16x8(cm[i][m], sc),
+                                                       __builtin_bit_cast(v8bf, xb[m * KB + 4 * i]), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mxfp4_word_bf16x8(cm[i][m + 1], sc),
+                                                       __builtin_bit_cast(v8bf, xb[(m + 1) * KB + 4 * i]), acc1, 0,
+                                                       0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);            // one block's operands at a time
+      if (i == 0) stamp<PROBE>(a.probe, kGuFirstData);
+    }
+    // lanes 0..31 hold gate rows jb + 4 kq + e, lanes 32..63 the same up rows
+    float gv[4], uv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gv[e] = acc0[e] + acc1[e];
+      uv[e] = half_partner(gv[e]);
+    }
+    if (kq < 2 && c < rec_n) {
+      const size_t o = (size_t)prec_hrow(rec, c) * I + jb + 4 * kq;   // 4 consecutive h elements
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {                 // h = hi + lo, two bf16 terms
+        const float v = silu(gv[e]) * uv[e];
+        hi[e] = f32_to_bf16_bits(v);
+        lo[e] = f32_to_bf16_bits(v - bf16_bits_to_f32(hi[e]));
+      }
+      *reinterpret_cast<uint2*>(a.h + o) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      *reinterpret_cast<uint2*>(a.hlo + o) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+    }
+    stamp<PROBE>(a.probe, kGuDone);
+    return;
+  } else {
   // token n of the record; the first token is computed as the codes arrive,
   // later ones (multi-token experts) after an opaque barrier on the codes so
   // their decoding is redone per token rather than held in registers
@@ -500,6 +593,7 @@ void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
     token(n);
   }
   stamp<PROBE>(a.probe, kGuDone);
+  }
 }
 
 // --------------------------------------------------------------- down --
@@ -514,7 +608,11 @@ struct DownLds {
   uint8_t scales[DC_WAVES][8 * DN_RG][kBlocks];
 };
 
-template <int NBD, bool PROBE>
+// MF: the products on the matrix cores: a wave's 16 rows are the 16 rows of
+// one tile; column t < 4 is token t's hi term of h, column 7 - t its lo term
+// (so a half-row mirror adds the two), each weight decoded once for all
+// tokens.  Otherwise per-token v_dot2 products.
+template <int NBD, bool PROBE, bool MF>
 __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(6, 6)))
 void decode_down_kernel(ForwardArgs a) {
   constexpr int KB = NBD * 8;                      // blocks per row (I / 32)
@@ -555,15 +653,26 @@ void decode_down_kernel(ForwardArgs a) {
     sv[i] = ld128(ws + min(off, (size_t)H * row_s - 16));
   }
   __builtin_amdgcn_sched_barrier(0);                // h and the scales go out before the code stream
-  u32x4 c[DN_RG][NBD];
+  constexpr int kMfLoads = MF ? KB / 4 : 1;
+  u32x4 c[MF ? 1 : DN_RG][MF ? 1 : NBD], cm[kMfLoads];
+  const int mr = lane & 15, kq = lane >> 4;
+  if constexpr (MF) {                               // lane (mr, kq): row r0 + mr, blocks 4 i + kq
+    const uint8_t* rq = wq + (size_t)min(r0 + mr, H - 1) * row_q + kq * 16;
 #pragma unroll
-  for (int cc = 0; cc < NBD; ++cc)
-#pragma unroll
-    for (int rg = 0; rg < DN_RG; ++rg) {
-      const int row = min(r0 + 8 * rg + g8, H - 1);
-      c[rg][cc] = ld128(wq + (size_t)row * row_q + cc * 128 + j8 * 16);
+    for (int i = 0; i < kMfLoads; ++i) {
+      cm[i] = ld128(rq + i * 64);
       __builtin_amdgcn_sched_barrier(0);            // issued in the order the products consume them
     }
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < NBD; ++cc)
+#pragma unroll
+      for (int rg = 0; rg < DN_RG; ++rg) {
+        const int row = min(r0 + 8 * rg + g8, H - 1);
+        c[rg][cc] = ld128(wq + (size_t)row * row_q + cc * 128 + j8 * 16);
+        __builtin_amdgcn_sched_barrier(0);          // issued in the order the products consume them
+      }
+  }
   stamp<PROBE>(a.probe, kDnIssued);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -579,6 +688,45 @@ void decode_down_kernel(ForwardArgs a) {
     reinterpret_cast<u32x4*>(sl)[min(lane + i * kWave, kSVec - 1)] = sv[i];
   block_barrier_lds();                              // h staged; the weight codes stay in flight
   if (r0 >= H) return;
+  if constexpr (MF) {
+    const int col = lane & 15;
+    const bool lo_col = col >= 4 && col < 8;
+    const int tq = min(col < 4 ? col : (lo_col ? 7 - col : 0), rec_n - 1);
+    const u32x4* hb = L.h + (size_t)((tq * 2 + (lo_col ? 1 : 0)) * 4) * KB + kq;
+    const uint8_t* sb = sl + mr * KB + kq;
+    v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kMfLoads; ++i) {
+      const float sc = e8m0_to_f32(sb[4 * i]);
+#pragma unroll
+      for (int m = 0; m < 4; m += 2) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mxfp4_word_bf16x8(cm[i][m], sc),
+                                                       __builtin_bit_cast(v8bf, hb[m * KB + 4 * i]), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mxfp4_word_bf16x8(cm[i][m + 1], sc),
+                                                       __builtin_bit_cast(v8bf, hb[(m + 1) * KB + 4 * i]), acc1, 0,
+                                                       0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == 0) stamp<PROBE>(a.probe, kDnFirstData);
+    }
+    float v[4];                                     // rows r0 + 4 kq + e: hi + lo of token col
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = acc0[e] + acc1[e];
+      v[e] = d + __uint_as_float(dpp_half_mirror(__float_as_uint(d)));
+    }
+    if (col < rec_n) {
+      const int t = prec_tok(rec, col);
+      const float wt = prec_w(rec, col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = r0 + 4 * kq + e;
+        if (row < H) unsafeAtomicAdd(&a.y[(size_t)t * H + row], wt * v[e]);
+      }
+    }
+    stamp<PROBE>(a.probe, kDnDone);
+    return;
+  } else {
   auto token = [&](int n) __attribute__((always_inline)) {   // as in the gate/up kernel
 
     const int t = prec_tok(rec, n);
@@ -630,6 +778,7 @@ void decode_down_kernel(ForwardArgs a) {
     token(n);
   }
   stamp<PROBE>(a.probe, kDnDone);
+  }
 }
 
 // -------------------------------------------------------------- launch --
@@ -637,8 +786,9 @@ namespace {
 
 template <int C, int NB, int Q, bool PROBE>
 void* gateup_instance(bool a8) {
-  return a8 ? reinterpret_cast<void*>(decode_gateup_kernel<C, NB, Q, true, PROBE>)
-            : reinterpret_cast<void*>(decode_gateup_kernel<C, NB, Q, false, PROBE>);
+  constexpr bool MF = Q == 2;                       // batches of 2-4 tokens: matrix cores
+  return a8 ? reinterpret_cast<void*>(decode_gateup_kernel<C, NB, Q, true, PROBE, MF>)
+            : reinterpret_cast<void*>(decode_gateup_kernel<C, NB, Q, false, PROBE, MF>);
 }
 
 // Instances: H = 2560 (5 blocks of 512 per row) with I = 768 (3 blocks of
@@ -651,16 +801,19 @@ void* pick_gateup(int E, int H, int Q, bool a8) {
   return c8 ? gateup_instance<8, 5, 2, PROBE>(a8) : gateup_instance<16, 5, 2, PROBE>(a8);
 }
 
+// One token: per-token dot products (the matrix-core tile would be 1/16
+// used); 2-4 tokens: matrix cores.
 template <bool PROBE>
-void* pick_down(int I) {
+void* pick_down(int I, int M) {
   if (I != 768) return nullptr;
-  return reinterpret_cast<void*>(decode_down_kernel<3, PROBE>);
+  return M >= 2 ? reinterpret_cast<void*>(decode_down_kernel<3, PROBE, true>)
+                : reinterpret_cast<void*>(decode_down_kernel<3, PROBE, false>);
 }
 
 }  // namespace
 
 bool decode_fast_fits(int M, int H, int I) {
-  return M >= 1 && M <= kRoutedMaxTokens && pick_gateup<false>(512, H, 1, false) && pick_down<false>(I);
+  return M >= 1 && M <= kRoutedMaxTokens && pick_gateup<false>(512, H, 1, false) && pick_down<false>(I, M);
 }
 
 namespace {
@@ -683,9 +836,9 @@ size_t decode_probe_stamps(int M, int k, int E, int H, int I, int has_shared) {
 hipError_t launch_decode(const ForwardArgs& a, const RouteOut& r, hipStream_t s, const Timing& tm, bool probe) {
   const int Q = decode_quads(a.M);
   void* gu = probe ? pick_gateup<true>(a.E, a.H, Q, a.act8 != 0) : pick_gateup<false>(a.E, a.H, Q, a.act8 != 0);
-  void* dn = probe ? pick_down<true>(a.I) : pick_down<false>(a.I);
+  void* dn = probe ? pick_down<true>(a.I, a.M) : pick_down<false>(a.I, a.M);
   if (!gu || !dn) return hipErrorInvalidValue;
-  // gate/up rows: [shared] [routed slots] [writer]; down rows: the records
+  // gate/up rows: [shared] [writer] [routed slots]; down rows: the records
   const dim3 ggu = decode_gateup_grid(a.M, a.k, a.E, a.I, a.has_shared), bgu(DC_THREADS);
   const dim3 gdn = decode_down_grid(a.M, a.k, a.E, a.H), bdn(DC_THREADS);
   void* gu_args[] = {const_cast<ForwardArgs*>(&a), const_cast<RouteOut*>(&r)};
