@@ -107,19 +107,19 @@ struct TopkScratch {
   __align__(16) int oid[MOE_MAX_TOPK];
 };
 
-// Top-k of one token's logits by one full wave, ties to the lower expert
-// index, and the weights exp(l_i - l_max) / sum over the kept.  Threshold: the
-// lanes form groups of G (G = 4 for k <= 8, 2 for k <= 16, else 1); T = the
-// largest group maximum that at least k group maxima reach.  Those k maxima
-// are k distinct logits >= T, so the k-th largest logit is >= T and every
-// logit of the top-k is a candidate (logit >= T).  The candidates -- usually
-// k plus a few -- are compacted into LDS and each is ranked against all of
-// them (greater key, or equal key and lower index, counts).  Lane i < k
-// returns the i-th expert and its weight.  Returns false (wave-uniform) when
-// more than 64 logits reach T (heavy ties); nothing is returned then.
-template <int kPer, bool PROBE = false>
-__device__ __forceinline__ bool wave_topk_rank(const float* row, int E, int k, TopkScratch& S, int& out_id,
-                                               float& out_w, unsigned long long* probe = nullptr) {
+// The candidates of one token's top-k and their ranks, by one full wave.
+// Threshold: the lanes form groups of G (G = 4 for k <= 8, 2 for k <= 16,
+// else 1); T = the largest group maximum that at least k group maxima reach.
+// Those k maxima are k distinct logits >= T, so the k-th largest logit is
+// >= T and every logit of the top-k is a candidate (logit >= T).  The
+// candidates -- usually k plus a few -- are compacted into LDS and each is
+// ranked against all of them (greater key, or equal key and lower index,
+// counts: ties go to the lower expert index).  Lane i < C gets candidate i's
+// key, expert and rank.  Returns C, or -1 (wave-uniform) when more than 64
+// logits reach T (heavy ties).
+template <int kPer, bool PROBE>
+__device__ __forceinline__ int wave_topk_candidates(const float* row, int E, int k, TopkScratch& S, uint32_t& mk,
+                                                    int& mi, int& rank, unsigned long long* probe) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t val[kPer];
   load_logit_keys<kPer>(row, E, val);
@@ -154,16 +154,16 @@ __device__ __forceinline__ bool wave_topk_rank(const float* row, int E, int k, T
     }
     base += (int)__popcll(mask);
   }
-  if (base > kWave) return false;
+  if (base > kWave) return -1;
   const int C = base;
   if (lane < 4) {                                   // padding: key 0 never outranks a candidate
     S.ckey[C + lane] = 0u;
     S.cid[C + lane] = 0x7FFFFFFF;
   }
   wave_lds_fence();
-  const uint32_t mk = (lane < C) ? S.ckey[lane] : 0u;
-  const int mi = (lane < C) ? S.cid[lane] : 0x7FFFFFFF;
-  int rank = 0;
+  mk = (lane < C) ? S.ckey[lane] : 0u;
+  mi = (lane < C) ? S.cid[lane] : 0x7FFFFFFF;
+  rank = 0;
   for (int q = 0; q < C; q += 4) {                  // C is wave-uniform
     const uint4 kq = *reinterpret_cast<const uint4*>(&S.ckey[q]);
     const int4 iq = *reinterpret_cast<const int4*>(&S.cid[q]);
@@ -172,6 +172,21 @@ __device__ __forceinline__ bool wave_topk_rank(const float* row, int E, int k, T
     rank += (int)(kq.z > mk || (kq.z == mk && iq.z < mi));
     rank += (int)(kq.w > mk || (kq.w == mk && iq.w < mi));
   }
+  return C;
+}
+
+// Top-k of one token's logits by one full wave (ranks as above), and the
+// weights exp(l_i - l_max) / sum over the kept.  Lane i < k returns the
+// i-th expert and its weight.  Returns false (wave-uniform) in the heavy-tie
+// case; nothing is returned then.
+template <int kPer, bool PROBE = false>
+__device__ __forceinline__ bool wave_topk_rank(const float* row, int E, int k, TopkScratch& S, int& out_id,
+                                               float& out_w, unsigned long long* probe = nullptr) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t mk;
+  int mi, rank;
+  const int C = wave_topk_candidates<kPer, PROBE>(row, E, k, S, mk, mi, rank, probe);
+  if (C < 0) return false;
   if (lane < C && rank < k) {
     S.okey[rank] = mk;
     S.oid[rank] = mi;
@@ -184,6 +199,45 @@ __device__ __forceinline__ bool wave_topk_rank(const float* row, int E, int k, T
   const float sum = group_sum<kWave>(ex);
   out_w = (lane < k) ? ex / sum : 0.f;
   return true;
+}
+
+// One slot of a one-token batch: the expert of rank s (every lane gets it)
+// and, if need_w, its weight, with the same arithmetic as wave_topk_rank
+// (the kept experts' exponentials are moved to the lanes of their ranks, so
+// the sum runs in the same order).
+template <int kPer, bool PROBE>
+__device__ __forceinline__ void wave_topk_pick(const float* row, int E, int k, int s, bool need_w, TopkScratch& S,
+                                               int& out_e, float& out_w, unsigned long long* probe) {
+  uint32_t mk;
+  int mi, rank;
+  const int C = wave_topk_candidates<kPer, PROBE>(row, E, k, S, mk, mi, rank, probe);
+  if (C < 0) {                                      // heavy ties: the sequential top-k
+    int id;
+    float wt;
+    wave_topk_softmax<kPer>(row, E, k, id, wt);
+    out_e = __builtin_amdgcn_readlane(id, s);
+    out_w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), s));
+    return;
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool kept = lane < C && rank < k;
+  const uint64_t sel = __ballot(lane < C && rank == s);
+  out_e = __builtin_amdgcn_readlane(mi, (int)__builtin_ctzll(sel));
+  out_w = 0.f;
+  if (need_w) {                                     // wave-uniform
+    const uint32_t top_key = __builtin_amdgcn_readlane(mk, (int)__builtin_ctzll(__ballot(lane < C && rank == 0)));
+    const float ex = kept ? expf(f32_from_orderable(mk) - f32_from_orderable(top_key)) : 0.f;
+    // lane r receives the exponential of rank r; the other lanes go one to
+    // one onto lanes k.. (every lane is written exactly once) and carry 0
+    const uint64_t km = __ballot(kept);
+    const int other = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(~km >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)~km, 0u));
+    const float er = __int_as_float(
+        __builtin_amdgcn_ds_permute((kept ? rank : k + other) * 4, kept ? __float_as_int(ex) : 0));
+    const float exr = lane < k ? er : 0.f;
+    const float sum = group_sum<kWave>(exr);
+    out_w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(exr), s)) / sum;
+  }
 }
 
 // The top-k of token t into ids[t*k ..], w[t*k ..] by wave t (all lanes).
@@ -398,17 +452,37 @@ void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
   }
 
   // routing first: the logits are each routing wave's first load
-  if (!shared_row)
-    for (int i = threadIdx.x; i < E; i += DC_THREADS) L.owner[i] = 0x7FFFFFFF;
-  if (!shared_row && wave < M)
-    route_token<C, PROBE>(ro.logits, wave, E, k, L.topk[wave], L.ids, L.w, nullptr, wave == 0 ? a.probe : nullptr);
+  const int slot = (int)blockIdx.y - srow - 1;      // routed rows
+  if (M == 1) {
+    // one token: slot s is its expert of rank s; only the record's writer
+    // (block column 0) needs the weight
+    if (!shared_row && wave == 0) {
+      int e;
+      float w;
+      wave_topk_pick<C, PROBE>(ro.logits, E, k, slot, blockIdx.x == 0, L.topk[0], e, w, a.probe);
+      if (lane == 0) {
+        L.ids[0] = e;
+        L.w[0] = w;
+      }
+    }
+  } else {
+    if (!shared_row)
+      for (int i = threadIdx.x; i < E; i += DC_THREADS) L.owner[i] = 0x7FFFFFFF;
+    if (!shared_row && wave < M)
+      route_token<C, PROBE>(ro.logits, wave, E, k, L.topk[wave], L.ids, L.w, nullptr, wave == 0 ? a.probe : nullptr);
+  }
   if (!shared_row) __syncthreads();
   stamp<PROBE>(a.probe, kGuRouted);
   PRec rec;
-  if (shared_row)
+  if (shared_row) {
     shared_record(M, k, E, rec);
-  else
-    routed_record(L.ids, L.w, L.owner, M, k, E, (int)blockIdx.y - srow - 1, rec);
+  } else if (M == 1) {
+    const int tok[4] = {0, 0, 0, 0}, hrow[4] = {slot, 0, 0, 0};
+    const float wt[4] = {L.w[0], 0.f, 0.f, 0.f};
+    prec_pack(rec, L.ids[0], 1, tok, wt, hrow);
+  } else {
+    routed_record(L.ids, L.w, L.owner, M, k, E, slot, rec);
+  }
   // record 0: the shared expert; record 1 + s: routed slot s (grid row srow + 1 + s)
   if (blockIdx.x == 0 && lane == 0 && wave == 0) prec_store(&recs[shared_row ? 0 : (int)blockIdx.y - srow], rec);
   stamp<PROBE>(a.probe, kGuSlot);
