@@ -25,6 +25,7 @@ constexpr int GU_SHORT_H = 32 * GU_HC * 16;         // longest row the single-pa
 constexpr int DN_SHORT_I = 16 * DN_HC * 16;         // (768)
 // Gate/up workgroups resident per CU (3 waves per SIMD, 4 waves a workgroup).
 constexpr int kGateupBlocksPerCu = 3;
+constexpr int kDownBlocksPerCu = 4;
 // Hinted line touches of a decode gate/up workgroup: its 2 * 16 rows of H/2
 // code bytes in 64-byte lines, kGuTouchLoads per lane of each idle wave
 // (three idle waves at M = 1 cover the 640 lines of H = 2560).
@@ -296,9 +297,18 @@ void gateup_kernel(ForwardArgs a, RouteOut r) {
       a.hdr->mfma_items = 0;
       a.hdr->mt_experts = 0;
     }
-    if (a.lists) {   // grid row y takes the y-th GEMV expert (rows past them exit)
-      if ((int)blockIdx.y >= a.hdr->gemv_experts) return;
-      resolve_slot(a.lists[blockIdx.y], a, s);
+    if (a.lists) {   // grid row y takes GEMV experts y, y + rows, ... (a grid sized to the
+                     // chip, not to every possible slot: no flood of empty workgroups)
+      if (jp0 >= a.I) return;
+      const int n = a.hdr->gemv_experts;
+      for (int y = blockIdx.y; y < n; y += gridDim.y) {
+        resolve_slot(a.lists[y], a, s);
+        if constexpr (SHORT)
+          gateup_short<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
+        else
+          gateup_long<GU_NP, GU_HC>(a, s, jp0, s_lds[wave]);
+      }
+      return;
     } else if (!resolve_slot(blockIdx.y, a, s)) {
       return;
     }
@@ -316,9 +326,17 @@ __global__ __launch_bounds__(DN_WPB * kWave) void down_kernel(ForwardArgs a) {
   __shared__ uint8_t s_lds[DN_WPB][DN_LDS_PER_WAVE];
   const int wave = threadIdx.x / kWave;
   const int r0 = (blockIdx.x * DN_WPB + wave) * 4 * DN_NR;
-  if (a.lists) {     // grid row y takes the y-th GEMV expert (rows past them exit)
-    if ((int)blockIdx.y >= a.hdr->gemv_experts) return;
-    resolve_slot(a.lists[blockIdx.y], a, s);
+  if (a.lists) {     // grid row y takes GEMV experts y, y + rows, ...
+    if (r0 >= a.H) return;
+    const int n = a.hdr->gemv_experts;
+    for (int y = blockIdx.y; y < n; y += gridDim.y) {
+      resolve_slot(a.lists[y], a, s);
+      if constexpr (SHORT)
+        down_short<DN_NR, DN_HC, ROWS>(a, s, r0, s_lds[wave]);
+      else
+        down_long<DN_NR, DN_HC, ROWS>(a, s, r0, s_lds[wave]);
+    }
+    return;
   } else if (!resolve_slot(gridDim.y - 1 - blockIdx.y, a, s)) {
     // decode: slots in reverse, so the shared expert (every token, the most
     // work; the last working slot) is dispatched before the routed ones
@@ -399,9 +417,17 @@ hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, 
     const int fit = kGateupBlocksPerCu * device_cus() / gx - extra;
     gy = (slots < fit ? slots : (fit > 1 ? fit : 1)) + extra;
   }
+  const int dx = (a.H + DN_ROWS_PER_BLOCK - 1) / DN_ROWS_PER_BLOCK;
+  int dy = slots;
+  if (a.lists) {   // batches: the kernels loop over the GEMV experts; two residency rounds of rows
+    const int cus = device_cus();
+    const int gfit = (2 * kGateupBlocksPerCu * cus + gx - 1) / gx, dfit = (2 * kDownBlocksPerCu * cus + dx - 1) / dx;
+    gy = gy < gfit ? gy : gfit;
+    dy = dy < dfit ? dy : dfit;
+  }
   dim3 ggu(gx, gy);
   dim3 bgu(GU_WPB * kWave);
-  dim3 gdn((a.H + DN_ROWS_PER_BLOCK - 1) / DN_ROWS_PER_BLOCK, slots), bdn(DN_WPB * kWave);
+  dim3 gdn(dx, dy), bdn(DN_WPB * kWave);
   auto dn = (a.I <= DN_SHORT_I) ? (a.yp ? down_kernel<true, true> : down_kernel<true, false>)
                                 : (a.yp ? down_kernel<false, true> : down_kernel<false, false>);
   // with events, they take the gate/up kernel's own begin/end timestamps

@@ -327,7 +327,7 @@ __device__ __forceinline__ void gateup_long(const ForwardArgs& a, const ExpertSl
 template <int NR, int HC, bool ROWS>
 __device__ __forceinline__ void down_short(const ForwardArgs& a, const ExpertSlot& s, int r0,
                                            uint8_t* s_lds) {
-  const int lane = threadIdx.x & (kWave - 1);
+  const int lane = opaque_lane();   // recomputed per call: nothing hoisted out of a slot loop
   const int grp = lane >> 4, j16 = lane & 15;
   const int H = a.H, I = a.I;
   const int KH = I / 16;
