@@ -477,11 +477,59 @@ def main():
         m4 = bench_moe(torch, binding, synth, args, synth.WORKLOADS["ling_m4_mtp"], cpu=not args.no_cpu_baseline,
                        cpu_budget=5.0, one_thread=False)
         keep = ("us_per_layer", "value", "unit", "ms_per_step", "layer_frac_of_hbm_peak", "expert_bytes_per_layer",
-                "expert_rate", "roofline", "mean_distinct_experts", "config", "timed_passes_us_per_layer",
+                "expert_rate", "read_floor", "roofline", "mean_distinct_experts", "config", "timed_passes_us_per_layer",
                 "cpu_baseline")
         out["ling_m4_mtp"] = {k: m4[k] for k in keep if k in m4}
         out["t_m4_over_t_m1"] = m4["us_per_layer"] / out["us_per_layer"]
     print(json.dumps(out), flush=True)
+
+
+def read_floor(torch, binding, wl, sets, true_ids, hev, order):
+    """The read-bandwidth floor of each set's bytes (moe_read_probe: one
+    kernel that only reads, every load of a workgroup in flight at once),
+    launched eagerly over the sets in `order`, mean kernel time per launch:
+    the gate/up weights of the layer's experts (routed + shared), their down
+    weights, all of their weights in one kernel, and the router's weights."""
+    import numpy as np
+    H, I, E = wl.H, wl.I, wl.E
+    gq, gs = 2 * I * (H // 2), 2 * I * (H // 32)             # bytes per expert
+    dq, ds = H * (I // 2), H * (I // 32)
+    def ranges(d, ids, parts):
+        experts = sorted(set(int(e) for e in np.asarray(ids).ravel())) + ([E] if wl.shared else [])
+        out = []
+        for e in experts:
+            if "gateup" in parts:
+                out += [(d.w13_q.data_ptr() + e * gq, gq), (d.w13_s.data_ptr() + e * gs, gs)]
+            if "down" in parts:
+                out += [(d.w2_q.data_ptr() + e * dq, dq), (d.w2_s.data_ptr() + e * ds, ds)]
+        return out
+    kinds = {"gateup": ("gateup",), "down": ("down",), "experts": ("gateup", "down"), "router": ()}
+    prepared = {k: [] for k in kinds}
+    for d, ids in zip(sets, true_ids):
+        for k, parts in kinds.items():
+            r = [(d.w_router.data_ptr(), E * H * 4)] if k == "router" else ranges(d, ids, parts)
+            mb = max(sz for _, sz in r)
+            a = torch.tensor([x for x, _ in r], dtype=torch.int64, device="cuda")
+            z = torch.tensor([sz for _, sz in r], dtype=torch.int64, device="cuda")
+            words = binding.read_probe_words(len(r), mb)
+            prepared[k].append((a, z, len(r), mb, torch.empty((words,), dtype=torch.int32, device="cuda"), words,
+                                sum(sz for _, sz in r)))
+    res = {}
+    for k in kinds:
+        evs = [(hev.create(), hev.create()) for _ in order]
+        for (i, (e0, e1)) in zip(order, evs):
+            a, z, n, mb, out, words, _ = prepared[k][i]
+            binding.moe_read_probe(a, z, n, mb, out, words, e0, e1)
+        torch.cuda.synchronize()
+        us = sum(hev.elapsed_ms(e0, e1) for e0, e1 in evs) / len(evs) * 1e3
+        nbytes = sum(prepared[k][i][6] for i in order) / len(order)
+        for e0, e1 in evs:
+            hev.destroy(e0)
+            hev.destroy(e1)
+        res[k] = {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
+    log("[floor] " + ", ".join(f"{k} {v['us']:.2f} us ({v['bytes'] / 1e6:.1f} MB, {v['gbs']:.0f} GB/s)"
+                               for k, v in res.items()))
+    return res
 
 
 def phase_table(torch, binding, synth, args, wl):
@@ -736,6 +784,7 @@ def bench_moe(torch, binding, synth, args, wl, cpu=True, cpu_budget=10.0, one_th
             f"({rate / HBM_PEAK_GBS:.1%} of 8 TB/s)")
 
     gu_kernel = gateup_kernel_name(wl, args.three_calls, hints is not None)
+    floor = read_floor(torch, binding, wl, sets, true_ids, hev, [step_sets[i] for i in range(n_ev)])
     out = {
         "metric": METRIC,
         "value": round(layer_gbs, 2),
@@ -765,6 +814,19 @@ def bench_moe(torch, binding, synth, args, wl, cpu=True, cpu_budget=10.0, one_th
         "expert_gbs": sum(exp_b) / (ms_total * 1e-3) / 1e9,
         "expert_frac_of_hbm_peak": sum(exp_b) / (ms_total * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "expert_rate": expert_rate,
+        # the same bytes read by a kernel that only reads (moe_read_probe):
+        # what the chip allows for each part, and how far each part is from it
+        "read_floor": {
+            "what": "mean kernel time of moe_read_probe over the timed sets: the layer's expert gate/up weights, "
+                    "their down weights, all of them in one kernel, and the router weights",
+            "gateup_us": floor["gateup"]["us"], "down_us": floor["down"]["us"],
+            "experts_us": floor["experts"]["us"], "router_us": floor["router"]["us"],
+            "experts_gbs": floor["experts"]["gbs"],
+            "layer_over_experts_floor": ms_per_step * 1e3 / floor["experts"]["us"],
+            "gateup_kernel_over_floor": (gu_ms * 1e3 / floor["gateup"]["us"]) if gu_kernel.startswith("decode") else None,
+            "down_kernel_over_floor": (dn_ms * 1e3 / floor["down"]["us"])
+            if gu_kernel.startswith("decode") and dn_ms is not None else None,
+        },
         "mean_distinct_experts": sum(D[l] for l in step_sets) / len(step_sets),
         "roofline": {"bound": "hbm", "kernel": gu_kernel,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -230,14 +230,39 @@ moe_status moe_layer_ex(const uint16_t* x, const float* w_router, const float* l
                         int32_t* sorted_pairs, int32_t* active_experts, int32_t* num_active, float* y,
                         void* workspace, size_t workspace_bytes, const moe_exec_opts* opts, void* stream);
 
+/* Measurement hook: the floor for streaming a set of byte ranges on this chip.
+ * One kernel reads every range the way the decode kernels stream expert
+ * weights -- 16 bytes per lane, each workgroup's chunk of
+ * MOE_READ_PROBE_CHUNK bytes requested at once -- and does nothing else; the
+ * bench reads a layer's expert weights with it to set their kernels' times
+ * against.
+ *   addrs       device uint64 [n]: range start addresses, 16-byte aligned
+ *   sizes       device int64 [n]: range lengths in bytes, multiples of 16, each
+ *               in [16, max_bytes] (ranges are read, never written)
+ *   max_bytes   host: the largest size, a multiple of 16
+ *   out         device uint32 [n][C], C = ceil(max_bytes / MOE_READ_PROBE_CHUNK):
+ *               out[i][c] = XOR of the little-endian 32-bit words of bytes
+ *               [c, c + 1) x MOE_READ_PROBE_CHUNK of range i (0 past its end)
+ *   out_words   >= n * C
+ *   start_event, stop_event  hipEvent_t recorded at the kernel's start and end
+ *               (both or neither; NULL: none)
+ * MOE_ERR_NULL, MOE_ERR_SHAPE (n outside [1, 65535], bad max_bytes, short
+ * out), MOE_ERR_ALIGN (addrs, sizes not 8-byte aligned, out not 4-byte
+ * aligned); sizes outside the stated bounds are undefined. */
+#define MOE_READ_PROBE_CHUNK 16384
+moe_status moe_read_probe(const uint64_t* addrs, const int64_t* sizes, int32_t n, int64_t max_bytes, uint32_t* out,
+                          size_t out_words, void* start_event, void* stop_event, void* stream);
+
 /* Measurement hook of the decode path (M <= 4, H = 2560, I = 768): moe_layer
  * with kernel instances that also write phase timestamps (the GPU's 100 MHz
  * constant clock, s_memrealtime) of thread 0 of every workgroup: per
  * workgroup index w = y * gridDim.x + x of each kernel's own grid,
  *   stamps[16w + 0..8]:  gate/up kernel entry, token 0's logits loaded, its
- *                        top-k threshold, its top-k done, the workgroup's
- *                        routing barrier passed, slot known, weight loads
- *                        issued, first weight block used, h written;
+ *                        top-k threshold, its top-k done (two or more
+ *                        tokens), the workgroup's routing barrier passed,
+ *                        slot known, weight loads issued, first weight block
+ *                        used, h written (the routing writer: its outputs
+ *                        written);
  *   stamps[16w + 9..13]: down kernel entry, record loaded, loads issued,
  *                        first weight block used, y added.
  * Stamps a workgroup does not reach keep their prior value.  Results are those

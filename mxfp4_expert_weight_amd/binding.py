@@ -85,6 +85,7 @@ _SIGNATURES = {
                                             _P, _P, _P, _P, _P, _SZ, ctypes.POINTER(moe_exec_opts), _P]),
     "moe_layer_ex": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P, _P,
                                     _P, _P, _P, _P, _P, _P, _P, _SZ, ctypes.POINTER(moe_exec_opts), _P]),
+    "moe_read_probe": (ctypes.c_int, [_P, _P, _I32, _I64, _P, ctypes.c_size_t, _P, _P, _P]),
     "moe_layer_noalloc": (ctypes.c_int, [_P, _P, _P, _I64, ctypes.POINTER(moe_mxfp4_weights), _I32, _I32, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_layer_probe_stamps": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
@@ -226,6 +227,18 @@ def moe_mxfp4_forward_ex(x, w: moe_mxfp4_weights, M, top_k, topk_weights, expert
                                       _ptr(active_experts), _ptr(num_active), _ptr(y), _ptr(workspace),
                                       workspace_bytes, ctypes.byref(opts) if opts is not None else None,
                                       _stream(stream)), "moe_mxfp4_forward_ex")
+
+
+READ_PROBE_CHUNK = 16384                # MOE_READ_PROBE_CHUNK: bytes per moe_read_probe output word
+
+
+def read_probe_words(n, max_bytes) -> int:
+    return n * (-(-max_bytes // READ_PROBE_CHUNK))
+
+
+def moe_read_probe(addrs, sizes, n, max_bytes, out, out_words, start_event=None, stop_event=None, stream=None):
+    _check(lib().moe_read_probe(_ptr(addrs), _ptr(sizes), n, max_bytes, _ptr(out), out_words, start_event,
+                                stop_event, _stream(stream)), "moe_read_probe")
 
 
 NOALLOC_WORKSPACE_BYTES = 8 << 20      # MOE_NOALLOC_WORKSPACE_BYTES

@@ -328,6 +328,19 @@ hipError_t noalloc_scratch(void** out) {
 
 extern "C" {
 
+moe_status moe_read_probe(const uint64_t* addrs, const int64_t* sizes, int32_t n, int64_t max_bytes, uint32_t* out,
+                          size_t out_words, void* start_event, void* stop_event, void* stream) {
+  if (!addrs || !sizes || !out) return MOE_ERR_NULL;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return MOE_ERR_NULL;
+  if (n < 1 || n > 65535 || max_bytes < 16 || max_bytes % 16 != 0 ||
+      read_probe_chunks(max_bytes) > INT32_MAX)
+    return MOE_ERR_SHAPE;
+  if (out_words < (size_t)n * (size_t)read_probe_chunks(max_bytes)) return MOE_ERR_SHAPE;
+  if (((uintptr_t)addrs & 7u) || ((uintptr_t)sizes & 7u) || ((uintptr_t)out & 3u)) return MOE_ERR_ALIGN;
+  return hip_status(launch_read_probe(addrs, sizes, n, max_bytes, out, (hipEvent_t)start_event,
+                                      (hipEvent_t)stop_event, (hipStream_t)stream));
+}
+
 moe_status moe_layer_noalloc(const uint16_t* x, const float* w_router, const float* logit_bias,
                              int64_t bias_row_stride, const moe_mxfp4_weights* w, int32_t M, int32_t top_k,
                              float* logits, int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,

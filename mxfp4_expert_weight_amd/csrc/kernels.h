@@ -213,6 +213,13 @@ bool decode_fast_fits(int M, int H, int I);
 // Stamps the measurement instances write: 8 per workgroup of the larger grid.
 size_t decode_probe_stamps(int M, int k, int E, int H, int I, int has_shared);
 hipError_t launch_decode(const ForwardArgs& a, const RouteOut& r, hipStream_t s, const Timing& tm, bool probe);
+
+// Read-bandwidth floor (moe_read_probe): one workgroup per 16 KB chunk of each
+// byte range, every load in flight at once.
+constexpr int64_t kReadProbeChunk = MOE_READ_PROBE_CHUNK;
+inline int64_t read_probe_chunks(int64_t max_bytes) { return (max_bytes + kReadProbeChunk - 1) / kReadProbeChunk; }
+hipError_t launch_read_probe(const uint64_t* addrs, const int64_t* sizes, int n, int64_t max_bytes, uint32_t* out,
+                             hipEvent_t start, hipEvent_t stop, hipStream_t s);
 hipError_t launch_forward_routed(const ForwardArgs& a, const RouteOut& r, hipStream_t s,
                                  const Timing& tm = Timing{});
 // MFMA path (mfma.hip): two-term MXFP8 quantisation of x, the dense gate/up

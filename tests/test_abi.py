@@ -135,6 +135,22 @@ def test_noalloc_layer_host_checks(lib):
     assert _status(f, *(args[:5] + [512] + args[6:])) == B.MOE_ERR_WORKSPACE
 
 
+def test_read_probe_host_checks(lib):
+    """moe_read_probe: pointers, sizes and alignment checked on the host."""
+    f = B.moe_read_probe
+    n, mb = 3, 2088960
+    words = B.read_probe_words(n, mb)
+    assert words == 3 * 128
+    assert _status(f, None, A, n, mb, A, words) == B.MOE_ERR_NULL
+    assert _status(f, A, A, n, mb, None, words) == B.MOE_ERR_NULL
+    assert _status(f, A, A, n, mb, A, words, A, None) == B.MOE_ERR_NULL        # one event of two
+    assert _status(f, A, A, 0, mb, A, words) == B.MOE_ERR_SHAPE
+    assert _status(f, A, A, n, 8, A, words) == B.MOE_ERR_SHAPE
+    assert _status(f, A, A, n, mb + 4, A, words) == B.MOE_ERR_SHAPE            # not a multiple of 16
+    assert _status(f, A, A, n, mb, A, words - 1) == B.MOE_ERR_SHAPE
+    assert _status(f, A + 4, A, n, mb, A, words) == B.MOE_ERR_ALIGN
+
+
 def test_exec_opts_host_checks(lib):
     """moe_exec_opts: act8 in {0, 1}; helper streams come as a pair, with all
     four events (checked before anything is enqueued)."""

@@ -164,3 +164,30 @@ def test_router_logits_and_routing(M, H, E, k, bias):
     bound = logit_error_bound(xf, w, b, H, M)
     check_routing(ids.cpu().numpy(), wts.cpu().numpy(), logits.cpu().numpy(), ref, bound, k,
                   f"router M={M}")
+
+
+def test_read_probe_checksums_exact():
+    """moe_read_probe: each 80 KB chunk's XOR of 32-bit words, bit-exact
+    against numpy, over ranges of mixed lengths and offsets (a ragged last
+    chunk, a range shorter than one chunk, a one-load range)."""
+    torch = need_gpu()
+    rng = np.random.default_rng(21)
+    buf = rng.integers(0, 2**32, size=(3 << 20) // 4, dtype=np.uint32)      # 3 MiB
+    d = torch.from_numpy(buf.view(np.int32)).cuda()
+    base = d.data_ptr()
+    ranges = [(0, 2088960), (16 * 12345, 122880), (1 << 20, 16), (48, 81920 * 3 + 32)]
+    n, mb = len(ranges), max(s for _, s in ranges)
+    addrs = torch.tensor([base + o for o, _ in ranges], dtype=torch.int64).cuda()
+    sizes = torch.tensor([s for _, s in ranges], dtype=torch.int64).cuda()
+    words = B.read_probe_words(n, mb)
+    out = torch.full((words,), -1, dtype=torch.int32).cuda()
+    say("read probe: 4 ranges")
+    B.moe_read_probe(addrs, sizes, n, mb, out, words)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32).reshape(n, -1)
+    raw = buf.view(np.uint8)
+    for i, (o, s) in enumerate(ranges):
+        for c in range(got.shape[1]):
+            lo, hi = o + c * B.READ_PROBE_CHUNK, o + min((c + 1) * B.READ_PROBE_CHUNK, s)
+            want = np.bitwise_xor.reduce(raw[lo:hi].view(np.uint32)) if hi > lo else np.uint32(0)
+            assert got[i, c] == want, (i, c)
