@@ -397,98 +397,21 @@ __device__ __forceinline__ float dot_block(const u32x4& c, float scale, const u3
 // token loop, not hoisted out of it into many live registers.  No instruction.
 __device__ __forceinline__ void keep_in_loop(u32x4& v) { asm volatile("" : "+v"(v)); }
 
-// Roles of the gate/up grid rows: [shared row] [writer row] [R routed rows]
-// (the writer is dispatched early: its loads then go out before the weight
-// stream fills the memory queues).
-// C: experts per lane of the top-k; NB: H / 512; Q: quads of row pairs per
-// wave (a workgroup covers 16 Q intermediate indices); A8: W4A8 (x rounded to
-// MXFP8 as it is staged); MF: the products on the matrix cores (Q = 2: a
-// wave's 8 gate and 8 up rows are the 16 rows of one tile, the slot's tokens
-// its columns), each weight decoded once for all of the slot's tokens;
-// otherwise per-token v_dot2 products.
-template <int C, int NB, int Q, bool A8, bool PROBE, bool MF>
-__global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(Q >= 2 ? 3 : 4, Q >= 2 ? 3 : 4)))
-void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
+// One slot's gate/up work for the rows of this workgroup: its x rows, scales
+// and code words requested in consumption order, x and the scales staged in
+// LDS, the products formed as the codes arrive, h written as two bf16 terms.
+// Q: quads of row pairs per wave (a workgroup covers 16 Q intermediate
+// indices); A8: W4A8 (x rounded to MXFP8 as it is staged); MF: the products on
+// the matrix cores (Q = 2: a wave's 8 gate and 8 up rows are the 16 rows of
+// one tile, the slot's tokens its columns), each weight decoded once for all
+// of the slot's tokens; otherwise per-token v_dot2 products.
+template <int NB, int Q, bool A8, bool PROBE, bool MF>
+__device__ __forceinline__ void gateup_slot(const ForwardArgs& a, GateupLds<NB, Q>& L, const PRec& rec) {
   constexpr int KB = NB * 16;                      // 32-element blocks per row
-  static_assert(Q >= 1 && Q <= 4, "quads");
   static_assert(!MF || Q == 2, "a matrix-core wave covers 8 row pairs");
-  using Lds = GateupLds<NB, Q>;
-  static_assert(sizeof(SmallSortLds<C, DC_MAXP>) <= sizeof(Lds::x), "the writer's sort state fits the x area");
-  __shared__ __align__(16) Lds L;
-  stamp<PROBE>(a.probe, kGuEntry);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int M = a.M, k = a.k, E = a.E, H = a.H, I = a.I;
-  const int srow = a.has_shared ? 1 : 0;
-  const bool writer = blockIdx.y == srow;
-  const bool shared_row = a.has_shared && blockIdx.y == 0;
-  {                                                // every workgroup zeroes a share of y (down adds into it)
-    const size_t nblk = (size_t)gridDim.x * gridDim.y;
-    const size_t b = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
-    for (size_t i = b * DC_THREADS + threadIdx.x; i < (size_t)M * H; i += nblk * DC_THREADS) a.y[i] = 0.f;
-  }
-  DecRec* recs = reinterpret_cast<DecRec*>(const_cast<SlotRec*>(a.rec));
-
-  if (writer) {
-    // the ABI's routing outputs: top-k of every token, the stable sort by
-    // expert, and the header's path counters
-    if (blockIdx.x != 0) return;
-    SmallSortLds<C, DC_MAXP>& W = *reinterpret_cast<SmallSortLds<C, DC_MAXP>*>(L.x);
-    if (wave < M) route_token<C>(ro.logits, wave, E, k, L.topk[wave], W.ids, W.w, W.tok);
-    __syncthreads();
-    const int N = M * k;
-    if (wave == 0) wave_sort_small(W, N, E, ro.ebits);
-    __syncthreads();
-    block_store_small_sort(W, N, E, ro.topk_ids, ro.topk_weights, ro.offsets, ro.sorted_pairs, ro.active,
-                           ro.num_active);
-    if (threadIdx.x == 0) {
-      a.hdr->gemv_experts = W.na + a.has_shared;
-      a.hdr->mfma_experts = 0;
-      a.hdr->mfma_items = 0;
-      a.hdr->mt_experts = 0;
-      if (!a.has_shared) recs[0].e = -1;            // record 0 is the shared expert's
-    }
-    stamp<PROBE>(a.probe, kGuDone);
-    return;
-  }
-
-  // routing first: the logits are each routing wave's first load
-  const int slot = (int)blockIdx.y - srow - 1;      // routed rows
-  if (M == 1) {
-    // one token: slot s is its expert of rank s; only the record's writer
-    // (block column 0) needs the weight
-    if (!shared_row && wave == 0) {
-      int e;
-      float w;
-      wave_topk_pick<C, PROBE>(ro.logits, E, k, slot, blockIdx.x == 0, L.topk[0], e, w, a.probe);
-      if (lane == 0) {
-        L.ids[0] = e;
-        L.w[0] = w;
-      }
-    }
-  } else {
-    if (!shared_row)
-      for (int i = threadIdx.x; i < E; i += DC_THREADS) L.owner[i] = 0x7FFFFFFF;
-    if (!shared_row && wave < M)
-      route_token<C, PROBE>(ro.logits, wave, E, k, L.topk[wave], L.ids, L.w, nullptr, wave == 0 ? a.probe : nullptr);
-  }
-  if (!shared_row) __syncthreads();
-  stamp<PROBE>(a.probe, kGuRouted);
-  PRec rec;
-  if (shared_row) {
-    shared_record(M, k, E, rec);
-  } else if (M == 1) {
-    const int tok[4] = {0, 0, 0, 0}, hrow[4] = {slot, 0, 0, 0};
-    const float wt[4] = {L.w[0], 0.f, 0.f, 0.f};
-    prec_pack(rec, L.ids[0], 1, tok, wt, hrow);
-  } else {
-    routed_record(L.ids, L.w, L.owner, M, k, E, slot, rec);
-  }
-  // record 0: the shared expert; record 1 + s: routed slot s (grid row srow + 1 + s)
-  if (blockIdx.x == 0 && lane == 0 && wave == 0) prec_store(&recs[shared_row ? 0 : (int)blockIdx.y - srow], rec);
-  stamp<PROBE>(a.probe, kGuSlot);
+  const int H = a.H, I = a.I;
   const int rec_e = prec_e(rec), rec_n = prec_n(rec);
-  if (rec_e < 0) return;                            // no expert in this slot (uniform over the block)
-
   // the slot's tokens' x rows (issued before the weights, consumed first);
   // stores are unconditional (a guarded one would make a branch that holds
   // the load): threads past the end rewrite the last element's own value
@@ -670,6 +593,94 @@ void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
   }
 }
 
+// Roles of the gate/up grid rows: [shared row] [writer row] [R routed rows]
+// (the writer is dispatched early: its loads then go out before the weight
+// stream fills the memory queues).  C: experts per lane of the top-k; NB:
+// H / 512; Q, A8, MF as for gateup_slot.
+template <int C, int NB, int Q, bool A8, bool PROBE, bool MF>
+__global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(Q >= 2 ? 3 : 4, Q >= 2 ? 3 : 4)))
+void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
+  constexpr int KB = NB * 16;                      // 32-element blocks per row
+  static_assert(Q >= 1 && Q <= 4, "quads");
+  static_assert(!MF || Q == 2, "a matrix-core wave covers 8 row pairs");
+  using Lds = GateupLds<NB, Q>;
+  static_assert(sizeof(SmallSortLds<C, DC_MAXP>) <= sizeof(Lds::x), "the writer's sort state fits the x area");
+  __shared__ __align__(16) Lds L;
+  stamp<PROBE>(a.probe, kGuEntry);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int M = a.M, k = a.k, E = a.E, H = a.H, I = a.I;
+  const int srow = a.has_shared ? 1 : 0;
+  const bool writer = blockIdx.y == srow;
+  const bool shared_row = a.has_shared && blockIdx.y == 0;
+  {                                                // every workgroup zeroes a share of y (down adds into it)
+    const size_t nblk = (size_t)gridDim.x * gridDim.y;
+    const size_t b = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+    for (size_t i = b * DC_THREADS + threadIdx.x; i < (size_t)M * H; i += nblk * DC_THREADS) a.y[i] = 0.f;
+  }
+  DecRec* recs = reinterpret_cast<DecRec*>(const_cast<SlotRec*>(a.rec));
+
+  if (writer) {
+    // the ABI's routing outputs: top-k of every token, the stable sort by
+    // expert, and the header's path counters
+    if (blockIdx.x != 0) return;
+    SmallSortLds<C, DC_MAXP>& W = *reinterpret_cast<SmallSortLds<C, DC_MAXP>*>(L.x);
+    if (wave < M) route_token<C>(ro.logits, wave, E, k, L.topk[wave], W.ids, W.w, W.tok);
+    __syncthreads();
+    const int N = M * k;
+    if (wave == 0) wave_sort_small(W, N, E, ro.ebits);
+    __syncthreads();
+    block_store_small_sort(W, N, E, ro.topk_ids, ro.topk_weights, ro.offsets, ro.sorted_pairs, ro.active,
+                           ro.num_active);
+    if (threadIdx.x == 0) {
+      a.hdr->gemv_experts = W.na + a.has_shared;
+      a.hdr->mfma_experts = 0;
+      a.hdr->mfma_items = 0;
+      a.hdr->mt_experts = 0;
+      if (!a.has_shared) recs[0].e = -1;            // record 0 is the shared expert's
+    }
+    stamp<PROBE>(a.probe, kGuDone);
+    return;
+  }
+
+  // routing first: the logits are each routing wave's first load
+  const int slot = (int)blockIdx.y - srow - 1;      // routed rows
+  if (M == 1) {
+    // one token: slot s is its expert of rank s; only the record's writer
+    // (block column 0) needs the weight
+    if (!shared_row && wave == 0) {
+      int e;
+      float w;
+      wave_topk_pick<C, PROBE>(ro.logits, E, k, slot, blockIdx.x == 0, L.topk[0], e, w, a.probe);
+      if (lane == 0) {
+        L.ids[0] = e;
+        L.w[0] = w;
+      }
+    }
+  } else {
+    if (!shared_row)
+      for (int i = threadIdx.x; i < E; i += DC_THREADS) L.owner[i] = 0x7FFFFFFF;
+    if (!shared_row && wave < M)
+      route_token<C, PROBE>(ro.logits, wave, E, k, L.topk[wave], L.ids, L.w, nullptr, wave == 0 ? a.probe : nullptr);
+  }
+  if (!shared_row) __syncthreads();
+  stamp<PROBE>(a.probe, kGuRouted);
+  PRec rec;
+  if (shared_row) {
+    shared_record(M, k, E, rec);
+  } else if (M == 1) {
+    const int tok[4] = {0, 0, 0, 0}, hrow[4] = {slot, 0, 0, 0};
+    const float wt[4] = {L.w[0], 0.f, 0.f, 0.f};
+    prec_pack(rec, L.ids[0], 1, tok, wt, hrow);
+  } else {
+    routed_record(L.ids, L.w, L.owner, M, k, E, slot, rec);
+  }
+  // record 0: the shared expert; record 1 + s: routed slot s (grid row srow + 1 + s)
+  if (blockIdx.x == 0 && lane == 0 && wave == 0) prec_store(&recs[shared_row ? 0 : (int)blockIdx.y - srow], rec);
+  stamp<PROBE>(a.probe, kGuSlot);
+  if (prec_e(rec) < 0) return;                      // no expert in this slot (uniform over the block)
+  gateup_slot<NB, Q, A8, PROBE, MF>(a, L, rec);
+}
+
 // --------------------------------------------------------------- down --
 // Workgroup (64 output rows, record y); wave: 16 rows as two 8-row groups,
 // lane (g8 = lane / 8, j8 = lane % 8) takes row r0 + 8 rg + g8, blocks
@@ -686,17 +697,14 @@ struct DownLds {
 // one tile; column t < 4 is token t's hi term of h, column 7 - t its lo term
 // (so a half-row mirror adds the two), each weight decoded once for all
 // tokens.  Otherwise per-token v_dot2 products.
-template <int NBD, bool PROBE, bool MF>
-__global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(6, 6)))
-void decode_down_kernel(ForwardArgs a) {
+// One record's down work for this workgroup's 64 output rows: h (both terms)
+// and the scale bytes staged in LDS, the code words in flight, products as
+// they arrive.  ROWS: each pair's weighted row goes to its own partial row of
+// yp (hrow order; a combine kernel sums them); otherwise fp32 atomics into y.
+template <int NBD, bool PROBE, bool MF, bool ROWS>
+__device__ __forceinline__ void down_slot(const ForwardArgs& a, DownLds<NBD>& L, const PRec& rec) {
   constexpr int KB = NBD * 8;                      // blocks per row (I / 32)
-  __shared__ __align__(16) DownLds<NBD> L;
-  stamp<PROBE>(a.probe, kDnEntry);
-  PRec rec;
-  prec_load(reinterpret_cast<const DecRec*>(a.rec) + blockIdx.y, rec);
   const int rec_e = prec_e(rec), rec_n = prec_n(rec);
-  if (rec_e < 0) return;
-  stamp<PROBE>(a.probe, kDnRecord);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int H = a.H, I = a.I;
   const int g8 = lane >> 3, j8 = lane & 7;
@@ -792,10 +800,15 @@ void decode_down_kernel(ForwardArgs a) {
     if (col < rec_n) {
       const int t = prec_tok(rec, col);
       const float wt = prec_w(rec, col);
+      if constexpr (ROWS) {                         // rows r0 + 4 kq .. + 3 of the pair's partial row
+        float* yr = a.yp + (size_t)prec_hrow(rec, col) * H + r0 + 4 * kq;
+        *reinterpret_cast<float4*>(yr) = make_float4(wt * v[0], wt * v[1], wt * v[2], wt * v[3]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = r0 + 4 * kq + e;
-        if (row < H) unsafeAtomicAdd(&a.y[(size_t)t * H + row], wt * v[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int row = r0 + 4 * kq + e;
+          if (row < H) unsafeAtomicAdd(&a.y[(size_t)t * H + row], wt * v[e]);
+        }
       }
     }
     stamp<PROBE>(a.probe, kDnDone);
@@ -839,7 +852,11 @@ void decode_down_kernel(ForwardArgs a) {
 #pragma unroll
       for (int rg = 0; rg < DN_RG; ++rg) {
         const int row = r0 + 8 * rg + g8;
-        if (row < H) unsafeAtomicAdd(&a.y[(size_t)t * H + row], wt * v[rg]);
+        if constexpr (ROWS) {
+          if (row < H) a.yp[(size_t)prec_hrow(rec, n) * H + row] = wt * v[rg];
+        } else {
+          if (row < H) unsafeAtomicAdd(&a.y[(size_t)t * H + row], wt * v[rg]);
+        }
       }
     }
   };
@@ -852,6 +869,71 @@ void decode_down_kernel(ForwardArgs a) {
     token(n);
   }
   stamp<PROBE>(a.probe, kDnDone);
+  }
+}
+
+template <int NBD, bool PROBE, bool MF>
+__global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(6, 6)))
+void decode_down_kernel(ForwardArgs a) {
+  constexpr int KB = NBD * 8;                      // blocks per row (I / 32)
+  __shared__ __align__(16) DownLds<NBD> L;
+  stamp<PROBE>(a.probe, kDnEntry);
+  PRec rec;
+  prec_load(reinterpret_cast<const DecRec*>(a.rec) + blockIdx.y, rec);
+  const int rec_e = prec_e(rec), rec_n = prec_n(rec);
+  if (rec_e < 0) return;
+  stamp<PROBE>(a.probe, kDnRecord);
+  down_slot<NBD, PROBE, MF, false>(a, L, rec);
+}
+
+// ------------------------------------------------------------- batches --
+// Batch experts with one or two tokens (the GEMV list that the sort epilogue
+// builds) at H = 2560, I = 768: the decode kernels' slot work, driven by the
+// records instead of the routing.  Grid row y takes list entries y, y + rows,
+// ...: a grid of two residency rounds, not one row per possible slot.
+
+// The record of a batch slot (SlotRec: e, n, first sorted position, first h
+// row, 4 tokens, 4 weights) as a decode record; h rows are consecutive.
+__device__ __forceinline__ void prec_from_slot(const SlotRec* src, PRec& r) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(src);
+  const u32x4 a = p[0], t = p[1], w = p[2];
+  const unsigned h0 = a[3];
+  r.a = u32x4{a[0], a[1], t[0], t[1]};
+  r.b = u32x4{t[2], t[3], w[0], w[1]};
+  r.c = u32x4{w[2], w[3], h0, h0 + 1u};
+  r.d = u32x4{h0 + 2u, h0 + 3u, 0u, 0u};
+}
+
+template <int NB>
+__global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void batch_gateup_kernel(ForwardArgs a) {
+  __shared__ __align__(16) GateupLds<NB, 2> L;
+  if (!a.yp) {                                     // atomics into y: every workgroup zeroes a share
+    const size_t nblk = (size_t)gridDim.x * gridDim.y;
+    const size_t b = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+    for (size_t i = b * DC_THREADS + threadIdx.x; i < (size_t)a.M * a.H; i += nblk * DC_THREADS) a.y[i] = 0.f;
+  }
+  const int n = a.hdr->gemv_experts;
+  for (int y = blockIdx.y; y < n; y += gridDim.y) {
+    PRec rec;
+    prec_from_slot(a.rec + a.lists[y], rec);
+    if (prec_e(rec) >= 0 && prec_n(rec) <= kRoutedMaxTokens)   // uniform over the workgroup
+      gateup_slot<NB, 2, false, false, true>(a, L, rec);
+    __syncthreads();                               // the next slot restages x and the scales
+  }
+}
+
+template <int NBD, bool ROWS>
+__global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(6, 6)))
+void batch_down_kernel(ForwardArgs a) {
+  __shared__ __align__(16) DownLds<NBD> L;
+  const int n = a.hdr->gemv_experts;
+  for (int y = blockIdx.y; y < n; y += gridDim.y) {
+    PRec rec;
+    prec_from_slot(a.rec + a.lists[y], rec);
+    if (prec_e(rec) >= 0 && prec_n(rec) <= kRoutedMaxTokens)
+      down_slot<NBD, false, true, ROWS>(a, L, rec);
+    __syncthreads();
   }
 }
 
@@ -905,6 +987,28 @@ size_t decode_probe_stamps(int M, int k, int E, int H, int I, int has_shared) {
   const dim3 g = decode_gateup_grid(M, k, E, I, has_shared), d = decode_down_grid(M, k, E, H);
   const size_t n = (size_t)g.x * g.y > (size_t)d.x * d.y ? (size_t)g.x * g.y : (size_t)d.x * d.y;
   return n * kProbeStamps;
+}
+
+bool batch_decode_fits(const ForwardArgs& a) {
+  return a.lists != nullptr && a.H == 2560 && a.I == 768 && a.mt_min <= kRoutedMaxTokens + 1;
+}
+
+hipError_t launch_decode_batch(const ForwardArgs& a, hipStream_t s, const Timing& tm, hipEvent_t zeroed,
+                               int cus) {
+  const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
+  const dim3 b(DC_THREADS);
+  const int gx = a.I / 32, dx = (a.H + DN_ROWS_WG - 1) / DN_ROWS_WG;
+  const int gfit = (2 * 3 * cus + gx - 1) / gx, dfit = (2 * 6 * cus + dx - 1) / dx;   // two residency rounds
+  const dim3 gg(gx, slots < gfit ? slots : gfit), gd(dx, slots < dfit ? slots : dfit);
+  void* args[] = {const_cast<ForwardArgs*>(&a)};
+  hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(batch_gateup_kernel<5>), gg, b, args, 0, s,
+                                    tm.gu_start, tm.gu_stop, 0);
+  if (e != hipSuccess) return e;
+  if (zeroed && (e = hipEventRecord(zeroed, s)) != hipSuccess) return e;   // y is zeroed from here on
+  if (a.act8 && (e = launch_h_round_trip(a, 0, s)) != hipSuccess) return e;
+  const void* dn = a.yp ? reinterpret_cast<const void*>(batch_down_kernel<3, true>)
+                        : reinterpret_cast<const void*>(batch_down_kernel<3, false>);
+  return hipExtLaunchKernel(dn, gd, b, args, 0, s, tm.dn_start, tm.dn_stop, 0);
 }
 
 hipError_t launch_decode(const ForwardArgs& a, const RouteOut& r, hipStream_t s, const Timing& tm, bool probe) {

@@ -449,6 +449,7 @@ hipError_t launch_pair(void (*gu)(ForwardArgs, RouteOut), const ForwardArgs& a, 
 }  // namespace
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t s, const Timing& tm, hipEvent_t zeroed) {
+  if (batch_decode_fits(a)) return launch_decode_batch(a, s, tm, zeroed, device_cus());
   const RouteOut none{};
   return launch_pair(a.H <= GU_SHORT_H ? gateup_kernel<true, 0> : gateup_kernel<false, 0>, a, none, false, s,
                      tm, zeroed);

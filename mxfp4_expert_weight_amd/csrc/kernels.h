@@ -213,6 +213,10 @@ bool decode_fast_fits(int M, int H, int I);
 // Stamps the measurement instances write: 8 per workgroup of the larger grid.
 size_t decode_probe_stamps(int M, int k, int E, int H, int I, int has_shared);
 hipError_t launch_decode(const ForwardArgs& a, const RouteOut& r, hipStream_t s, const Timing& tm, bool probe);
+// Batches at H = 2560, I = 768 whose GEMV experts (one or two tokens) run on
+// the decode kernels' slot code (records from the sort epilogue's list).
+bool batch_decode_fits(const ForwardArgs& a);
+hipError_t launch_decode_batch(const ForwardArgs& a, hipStream_t s, const Timing& tm, hipEvent_t zeroed, int cus);
 
 // Read-bandwidth floor (moe_read_probe): one workgroup per 16 KB chunk of each
 // byte range, every load in flight at once.

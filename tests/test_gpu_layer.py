@@ -94,6 +94,9 @@ def test_tiny_config_every_element(fused):
     (12, 256, 256, 6, 4, True, "plain"),     # few-token matrix cores, shared expert included
     (12, 8192, 256, 8, 4, True, "plain"),    # few-token matrix cores, long rows (bf16 h: 1.26x the bar)
     (24, 512, 512, 10, 3, True, "zipf"),     # GEMV, few-token and scaled-MFMA experts in one layer
+    (6, 2560, 768, 64, 4, True, "plain"),    # batch 1-2-token experts on the decode kernels: atomics into y
+    (12, 2560, 768, 40, 8, True, "zipf"),    # the same beside the few-token matrix cores
+    (20, 2560, 768, 64, 8, True, "zipf"),    # the same combining by rows, scaled-MFMA shared expert
 ])
 def test_edge_shapes_every_element(M, H, I, E, k, shared, routing):
     torch = need_gpu()
