@@ -61,7 +61,7 @@ ForwardArgs layer_args(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M,
   a.M = M; a.k = top_k; a.E = w->num_experts; a.H = w->hidden; a.I = w->inter;
   a.has_shared = w->has_shared;
   const bool mt = mt_path(M, a.H, a.I);
-  a.mt_min = mt ? kMtMinTokens : INT_MAX;
+  a.mt_min = mt ? mt_min_tokens(a.H, a.I) : INT_MAX;
   a.mt_max = kMtMaxTokens;
   const bool on = mfma_path(M, a.H, a.I);
   a.mfma_min = on ? kMfmaMinTokens : INT_MAX;
@@ -137,7 +137,7 @@ moe_status check_opts(const moe_exec_opts* o) {
 // after the join.  Without helpers every kernel goes on `s` in order.
 hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, const moe_exec_opts* o) {
   const bool mfma = a.mfma_min == kMfmaMinTokens;
-  const bool mt = a.mt_min == kMtMinTokens;
+  const bool mt = a.mt_min != INT_MAX;
   const bool rows = a.yp != nullptr;
   const Timing tm = timing_of(o);
   hipError_t e = hipSuccess;
@@ -291,7 +291,7 @@ moe_status forward_impl(const uint16_t* x, const moe_mxfp4_weights* w, int32_t M
                               const_cast<uint16_t*>(a.x), s) != hipSuccess)
       return MOE_ERR_HIP;
   }
-  if (a.mfma_min == kMfmaMinTokens || a.mt_min == kMtMinTokens || a.yp) {
+  if (a.mfma_min == kMfmaMinTokens || a.mt_min != INT_MAX || a.yp) {
     // the path choice needs per-expert token counts, the combine the pairs'
     // sorted positions: records (slot lists, MFMA items, positions) first
     const RecOut ro = layer_recout(a, workspace);

@@ -78,6 +78,9 @@ struct ForwardArgs {
 // kRoutedMaxTokens tokens whose reduction lengths are multiples of its
 // 256-element chunk; experts with kMtMinTokens..kMtMaxTokens tokens.
 constexpr int kMtMinTokens = 3;
+// At H = 2560, I = 768 the batch experts with up to 4 tokens run on the decode
+// kernels' slot code, so the few-token kernels start at 5.
+inline int mt_min_tokens(int H, int I) { return (H == 2560 && I == 768) ? kRoutedMaxTokens + 1 : kMtMinTokens; }
 constexpr int kMtMaxTokens = 16;
 constexpr int kMtChunk = 256;
 

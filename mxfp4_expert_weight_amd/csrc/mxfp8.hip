@@ -116,7 +116,7 @@ hipError_t launch_h_round_trip(const ForwardArgs& a, int path, hipStream_t s) {
   const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
   const bool mt_on = a.mt_min != INT_MAX, mfma_on = a.mfma_min != INT_MAX;
   // most tokens an expert of the path can have
-  const int nmax = path == 1 ? kMtMaxTokens : (mt_on ? kMtMinTokens - 1 : (mfma_on ? a.mfma_min - 1 : a.M));
+  const int nmax = path == 1 ? kMtMaxTokens : (mt_on ? a.mt_min - 1 : (mfma_on ? a.mfma_min - 1 : a.M));
   const int64_t threads = 2 * (int64_t)min(nmax, a.M) * (a.I / 32);
   const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)slots);
   if (path == 0)

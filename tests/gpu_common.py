@@ -106,8 +106,10 @@ def check_routing(ids_gpu, w_gpu, logits_gpu, ref_logits, bound, k, what=""):
 def expected_paths(wl, ids):
     """(GEMV, few-token matrix-core, scaled-MFMA) expert counts of a layer.
     Scaled MFMA: experts with >= 16 tokens when M >= 16 and H, I are multiples
-    of 128.  Few-token matrix cores: 3..16 tokens (below the MFMA range) when
-    M > 4 and H, I are multiples of 256.  The rest: GEMV."""
+    of 128.  Few-token matrix cores: 3..16 tokens (5..16 at H = 2560,
+    I = 768, where the experts with up to 4 tokens run on the decode kernels'
+    slot code, counted as GEMV) below the MFMA range when M > 4 and H, I are
+    multiples of 256.  The rest: GEMV."""
     counts = np.bincount(np.asarray(ids).ravel(), minlength=wl.E)
     n = [int(c) for c in counts if c > 0] + ([wl.M] if wl.shared else [])
     mfma_on = wl.M >= 16 and wl.H % 128 == 0 and wl.I % 128 == 0
@@ -116,7 +118,7 @@ def expected_paths(wl, ids):
     for c in n:
         if mfma_on and c >= 16:
             paths[2] += 1
-        elif mt_on and 3 <= c <= 16:
+        elif mt_on and (5 if (wl.H, wl.I) == (2560, 768) else 3) <= c <= 16:
             paths[1] += 1
         else:
             paths[0] += 1

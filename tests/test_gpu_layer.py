@@ -161,12 +161,14 @@ def _batch_sample(ids, wl):
     """At least 32 tokens of a batch for the token-by-token oracle: for M <= 32
     every token; otherwise four tokens from each 64-token tile of the batch,
     chosen so that every tile has a token routed to an expert on each path the
-    layer runs (scaled MFMA: >= 16 tokens; few-token matrix cores: 3..15;
-    GEMV: 1..2), then the tile's first tokens."""
+    layer runs (scaled MFMA: >= 16 tokens; few-token matrix cores: 3..15, or
+    5..15 at H = 2560, I = 768; the rest: GEMV or the decode kernels' slot
+    code), then the tile's first tokens."""
     if wl.M <= 32:
         return list(range(wl.M))
     counts = np.bincount(ids.ravel(), minlength=wl.E)
-    cls = np.select([counts >= 16, counts >= 3, counts >= 1], [2, 1, 0], -1)
+    mt_lo = 5 if (wl.H, wl.I) == (2560, 768) else 3
+    cls = np.select([counts >= 16, counts >= mt_lo, counts >= 1], [2, 1, 0], -1)
     tokens = []
     for t0 in range(0, wl.M, 64):
         tile = list(range(t0, min(t0 + 64, wl.M)))
@@ -201,8 +203,9 @@ def test_ling_batch_sampled_tokens(name):
     assert len(tokens) >= 32
     if wl.M > 32:
         counts = np.bincount(g["ids"].ravel(), minlength=wl.E)
+        mt_lo = 5 if (wl.H, wl.I) == (2560, 768) else 3
         per_path = [int(np.sum([np.any(np.isin(g["ids"][t], np.nonzero(sel)[0])) for t in tokens]))
-                    for sel in (counts >= 16, (counts >= 3) & (counts < 16), (counts >= 1) & (counts <= 2))]
+                    for sel in (counts >= 16, (counts >= mt_lo) & (counts < 16), (counts >= 1) & (counts < mt_lo))]
         assert all(c > 0 for c in per_path), f"{name}: sampled tokens per path {per_path}"
     say(f"oracle over {len(tokens)} tokens of {name}")
     r = oracle.moe_layer_tokens(tokens, ls.x_bits, ls.w_router, ls.bias, ls.w13_q, ls.w13_s,
