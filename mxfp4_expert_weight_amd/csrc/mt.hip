@@ -109,17 +109,33 @@ __device__ __forceinline__ void mt_stage_store(uint8_t* rows, int row, int part,
   d[1] = u1;
 }
 
+// Workgroup -> (slot, column).  Workgroups are handed to the chip's 8 XCDs
+// in turn by their linear index, and each XCD has its own L2: with the grid
+// laid out so that linear index L goes to XCD L mod 8 and an XCD's k-th
+// workgroup takes column k mod C of slot 8 (k / C) + XCD, every column of a
+// slot runs on one XCD and the slot's activations are fetched into one L2
+// instead of up to eight.  The grid is 1-D, C x (slots rounded up to 8).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int mt_slots(const ForwardArgs& a) { return max_slots(a.M, a.k, a.E) - 1 + a.has_shared; }
+__device__ __forceinline__ void mt_tile(int cols, int& slot, int& col) {
+  const int L = (int)blockIdx.x, xcd = L % kXcds, k = L / kXcds;
+  slot = (k / cols) * kXcds + xcd;
+  col = k % cols;
+}
+
 // ------------------------------------------------------------- gate/up --
 // Workgroup (64 intermediate indices, slot): wave w takes indices
 // j0 + 16w .. + 15 as a gate tile and an up tile over the expert's tokens, so
 // h = SiLU(g) * u is formed in registers.
 __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs a) {
   SlotRec rec;
-  if (!mt_slot(a, blockIdx.y, rec)) return;                  // uniform over the workgroup
+  int slot, col;
+  mt_tile(a.I / MT_GU_J, slot, col);
+  if (slot >= mt_slots(a) || !mt_slot(a, slot, rec)) return;  // uniform over the workgroup
   __shared__ MtStage st;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int g = lane >> 4, j = lane & 15;
-  const int jw = blockIdx.x * MT_GU_J + 16 * wave;
+  const int jw = col * MT_GU_J + 16 * wave;
   const int H = a.H, I = a.I;
   const int64_t grow = (int64_t)rec.e * 2 * I + jw + j;      // this lane's gate row; up row is + I
   const uint8_t* gq = a.w13_q + grow * (H / 2);
@@ -181,12 +197,14 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
 // their MXFP8 h in hi alone.
 __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a) {
   SlotRec rec;
-  if (!mt_slot(a, blockIdx.y, rec)) return;
+  int slot, col;
+  mt_tile(a.H / MT_DN_R, slot, col);
+  if (slot >= mt_slots(a) || !mt_slot(a, slot, rec)) return;
   __shared__ MtStage st, stl;
   const bool two = !a.act8;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int g = lane >> 4, j = lane & 15;
-  const int rw = blockIdx.x * MT_DN_R + 32 * wave;
+  const int rw = col * MT_DN_R + 32 * wave;
   const int H = a.H, I = a.I;
   const int64_t row0 = (int64_t)rec.e * H + rw + j;           // tile 0 row; tile 1 is + 16
   const uint8_t* q0 = a.w2_q + row0 * (I / 2);
@@ -264,13 +282,15 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
 
 hipError_t launch_gateup_mt(const ForwardArgs& a, hipStream_t s) {
   const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
-  gateup_mt_kernel<<<dim3(a.I / MT_GU_J, slots), dim3(MT_WAVES * kWave), 0, s>>>(a);
+  const int slots8 = (slots + kXcds - 1) / kXcds * kXcds;
+  gateup_mt_kernel<<<dim3((a.I / MT_GU_J) * slots8), dim3(MT_WAVES * kWave), 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mt(const ForwardArgs& a, hipStream_t s) {
   const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
-  down_mt_kernel<<<dim3(a.H / MT_DN_R, slots), dim3(MT_WAVES * kWave), 0, s>>>(a);
+  const int slots8 = (slots + kXcds - 1) / kXcds * kXcds;
+  down_mt_kernel<<<dim3((a.H / MT_DN_R) * slots8), dim3(MT_WAVES * kWave), 0, s>>>(a);
   return hipGetLastError();
 }
 
