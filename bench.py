@@ -426,6 +426,8 @@ def main():
                     help="ling_m1 alone (the default run also measures ling_m4_mtp into the same line)")
     ap.add_argument("--three-calls", action="store_true",
                     help="time moe_route + moe_sort_by_expert + moe_mxfp4_forward instead of moe_layer")
+    ap.add_argument("--no-helpers", action="store_true",
+                    help="batches: every expert kernel on the one stream (no helper streams)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (reference for rocprof byte counters)")
     ap.add_argument("--profile-summary", nargs="+", metavar="DIR",
@@ -594,7 +596,7 @@ def bench_moe(torch, binding, synth, args, wl, cpu=True, cpu_budget=10.0, one_th
     buf = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
     weights = [d.weights() for d in sets]
     # batches run their matrix-core experts on two helper streams of ours
-    helpers = HelperStreams() if wl.M > 4 else None
+    helpers = HelperStreams() if wl.M > 4 and not args.no_helpers else None
 
     # one eager pass: loads the kernels and records each set's distinct-expert count
     D, G, true_ids = [], [], []

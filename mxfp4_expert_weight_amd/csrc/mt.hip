@@ -56,29 +56,53 @@ __device__ __forceinline__ bool mt_slot(const ForwardArgs& a, int y, SlotRec& r)
   return r.e >= 0 && r.n >= a.mt_min && r.n <= a.mt_max && r.n < a.mfma_min;
 }
 
-// Weight codes and scales of one row for chunk kc: 32 code bytes and the two
-// scale bytes of lane group g.
+// Weight codes of one row for chunk kc: the 32 code bytes of lane group g.
 struct MtRowChunk {
   uint4 c0, c1;
-  uint32_t s0, s1;
 };
-__device__ __forceinline__ MtRowChunk mt_load_row(const uint8_t* row_q, const uint8_t* row_s, int kc, int g) {
+__device__ __forceinline__ MtRowChunk mt_load_row(const uint8_t* row_q, int kc, int g) {
   MtRowChunk m;
   const uint4* q = reinterpret_cast<const uint4*>(row_q + kc * (MT_KC / 2) + 32 * g);
   m.c0 = q[0];
   m.c1 = q[1];
-  m.s0 = row_s[kc * (MT_KC / 32) + 2 * g];
-  m.s1 = row_s[kc * (MT_KC / 32) + 2 * g + 1];
   return m;
 }
 
-// A operand of step s: the 8 weights of code word s, decoded to bf16.
-__device__ __forceinline__ v8bf mt_frag_a(const MtRowChunk& m, int s) {
+// The scales of a workgroup's weight rows sit in LDS for the whole kernel:
+// a scale read per chunk and row from global memory costs a load instruction
+// as dear as a code load (16 rows, one cache line each) for an eighth of the
+// bytes.  `rows` consecutive rows of rb = K/32 bytes at src (16-byte aligned,
+// rows * rb a multiple of 16) go to LDS with a pitch of rb + 4 bytes, an odd
+// number of words (K is a multiple of 256), so 16 rows read at one column
+// fall in 16 banks.
+__device__ __forceinline__ int mt_scale_pitch(int K) { return K / 32 + 4; }
+__device__ __forceinline__ void mt_stage_scales(uint8_t* dst, const uint8_t* src, int rows, int K) {
+  const int rb = K / 32, wpr = rb / 4, pitch = rb + 4;
+  const int n16 = rows * rb / 16;
+  for (int i = threadIdx.x; i < n16; i += blockDim.x) {
+    const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int word = 4 * i + q, r = word / wpr, c = word - r * wpr;
+      *reinterpret_cast<uint32_t*>(dst + r * pitch + 4 * c) = w[q];
+    }
+  }
+}
+// The two scale bytes of lane group g for chunk kc of a staged row (blocks
+// 8 kc + 2g and 8 kc + 2g + 1).
+__device__ __forceinline__ uint32_t mt_scales(const uint8_t* row_lds, int kc, int g) {
+  return *reinterpret_cast<const uint16_t*>(row_lds + kc * (MT_KC / 32) + 2 * g);
+}
+
+// A operand of step s: the 8 weights of code word s, decoded to bf16 with
+// the block scale (low byte of s01 for steps 0-3, high byte for 4-7).
+__device__ __forceinline__ v8bf mt_frag_a(const MtRowChunk& m, uint32_t s01, int s) {
   const uint32_t w = (s & 3) == 0 ? ((s < 4) ? m.c0.x : m.c1.x)
                    : (s & 3) == 1 ? ((s < 4) ? m.c0.y : m.c1.y)
                    : (s & 3) == 2 ? ((s < 4) ? m.c0.z : m.c1.z)
                                   : ((s < 4) ? m.c0.w : m.c1.w);
-  const float sc = e8m0_to_f32(s < 4 ? m.s0 : m.s1);
+  const float sc = e8m0_to_f32(s < 4 ? (s01 & 0xFFu) : (s01 >> 8));
   const bf16x2 p0 = mxfp4_pair_bf16<0>(w, sc), p1 = mxfp4_pair_bf16<1>(w, sc);
   const bf16x2 p2 = mxfp4_pair_bf16<2>(w, sc), p3 = mxfp4_pair_bf16<3>(w, sc);
   v8bf v;
@@ -94,19 +118,56 @@ __device__ __forceinline__ v8bf mt_frag_b(const uint8_t* rows, int s, int g, int
 }
 
 // Staging of token rows: thread (row tid/16, part tid%16) moves 16 bf16 of
-// its token's 256-element chunk.  Rows past the expert's tokens are zero.
-__device__ __forceinline__ void mt_stage_load(uint4& u0, uint4& u1, const uint16_t* src_row, bool valid, int kc,
-                                              int part) {
+// its token's 256-element chunk.  Rows past the expert's tokens repeat a valid
+// row: token column j of a product only reaches output column j, and those
+// columns are never stored.
+__device__ __forceinline__ void mt_stage_load(uint4& u0, uint4& u1, const uint16_t* src_row, int kc, int part) {
   const uint4* p = reinterpret_cast<const uint4*>(src_row + kc * MT_KC + 16 * part);
-  const uint4 a = p[0], b = p[1];
-  const uint32_t m = valid ? 0xFFFFFFFFu : 0u;   // word masks: no vector selects (they go through scratch)
-  u0 = make_uint4(a.x & m, a.y & m, a.z & m, a.w & m);
-  u1 = make_uint4(b.x & m, b.y & m, b.z & m, b.w & m);
+  u0 = p[0];
+  u1 = p[1];
 }
 __device__ __forceinline__ void mt_stage_store(uint8_t* rows, int row, int part, uint4 u0, uint4 u1) {
   uint4* d = reinterpret_cast<uint4*>(rows + row * MT_PITCH + 32 * part);
   d[0] = u0;
   d[1] = u1;
+}
+
+// Products of one staged chunk with a wave's gate and up tiles (scale words
+// sg, su of the lane's gate and up rows).
+__device__ __forceinline__ void mt_gu_products(v4f& accg, v4f& accu, const MtRowChunk& wg, const MtRowChunk& wu,
+                                               uint32_t sg, uint32_t su, const uint8_t* rows, int g, int j) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const v8bf b = mt_frag_b(rows, s, g, j);
+    accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(wg, sg, s), b, accg, 0, 0, 0);
+    accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(wu, su, s), b, accu, 0, 0, 0);
+  }
+}
+
+// Products of one staged chunk of h with a wave's two down tiles: the hi
+// term, and with `two` the lo term too (h = hi + lo).
+__device__ __forceinline__ void mt_down_products(v4f& acc0, v4f& acc1, const MtRowChunk& w0, const MtRowChunk& w1,
+                                                 uint32_t s0, uint32_t s1, const uint8_t* rows,
+                                                 const uint8_t* rows_lo, bool two, int g, int j) {
+  if (two) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const v8bf b = mt_frag_b(rows, s, g, j);
+      const v8bf bl = mt_frag_b(rows_lo, s, g, j);
+      const v8bf a0 = mt_frag_a(w0, s0, s), a1 = mt_frag_a(w1, s1, s);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc1, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const v8bf b = mt_frag_b(rows, s, g, j);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(w0, s0, s), b, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(w1, s1, s), b, acc1, 0, 0, 0);
+    }
+  }
 }
 
 // Workgroup -> (slot, column).  Workgroups are handed to the chip's 8 XCDs
@@ -133,15 +194,18 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
   mt_tile(a.I / MT_GU_J, slot, col);
   if (slot >= mt_slots(a) || !mt_slot(a, slot, rec)) return;  // uniform over the workgroup
   __shared__ MtStage st;
+  extern __shared__ __align__(16) uint8_t mt_scale_lds[];     // 64 gate rows, then 64 up rows
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int g = lane >> 4, j = lane & 15;
   const int jw = col * MT_GU_J + 16 * wave;
   const int H = a.H, I = a.I;
-  const int64_t grow = (int64_t)rec.e * 2 * I + jw + j;      // this lane's gate row; up row is + I
+  const int64_t grow0 = (int64_t)rec.e * 2 * I + col * MT_GU_J;   // the workgroup's first gate row
+  const int64_t grow = grow0 + 16 * wave + j;                     // this lane's gate row; up row is + I
   const uint8_t* gq = a.w13_q + grow * (H / 2);
-  const uint8_t* gs = a.w13_s + grow * (H / 32);
   const uint8_t* uq = gq + (int64_t)I * (H / 2);
-  const uint8_t* us = gs + (int64_t)I * (H / 32);
+  const int sp = mt_scale_pitch(H);
+  const uint8_t* gsl = mt_scale_lds + (16 * wave + j) * sp;
+  const uint8_t* usl = gsl + MT_GU_J * sp;
   const int srow = threadIdx.x >> 4, part = threadIdx.x & 15;
   int stok = 0;
   float sw;
@@ -150,30 +214,46 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
   const uint16_t* xsrc = a.x + (int64_t)stok * H;
   const int nk = H / MT_KC;
   uint4 x0, x1;
-  mt_stage_load(x0, x1, xsrc, sv, 0, part);
+  mt_stage_load(x0, x1, xsrc, 0, part);
+  MtRowChunk ga = mt_load_row(gq, 0, g), ua = mt_load_row(uq, 0, g), gb, ub;
+  mt_stage_scales(mt_scale_lds, a.w13_s + grow0 * (H / 32), MT_GU_J, H);
+  mt_stage_scales(mt_scale_lds + MT_GU_J * sp, a.w13_s + (grow0 + I) * (H / 32), MT_GU_J, H);
   mt_stage_store(st.rows[0], srow, part, x0, x1);
-  MtRowChunk wg = mt_load_row(gq, gs, 0, g), wu = mt_load_row(uq, us, 0, g);
   v4f accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    const int cur = kc & 1;
-    const bool more = kc + 1 < nk;
-    MtRowChunk ng = wg, nu = wu;
-    if (more) {                                  // next chunk in flight during this one's products
-      mt_stage_load(x0, x1, xsrc, sv, kc + 1, part);
-      ng = mt_load_row(gq, gs, kc + 1, g);
-      nu = mt_load_row(uq, us, kc + 1, g);
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const v8bf b = mt_frag_b(st.rows[cur], s, g, j);
-      accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(wg, s), b, accg, 0, 0, 0);
-      accu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(wu, s), b, accu, 0, 0, 0);
-    }
-    if (more) mt_stage_store(st.rows[cur ^ 1], srow, part, x0, x1);
-    block_barrier_lds();                         // the next chunk's weights stay in flight
-    wg = ng;
-    wu = nu;
+  // Chunks alternate between register sets (a, b) and LDS buffers (0, 1): the
+  // next chunk's loads land in the idle set while this chunk is multiplied.
+  // The steady-state loop issues its loads unconditionally (a load under a
+  // branch would make every later wait cover it too), and a scheduling fence
+  // keeps the products after them; the last one or two chunks are done after
+  // the loop.
+  int kc = 0;
+  for (; kc + 2 < nk; kc += 2) {
+    mt_stage_load(x0, x1, xsrc, kc + 1, part);
+    gb = mt_load_row(gq, kc + 1, g);
+    ub = mt_load_row(uq, kc + 1, g);
+    __builtin_amdgcn_sched_barrier(0);
+    mt_gu_products(accg, accu, ga, ua, mt_scales(gsl, kc, g), mt_scales(usl, kc, g), st.rows[0], g, j);
+    mt_stage_store(st.rows[1], srow, part, x0, x1);
+    block_barrier_lds();
+    mt_stage_load(x0, x1, xsrc, kc + 2, part);
+    ga = mt_load_row(gq, kc + 2, g);
+    ua = mt_load_row(uq, kc + 2, g);
+    __builtin_amdgcn_sched_barrier(0);
+    mt_gu_products(accg, accu, gb, ub, mt_scales(gsl, kc + 1, g), mt_scales(usl, kc + 1, g), st.rows[1], g, j);
+    mt_stage_store(st.rows[0], srow, part, x0, x1);
+    block_barrier_lds();
+  }
+  if (kc + 1 < nk) {
+    mt_stage_load(x0, x1, xsrc, kc + 1, part);
+    gb = mt_load_row(gq, kc + 1, g);
+    ub = mt_load_row(uq, kc + 1, g);
+    mt_gu_products(accg, accu, ga, ua, mt_scales(gsl, kc, g), mt_scales(usl, kc, g), st.rows[0], g, j);
+    mt_stage_store(st.rows[1], srow, part, x0, x1);
+    block_barrier_lds();
+    mt_gu_products(accg, accu, gb, ub, mt_scales(gsl, kc + 1, g), mt_scales(usl, kc + 1, g), st.rows[1], g, j);
+  } else {
+    mt_gu_products(accg, accu, ga, ua, mt_scales(gsl, kc, g), mt_scales(usl, kc, g), st.rows[0], g, j);
   }
   // lane (g, j): indices jw + 4g + r of token j
   if (j < rec.n) {   // h = hi + lo, two bf16 terms (W4A8: the MXFP8 round trip reads both)
@@ -201,65 +281,73 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
   mt_tile(a.H / MT_DN_R, slot, col);
   if (slot >= mt_slots(a) || !mt_slot(a, slot, rec)) return;
   __shared__ MtStage st, stl;
+  extern __shared__ __align__(16) uint8_t mt_scale_lds[];     // the workgroup's 128 rows
   const bool two = !a.act8;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int g = lane >> 4, j = lane & 15;
   const int rw = col * MT_DN_R + 32 * wave;
   const int H = a.H, I = a.I;
-  const int64_t row0 = (int64_t)rec.e * H + rw + j;           // tile 0 row; tile 1 is + 16
+  const int64_t wrow0 = (int64_t)rec.e * H + col * MT_DN_R;       // the workgroup's first row
+  const int64_t row0 = (int64_t)rec.e * H + rw + j;               // tile 0 row; tile 1 is + 16
   const uint8_t* q0 = a.w2_q + row0 * (I / 2);
-  const uint8_t* s0 = a.w2_s + row0 * (I / 32);
   const uint8_t* q1 = q0 + 16 * (I / 2);
-  const uint8_t* s1 = s0 + 16 * (I / 32);
+  const int sp = mt_scale_pitch(I);
+  const uint8_t* s0l = mt_scale_lds + (32 * wave + j) * sp;
+  const uint8_t* s1l = s0l + 16 * sp;
   const int srow = threadIdx.x >> 4, part = threadIdx.x & 15;
   const bool sv = srow < rec.n;
   const uint16_t* hsrc = a.h + ((int64_t)rec.hrow0 + (sv ? srow : 0)) * I;
   const uint16_t* lsrc = a.hlo + ((int64_t)rec.hrow0 + (sv ? srow : 0)) * I;
   const int nk = I / MT_KC;
-  uint4 x0, x1, l0 = make_uint4(0, 0, 0, 0), l1 = l0;
-  mt_stage_load(x0, x1, hsrc, sv, 0, part);
-  if (two) mt_stage_load(l0, l1, lsrc, sv, 0, part);
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  uint4 x0, x1, l0 = z, l1 = z;
+  mt_stage_load(x0, x1, hsrc, 0, part);
+  if (two) mt_stage_load(l0, l1, lsrc, 0, part);
+  MtRowChunk a0 = mt_load_row(q0, 0, g), a1 = mt_load_row(q1, 0, g), b0, b1;
+  mt_stage_scales(mt_scale_lds, a.w2_s + wrow0 * (I / 32), MT_DN_R, I);
   mt_stage_store(st.rows[0], srow, part, x0, x1);
   if (two) mt_stage_store(stl.rows[0], srow, part, l0, l1);
-  MtRowChunk w0 = mt_load_row(q0, s0, 0, g), w1 = mt_load_row(q1, s1, 0, g);
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    const int cur = kc & 1;
-    const bool more = kc + 1 < nk;
-    MtRowChunk n0 = w0, n1 = w1;
-    if (more) {
-      mt_stage_load(x0, x1, hsrc, sv, kc + 1, part);
-      if (two) mt_stage_load(l0, l1, lsrc, sv, kc + 1, part);
-      n0 = mt_load_row(q0, s0, kc + 1, g);
-      n1 = mt_load_row(q1, s1, kc + 1, g);
-    }
-    if (two) {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const v8bf b = mt_frag_b(st.rows[cur], s, g, j);
-        const v8bf bl = mt_frag_b(stl.rows[cur], s, g, j);
-        const v8bf a0 = mt_frag_a(w0, s), a1 = mt_frag_a(w1, s);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bl, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bl, acc1, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const v8bf b = mt_frag_b(st.rows[cur], s, g, j);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(w0, s), b, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mt_frag_a(w1, s), b, acc1, 0, 0, 0);
-      }
-    }
-    if (more) {
-      mt_stage_store(st.rows[cur ^ 1], srow, part, x0, x1);
-      if (two) mt_stage_store(stl.rows[cur ^ 1], srow, part, l0, l1);
-    }
+  // the same alternation as gate/up
+  int kc = 0;
+  for (; kc + 2 < nk; kc += 2) {
+    mt_stage_load(x0, x1, hsrc, kc + 1, part);
+    if (two) mt_stage_load(l0, l1, lsrc, kc + 1, part);
+    b0 = mt_load_row(q0, kc + 1, g);
+    b1 = mt_load_row(q1, kc + 1, g);
+    __builtin_amdgcn_sched_barrier(0);
+    mt_down_products(acc0, acc1, a0, a1, mt_scales(s0l, kc, g), mt_scales(s1l, kc, g), st.rows[0], stl.rows[0], two,
+                     g, j);
+    mt_stage_store(st.rows[1], srow, part, x0, x1);
+    if (two) mt_stage_store(stl.rows[1], srow, part, l0, l1);
     block_barrier_lds();
-    w0 = n0;
-    w1 = n1;
+    mt_stage_load(x0, x1, hsrc, kc + 2, part);
+    if (two) mt_stage_load(l0, l1, lsrc, kc + 2, part);
+    a0 = mt_load_row(q0, kc + 2, g);
+    a1 = mt_load_row(q1, kc + 2, g);
+    __builtin_amdgcn_sched_barrier(0);
+    mt_down_products(acc0, acc1, b0, b1, mt_scales(s0l, kc + 1, g), mt_scales(s1l, kc + 1, g), st.rows[1],
+                     stl.rows[1], two, g, j);
+    mt_stage_store(st.rows[0], srow, part, x0, x1);
+    if (two) mt_stage_store(stl.rows[0], srow, part, l0, l1);
+    block_barrier_lds();
+  }
+  if (kc + 1 < nk) {
+    mt_stage_load(x0, x1, hsrc, kc + 1, part);
+    if (two) mt_stage_load(l0, l1, lsrc, kc + 1, part);
+    b0 = mt_load_row(q0, kc + 1, g);
+    b1 = mt_load_row(q1, kc + 1, g);
+    mt_down_products(acc0, acc1, a0, a1, mt_scales(s0l, kc, g), mt_scales(s1l, kc, g), st.rows[0], stl.rows[0], two,
+                     g, j);
+    mt_stage_store(st.rows[1], srow, part, x0, x1);
+    if (two) mt_stage_store(stl.rows[1], srow, part, l0, l1);
+    block_barrier_lds();
+    mt_down_products(acc0, acc1, b0, b1, mt_scales(s0l, kc + 1, g), mt_scales(s1l, kc + 1, g), st.rows[1],
+                     stl.rows[1], two, g, j);
+  } else {
+    mt_down_products(acc0, acc1, a0, a1, mt_scales(s0l, kc, g), mt_scales(s1l, kc, g), st.rows[0], stl.rows[0], two,
+                     g, j);
   }
   if (j < rec.n) {
     int t;
@@ -280,17 +368,27 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
   }
 }
 
+// Grid rows for the few-token experts: with the slot list, at most one expert
+// per mt_min routed pairs (plus the shared one) can be on this path, so rows
+// past that bound are not launched; without it, every slot.
+static int mt_grid_slots(const ForwardArgs& a) {
+  int routed = max_slots(a.M, a.k, a.E) - 1;
+  if (a.lists) routed = std::min(routed, a.M * a.k / a.mt_min);
+  const int slots = routed + (a.has_shared ? 1 : 0);
+  return (slots + kXcds - 1) / kXcds * kXcds;
+}
+
 hipError_t launch_gateup_mt(const ForwardArgs& a, hipStream_t s) {
-  const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
-  const int slots8 = (slots + kXcds - 1) / kXcds * kXcds;
-  gateup_mt_kernel<<<dim3((a.I / MT_GU_J) * slots8), dim3(MT_WAVES * kWave), 0, s>>>(a);
+  const int slots8 = mt_grid_slots(a);
+  const size_t shmem = (size_t)2 * MT_GU_J * (a.H / 32 + 4);   // gate and up rows' scales
+  gateup_mt_kernel<<<dim3((a.I / MT_GU_J) * slots8), dim3(MT_WAVES * kWave), shmem, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mt(const ForwardArgs& a, hipStream_t s) {
-  const int slots = max_slots(a.M, a.k, a.E) - 1 + (a.has_shared ? 1 : 0);
-  const int slots8 = (slots + kXcds - 1) / kXcds * kXcds;
-  down_mt_kernel<<<dim3((a.H / MT_DN_R) * slots8), dim3(MT_WAVES * kWave), 0, s>>>(a);
+  const int slots8 = mt_grid_slots(a);
+  const size_t shmem = (size_t)MT_DN_R * (a.I / 32 + 4);
+  down_mt_kernel<<<dim3((a.H / MT_DN_R) * slots8), dim3(MT_WAVES * kWave), shmem, s>>>(a);
   return hipGetLastError();
 }
 
