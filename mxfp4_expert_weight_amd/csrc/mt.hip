@@ -31,16 +31,17 @@ struct MtStage {
   __align__(16) uint8_t rows[2][MT_TOK * MT_PITCH];
 };
 
-// Token number c (sorted order) of the expert: its row of x, routing weight and h row.
+// Token number c (sorted order) of the expert: its row of x and routing
+// weight.  Branch-free (c is clamped to the expert's tokens, and the shared
+// expert, pbeg < 0, takes token c with weight 1), so the loads are not waited
+// for where they are issued.
 __device__ __forceinline__ void mt_token(const ForwardArgs& a, const SlotRec& r, int c, int& t, float& w) {
-  if (r.pbeg >= 0) {
-    const int pair = a.sorted_pairs[r.pbeg + c];
-    t = pair / a.k;
-    w = a.topk_weights[pair];
-  } else {
-    t = c;
-    w = 1.f;
-  }
+  const int cc = min(c, r.n - 1);
+  const int pair0 = a.sorted_pairs[max(r.pbeg, 0) + cc];   // in bounds: cc < M <= M*k for the shared expert
+  const int pair = r.pbeg >= 0 ? pair0 : 0;                 // its value is only trusted for routed experts
+  const float pw = a.topk_weights[pair];
+  t = r.pbeg >= 0 ? pair / a.k : cc;
+  w = r.pbeg >= 0 ? pw : 1.f;
 }
 
 // The record of grid row y, if its expert is on this path: with the slot
@@ -71,22 +72,26 @@ __device__ __forceinline__ MtRowChunk mt_load_row(const uint8_t* row_q, int kc, 
 // The scales of a workgroup's weight rows sit in LDS for the whole kernel:
 // a scale read per chunk and row from global memory costs a load instruction
 // as dear as a code load (16 rows, one cache line each) for an eighth of the
-// bytes.  `rows` consecutive rows of rb = K/32 bytes at src (16-byte aligned,
-// rows * rb a multiple of 16) go to LDS with a pitch of rb + 4 bytes, an odd
-// number of words (K is a multiple of 256), so 16 rows read at one column
-// fall in 16 banks.
-__device__ __forceinline__ int mt_scale_pitch(int K) { return K / 32 + 4; }
-__device__ __forceinline__ void mt_stage_scales(uint8_t* dst, const uint8_t* src, int rows, int K) {
-  const int rb = K / 32, wpr = rb / 4, pitch = rb + 4;
-  const int n16 = rows * rb / 16;
-  for (int i = threadIdx.x; i < n16; i += blockDim.x) {
-    const uint4 v = reinterpret_cast<const uint4*>(src)[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// bytes.  The rows are two runs of consecutive rows (16-byte aligned, each a
+// whole number of 16-byte words: half16 of them at src0, n16 - half16 at
+// src1), copied as they are; four words per thread are in flight at once.
+// Loads use clamped indices and stores past the end go to a spare word at
+// dst[n16], so no load is moved into a branch and waited on there.
+__device__ __forceinline__ int mt_scale_pitch(int K) { return K / 32; }
+__device__ __forceinline__ void mt_stage_scales(uint8_t* dst, const uint8_t* src0, const uint8_t* src1, int half16,
+                                                int n16) {
+  const uint4* s0 = reinterpret_cast<const uint4*>(src0);
+  const uint4* s1 = reinterpret_cast<const uint4*>(src1) - half16;
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  for (int b = 0; b < n16; b += 4 * (int)blockDim.x) {
+    uint4 v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int word = 4 * i + q, r = word / wpr, c = word - r * wpr;
-      *reinterpret_cast<uint32_t*>(dst + r * pitch + 4 * c) = w[q];
+      const int i = min(b + q * (int)blockDim.x + (int)threadIdx.x, n16 - 1);
+      v[q] = (i < half16 ? s0 : s1)[i];
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) d[min(b + q * (int)blockDim.x + (int)threadIdx.x, n16)] = v[q];
   }
 }
 // The two scale bytes of lane group g for chunk kc of a staged row (blocks
@@ -207,17 +212,18 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
   const uint8_t* gsl = mt_scale_lds + (16 * wave + j) * sp;
   const uint8_t* usl = gsl + MT_GU_J * sp;
   const int srow = threadIdx.x >> 4, part = threadIdx.x & 15;
-  int stok = 0;
+  // prologue: the token lookup, the first chunk's weights and the scales
+  // are all requested before any of them is waited for
+  int stok;
   float sw;
-  const bool sv = srow < rec.n;
-  if (sv) mt_token(a, rec, srow, stok, sw);
+  mt_token(a, rec, srow, stok, sw);   // rows past the expert's tokens repeat its last one
+  MtRowChunk ga = mt_load_row(gq, 0, g), ua = mt_load_row(uq, 0, g), gb, ub;
   const uint16_t* xsrc = a.x + (int64_t)stok * H;
   const int nk = H / MT_KC;
   uint4 x0, x1;
   mt_stage_load(x0, x1, xsrc, 0, part);
-  MtRowChunk ga = mt_load_row(gq, 0, g), ua = mt_load_row(uq, 0, g), gb, ub;
-  mt_stage_scales(mt_scale_lds, a.w13_s + grow0 * (H / 32), MT_GU_J, H);
-  mt_stage_scales(mt_scale_lds + MT_GU_J * sp, a.w13_s + (grow0 + I) * (H / 32), MT_GU_J, H);
+  mt_stage_scales(mt_scale_lds, a.w13_s + grow0 * (H / 32), a.w13_s + (grow0 + I) * (H / 32), MT_GU_J * sp / 16,
+                  2 * MT_GU_J * sp / 16);
   mt_stage_store(st.rows[0], srow, part, x0, x1);
   v4f accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
@@ -300,11 +306,13 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
   const uint16_t* lsrc = a.hlo + ((int64_t)rec.hrow0 + (sv ? srow : 0)) * I;
   const int nk = I / MT_KC;
   const uint4 z = make_uint4(0, 0, 0, 0);
+  // prologue: the first chunk's weights and h rows, then the scales
   uint4 x0, x1, l0 = z, l1 = z;
+  MtRowChunk a0 = mt_load_row(q0, 0, g), a1 = mt_load_row(q1, 0, g), b0, b1;
   mt_stage_load(x0, x1, hsrc, 0, part);
   if (two) mt_stage_load(l0, l1, lsrc, 0, part);
-  MtRowChunk a0 = mt_load_row(q0, 0, g), a1 = mt_load_row(q1, 0, g), b0, b1;
-  mt_stage_scales(mt_scale_lds, a.w2_s + wrow0 * (I / 32), MT_DN_R, I);
+  const uint8_t* ssrc = a.w2_s + wrow0 * (I / 32);
+  mt_stage_scales(mt_scale_lds, ssrc, ssrc, MT_DN_R * sp / 16, MT_DN_R * sp / 16);
   mt_stage_store(st.rows[0], srow, part, x0, x1);
   if (two) mt_stage_store(stl.rows[0], srow, part, l0, l1);
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -380,14 +388,14 @@ static int mt_grid_slots(const ForwardArgs& a) {
 
 hipError_t launch_gateup_mt(const ForwardArgs& a, hipStream_t s) {
   const int slots8 = mt_grid_slots(a);
-  const size_t shmem = (size_t)2 * MT_GU_J * (a.H / 32 + 4);   // gate and up rows' scales
+  const size_t shmem = (size_t)2 * MT_GU_J * (a.H / 32) + 16;   // gate and up rows' scales, a spare word
   gateup_mt_kernel<<<dim3((a.I / MT_GU_J) * slots8), dim3(MT_WAVES * kWave), shmem, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mt(const ForwardArgs& a, hipStream_t s) {
   const int slots8 = mt_grid_slots(a);
-  const size_t shmem = (size_t)MT_DN_R * (a.I / 32 + 4);
+  const size_t shmem = (size_t)MT_DN_R * (a.I / 32) + 16;
   down_mt_kernel<<<dim3((a.H / MT_DN_R) * slots8), dim3(MT_WAVES * kWave), shmem, s>>>(a);
   return hipGetLastError();
 }
