@@ -65,6 +65,65 @@ __global__ __launch_bounds__(128) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// Batches of more than 8 and fewer than kRouterGemmMinTokens tokens with
+// rows of at most 2560: a workgroup of RL_WAVES waves takes RL_WAVES expert
+// rows (one per wave, in registers as above) and passes of RL_TOK tokens
+// whose x rows it stages in LDS once for all of its waves, so x is read from
+// L2 once per workgroup instead of once per wave.  Same products and sums, in
+// the same order, as router_logits_kernel.
+constexpr int RL_WAVES = 8, RL_TOK = 8;
+__global__ __launch_bounds__(RL_WAVES * kWave) void router_lds_kernel(const uint16_t* __restrict__ x,
+                                                                     const float* __restrict__ w_router,
+                                                                     const float* __restrict__ bias,
+                                                                     int64_t bias_stride, int M, int H, int E,
+                                                                     float* __restrict__ logits) {
+  constexpr int VMAX = 10;                         // H <= 2560
+  __shared__ uint2 xs[RL_TOK][VMAX * kWave];       // 4 bf16 per entry; entries past the row are zero
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int e = blockIdx.x * RL_WAVES + wave;
+  const int nvec = H / 4;
+  const float4* wrow = reinterpret_cast<const float4*>(w_router + (size_t)min(e, E - 1) * H);
+  float4 w[VMAX];
+#pragma unroll
+  for (int i = 0; i < VMAX; ++i) {
+    const int v = lane + kWave * i;
+    const float4 t = wrow[min(v, nvec - 1)];
+    w[i] = (v < nvec) ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int t0 = blockIdx.y * RL_TOK; t0 < M; t0 += gridDim.y * RL_TOK) {
+    // stage RL_TOK rows (clamped to the last token), 8 bf16 per thread step
+    constexpr int kPairs = RL_TOK * VMAX * kWave / 2;    // uint4 entries of the stage
+    for (int i = threadIdx.x; i < kPairs; i += RL_WAVES * kWave) {
+      const int q = i / (VMAX * kWave / 2), v2 = i - q * (VMAX * kWave / 2);   // uint2 entries 2 v2, 2 v2 + 1
+      const uint4* xrow = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + q, M - 1) * H);
+      const uint4 u = xrow[min(v2, nvec / 2 - 1)];
+      const bool in0 = 2 * v2 < nvec, in1 = 2 * v2 + 1 < nvec;
+      xs[q][2 * v2] = in0 ? make_uint2(u.x, u.y) : make_uint2(0, 0);
+      xs[q][2 * v2 + 1] = in1 ? make_uint2(u.z, u.w) : make_uint2(0, 0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < RL_TOK; ++q) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i) {
+        const uint2 xv = xs[q][lane + kWave * i];
+        acc = fmaf(bf16_bits_to_f32(xv.x & 0xFFFFu), w[i].x, acc);
+        acc = fmaf(bf16_bits_to_f32(xv.x >> 16), w[i].y, acc);
+        acc = fmaf(bf16_bits_to_f32(xv.y & 0xFFFFu), w[i].z, acc);
+        acc = fmaf(bf16_bits_to_f32(xv.y >> 16), w[i].w, acc);
+      }
+      acc = group_sum<kWave>(acc);
+      const int t = t0 + q;
+      if (lane == 0 && t < M && e < E) {
+        if (bias) acc += bias[(size_t)t * bias_stride + e];
+        logits[(size_t)t * E + e] = acc;
+      }
+    }
+    __syncthreads();                               // the stage is rewritten by the next pass
+  }
+}
+
 // Batches on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16).  Each fp32
 // router weight is split exactly into three bf16 parts by truncation:
 // w1 = w with its low 16 bits cleared, w2 = (w - w1) the same way, w3 = the
@@ -284,6 +343,11 @@ hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const 
     auto kern = (H == 10 * RM_KC) ? router_mfma_kernel<10> : router_mfma_kernel<0>;
     kern<<<dim3((E + RM_E - 1) / RM_E, (M + RM_T - 1) / RM_T), dim3(RM_THREADS), 0, s>>>(
         x, w_router, bias, bias_stride, M, H, E, logits);
+    return hipGetLastError();
+  }
+  if (M > 8 && H <= 2560 && H % 8 == 0) {
+    const dim3 grid((E + RL_WAVES - 1) / RL_WAVES, (M + RL_TOK - 1) / RL_TOK);
+    router_lds_kernel<<<grid, RL_WAVES * kWave, 0, s>>>(x, w_router, bias, bias_stride, M, H, E, logits);
     return hipGetLastError();
   }
   const int waves_per_block = 2;

@@ -4,11 +4,14 @@
 
 namespace moe {
 
-// Whether the sort's outputs (and a copy of its input ids) also fit in LDS
-// next to its working set (64 KiB per workgroup), for the records epilogue.
-__host__ __device__ inline size_t sort_lds_extra(int nw, int N, int E) { return 2 * (size_t)N + E + 1 + 4 * nw + 4; }
+// Whether the sort's outputs and copies of its inputs (ids, and the routing
+// weights the records carry) also fit in LDS next to its working set, for the
+// records epilogue: then the epilogue reads nothing from global memory.  The
+// budget is the 160 KiB a CDNA4 workgroup can hold.
+constexpr size_t kSortLdsBytes = 160 * 1024;
+__host__ __device__ inline size_t sort_lds_extra(int nw, int N, int E) { return 3 * (size_t)N + E + 4 * nw + 7; }
 __host__ __device__ inline bool sort_keeps_lds(int nw, int N, int E) {
-  return sizeof(int) * (sort_lds_ints(nw, E) + sort_lds_extra(nw, N, E)) <= 65536;
+  return sizeof(int) * (sort_lds_ints(nw, E) + sort_lds_extra(nw, N, E)) <= kSortLdsBytes;
 }
 
 __global__ __launch_bounds__(512) void sort_by_expert_kernel(const int* __restrict__ ids, int N, int E,
@@ -22,28 +25,38 @@ __global__ __launch_bounds__(512) void sort_by_expert_kernel(const int* __restri
   const size_t base = sort_lds_ints(nw, E);
   if (ro.rec && sort_keeps_lds(nw, N, E)) {
     // the records epilogue reads the sort from LDS: sorted pairs, active list,
-    // D and the offsets left at lds + nw*E
+    // D and the offsets left at lds + nw*E, and the ids and weights
     int* sp = lds + base;
     int* act = sp + N;
     int* na = act + E;
     int* scan = na + 1;
-    int* ids_l = scan + 4 * nw + 4;
-    // the ids are read twice (histogram, placement): one coalesced copy first,
-    // so neither pass waits on global loads step by step
-    for (int i0 = 0; i0 < N; i0 += 8 * blockDim.x) {    // 8 loads in flight per thread
+    int* ids_l = scan + 4 * nw + 4;                // N + 1 (a spare word)
+    float* w_l = reinterpret_cast<float*>(ids_l + N + 1);   // N + 1
+    // ids (read twice: histogram, placement) and weights: one coalesced copy
+    // first, 8 loads per thread in flight; loads at clamped indices and
+    // stores past the end to the spare word, so no load waits in a branch
+    for (int i0 = 0; i0 < N; i0 += 8 * blockDim.x) {
       int v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = ids[min(i0 + q * (int)blockDim.x + (int)threadIdx.x, N - 1)];
+      float wv[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const int i = i0 + q * blockDim.x + threadIdx.x;
-        if (i < N) ids_l[i] = v[q];
+        const int i = min(i0 + q * (int)blockDim.x + (int)threadIdx.x, N - 1);
+        v[q] = ids[i];
+        wv[q] = ro.topk_weights[i];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = min(i0 + q * (int)blockDim.x + (int)threadIdx.x, N);
+        ids_l[i] = v[q];
+        w_l[i] = wv[q];
       }
     }
     __syncthreads();
     block_sort_pairs(ids_l, N, E, ebits, lds, offsets, sorted_pairs, active, num_active, sp, act, na);
     __syncthreads();
-    block_write_slot_records(ro, E, max_slots(ro.M, ro.k, E), lds + (size_t)nw * E, sp, act, na, scan);
+    RecOut r = ro;
+    r.topk_weights = w_l;
+    block_write_slot_records(r, E, max_slots(ro.M, ro.k, E), lds + (size_t)nw * E, sp, act, na, scan, ids_l);
     return;
   }
   block_sort_pairs(ids, N, E, ebits, lds, offsets, sorted_pairs, active, num_active);
@@ -77,6 +90,11 @@ hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int
   const int nw = 8;
   const size_t shmem =
       sizeof(int) * (sort_lds_ints(nw, E) + (ro.rec && sort_keeps_lds(nw, N, E) ? sort_lds_extra(nw, N, E) : 4 * nw + 4));
+  if (shmem > 65536) {                             // more than the default dynamic LDS of a launch
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(sort_by_expert_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
   sort_by_expert_kernel<<<1, nw * kWave, shmem, s>>>(ids, N, E, expert_bits(E), offsets, sorted_pairs,
                                                      active, num_active, ro);
   return hipGetLastError();

@@ -171,18 +171,26 @@ __device__ __forceinline__ int expert_path(int n, int mt_min, int mt_max, int mf
 // experts at lists[nslots..), in slot order.  Then the path counters in the header and, with the MFMA path on,
 // its work items: (slot, 64-token tile) for every slot with at least
 // ro.mfma_min tokens, in slot order.  `lds` holds 4 * waves + 4 ints.
+// `ids` (optional): the pairs' expert ids, so the dropped pairs' -1 and the
+// others' positions go out in one pass with no ordering between them.
 __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nslots,
                                                 const int* __restrict__ offsets,
                                                 const int* __restrict__ sorted_pairs,
                                                 const int* __restrict__ active,
-                                                const int* __restrict__ num_active, int* lds) {
+                                                const int* __restrict__ num_active, int* lds,
+                                                const int* ids = nullptr) {
   const int D = *num_active;
   const int bd = blockDim.x, tid = threadIdx.x;
   if (ro.inv) {   // sorted position of every flattened pair (-1: dropped id)
     const int N = ro.M * ro.k, nvalid = offsets[E];
-    for (int i = tid; i < N; i += bd) ro.inv[i] = -1;
-    __threadfence_block();
-    __syncthreads();
+    if (ids) {
+      for (int i = tid; i < N; i += bd)
+        if ((unsigned)ids[i] >= (unsigned)E) ro.inv[i] = -1;
+    } else {
+      for (int i = tid; i < N; i += bd) ro.inv[i] = -1;
+      __threadfence_block();
+      __syncthreads();
+    }
     for (int i = tid; i < nvalid; i += bd) ro.inv[sorted_pairs[i]] = i;
   }
   const int per = (nslots + bd - 1) / bd;
