@@ -14,7 +14,7 @@ __host__ __device__ inline bool sort_keeps_lds(int nw, int N, int E) {
   return sizeof(int) * (sort_lds_ints(nw, E) + sort_lds_extra(nw, N, E)) <= kSortLdsBytes;
 }
 
-__global__ __launch_bounds__(512) void sort_by_expert_kernel(const int* __restrict__ ids, int N, int E,
+__global__ __launch_bounds__(1024) void sort_by_expert_kernel(const int* __restrict__ ids, int N, int E,
                                                              int ebits, int* __restrict__ offsets,
                                                              int* __restrict__ sorted_pairs,
                                                              int* __restrict__ active,
@@ -86,8 +86,9 @@ int expert_bits(int E) {
 
 hipError_t launch_sort_by_expert(const int* ids, int N, int E, int* offsets, int* sorted_pairs,
                                  int* active, int* num_active, hipStream_t s, RecOut ro) {
-  // 8 waves whatever N: the records epilogue has a slot per thread
-  const int nw = 8;
+  // 8 waves (the records epilogue has a slot per thread), 16 for long inputs
+  // (each wave places half as many pairs)
+  const int nw = N >= 1024 ? 16 : 8;
   const size_t shmem =
       sizeof(int) * (sort_lds_ints(nw, E) + (ro.rec && sort_keeps_lds(nw, N, E) ? sort_lds_extra(nw, N, E) : 4 * nw + 4));
   if (shmem > 65536) {                             // more than the default dynamic LDS of a launch
