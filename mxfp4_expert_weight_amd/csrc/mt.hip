@@ -23,8 +23,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int MT_KC = 256;                 // K per staged chunk (8 steps of 32)
 constexpr int MT_TOK = 16;                 // token columns of one tile
 constexpr int MT_PITCH = MT_KC * 2 + 16;   // LDS bytes per staged token row (+16 spreads banks)
-constexpr int MT_WAVES = 4;
-constexpr int MT_GU_J = 16 * MT_WAVES;     // intermediate indices per gate/up workgroup
+constexpr int MT_WAVES = 4;                // down workgroup
+constexpr int MT_GU_WAVES = 8;             // gate/up workgroup: the staged x rows serve 8 waves
+constexpr int MT_GU_J = 16 * MT_GU_WAVES;  // intermediate indices per gate/up workgroup
 constexpr int MT_DN_R = 32 * MT_WAVES;     // output rows per down workgroup
 
 struct MtStage {
@@ -131,6 +132,13 @@ __device__ __forceinline__ void mt_stage_load(uint4& u0, uint4& u1, const uint16
   u0 = p[0];
   u1 = p[1];
 }
+// The same with 32 parts of 16 bytes per row (eight-wave workgroups).
+__device__ __forceinline__ void mt_stage_load1(uint4& u, const uint16_t* src_row, int kc, int part) {
+  u = *reinterpret_cast<const uint4*>(src_row + kc * MT_KC + 8 * part);
+}
+__device__ __forceinline__ void mt_stage_store1(uint8_t* rows, int row, int part, uint4 u) {
+  *reinterpret_cast<uint4*>(rows + row * MT_PITCH + 16 * part) = u;
+}
 __device__ __forceinline__ void mt_stage_store(uint8_t* rows, int row, int part, uint4 u0, uint4 u1) {
   uint4* d = reinterpret_cast<uint4*>(rows + row * MT_PITCH + 32 * part);
   d[0] = u0;
@@ -193,7 +201,7 @@ __device__ __forceinline__ void mt_tile(int cols, int& slot, int& col) {
 // Workgroup (64 intermediate indices, slot): wave w takes indices
 // j0 + 16w .. + 15 as a gate tile and an up tile over the expert's tokens, so
 // h = SiLU(g) * u is formed in registers.
-__global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs a) {
+__global__ __launch_bounds__(MT_GU_WAVES * kWave) void gateup_mt_kernel(ForwardArgs a) {
   SlotRec rec;
   int slot, col;
   mt_tile(a.I / MT_GU_J, slot, col);
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
   const int sp = mt_scale_pitch(H);
   const uint8_t* gsl = mt_scale_lds + (16 * wave + j) * sp;
   const uint8_t* usl = gsl + MT_GU_J * sp;
-  const int srow = threadIdx.x >> 4, part = threadIdx.x & 15;
+  const int srow = threadIdx.x >> 5, part = threadIdx.x & 31;   // 16 rows x 32 parts of 16 bytes
   // prologue: the token lookup, the first chunk's weights and the scales
   // are all requested before any of them is waited for
   int stok;
@@ -220,11 +228,11 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
   MtRowChunk ga = mt_load_row(gq, 0, g), ua = mt_load_row(uq, 0, g), gb, ub;
   const uint16_t* xsrc = a.x + (int64_t)stok * H;
   const int nk = H / MT_KC;
-  uint4 x0, x1;
-  mt_stage_load(x0, x1, xsrc, 0, part);
+  uint4 x0;
+  mt_stage_load1(x0, xsrc, 0, part);
   mt_stage_scales(mt_scale_lds, a.w13_s + grow0 * (H / 32), a.w13_s + (grow0 + I) * (H / 32), MT_GU_J * sp / 16,
                   2 * MT_GU_J * sp / 16);
-  mt_stage_store(st.rows[0], srow, part, x0, x1);
+  mt_stage_store1(st.rows[0], srow, part, x0);
   v4f accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   // Chunks alternate between register sets (a, b) and LDS buffers (0, 1): the
@@ -235,27 +243,27 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void gateup_mt_kernel(ForwardArgs
   // the loop.
   int kc = 0;
   for (; kc + 2 < nk; kc += 2) {
-    mt_stage_load(x0, x1, xsrc, kc + 1, part);
+    mt_stage_load1(x0, xsrc, kc + 1, part);
     gb = mt_load_row(gq, kc + 1, g);
     ub = mt_load_row(uq, kc + 1, g);
     __builtin_amdgcn_sched_barrier(0);
     mt_gu_products(accg, accu, ga, ua, mt_scales(gsl, kc, g), mt_scales(usl, kc, g), st.rows[0], g, j);
-    mt_stage_store(st.rows[1], srow, part, x0, x1);
+    mt_stage_store1(st.rows[1], srow, part, x0);
     block_barrier_lds();
-    mt_stage_load(x0, x1, xsrc, kc + 2, part);
+    mt_stage_load1(x0, xsrc, kc + 2, part);
     ga = mt_load_row(gq, kc + 2, g);
     ua = mt_load_row(uq, kc + 2, g);
     __builtin_amdgcn_sched_barrier(0);
     mt_gu_products(accg, accu, gb, ub, mt_scales(gsl, kc + 1, g), mt_scales(usl, kc + 1, g), st.rows[1], g, j);
-    mt_stage_store(st.rows[0], srow, part, x0, x1);
+    mt_stage_store1(st.rows[0], srow, part, x0);
     block_barrier_lds();
   }
   if (kc + 1 < nk) {
-    mt_stage_load(x0, x1, xsrc, kc + 1, part);
+    mt_stage_load1(x0, xsrc, kc + 1, part);
     gb = mt_load_row(gq, kc + 1, g);
     ub = mt_load_row(uq, kc + 1, g);
     mt_gu_products(accg, accu, ga, ua, mt_scales(gsl, kc, g), mt_scales(usl, kc, g), st.rows[0], g, j);
-    mt_stage_store(st.rows[1], srow, part, x0, x1);
+    mt_stage_store1(st.rows[1], srow, part, x0);
     block_barrier_lds();
     mt_gu_products(accg, accu, gb, ub, mt_scales(gsl, kc + 1, g), mt_scales(usl, kc + 1, g), st.rows[1], g, j);
   } else {
@@ -389,7 +397,7 @@ static int mt_grid_slots(const ForwardArgs& a) {
 hipError_t launch_gateup_mt(const ForwardArgs& a, hipStream_t s) {
   const int slots8 = mt_grid_slots(a);
   const size_t shmem = (size_t)2 * MT_GU_J * (a.H / 32) + 16;   // gate and up rows' scales, a spare word
-  gateup_mt_kernel<<<dim3((a.I / MT_GU_J) * slots8), dim3(MT_WAVES * kWave), shmem, s>>>(a);
+  gateup_mt_kernel<<<dim3((a.I / MT_GU_J) * slots8), dim3(MT_GU_WAVES * kWave), shmem, s>>>(a);
   return hipGetLastError();
 }
 
