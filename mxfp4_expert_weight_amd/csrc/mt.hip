@@ -23,10 +23,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int MT_KC = 256;                 // K per staged chunk (8 steps of 32)
 constexpr int MT_TOK = 16;                 // token columns of one tile
 constexpr int MT_PITCH = MT_KC * 2 + 16;   // LDS bytes per staged token row (+16 spreads banks)
-constexpr int MT_WAVES = 4;                // down workgroup
 constexpr int MT_GU_WAVES = 8;             // gate/up workgroup: the staged x rows serve 8 waves
+constexpr int MT_DN_WAVES = 8;             // down workgroup: the staged h rows serve 8 waves
 constexpr int MT_GU_J = 16 * MT_GU_WAVES;  // intermediate indices per gate/up workgroup
-constexpr int MT_DN_R = 32 * MT_WAVES;     // output rows per down workgroup
+constexpr int MT_DN_R = 32 * MT_DN_WAVES;  // output rows per down workgroup
 
 struct MtStage {
   __align__(16) uint8_t rows[2][MT_TOK * MT_PITCH];
@@ -123,26 +123,15 @@ __device__ __forceinline__ v8bf mt_frag_b(const uint8_t* rows, int s, int g, int
   return __builtin_bit_cast(v8bf, u);
 }
 
-// Staging of token rows: thread (row tid/16, part tid%16) moves 16 bf16 of
-// its token's 256-element chunk.  Rows past the expert's tokens repeat a valid
-// row: token column j of a product only reaches output column j, and those
-// columns are never stored.
-__device__ __forceinline__ void mt_stage_load(uint4& u0, uint4& u1, const uint16_t* src_row, int kc, int part) {
-  const uint4* p = reinterpret_cast<const uint4*>(src_row + kc * MT_KC + 16 * part);
-  u0 = p[0];
-  u1 = p[1];
-}
-// The same with 32 parts of 16 bytes per row (eight-wave workgroups).
+// Staging of token rows: thread (row tid / 32, part tid % 32) moves 8 bf16
+// (16 bytes) of its token's 256-element chunk.  Rows past the expert's tokens
+// repeat a valid row: token column j of a product only reaches output column
+// j, and those columns are never stored.
 __device__ __forceinline__ void mt_stage_load1(uint4& u, const uint16_t* src_row, int kc, int part) {
   u = *reinterpret_cast<const uint4*>(src_row + kc * MT_KC + 8 * part);
 }
 __device__ __forceinline__ void mt_stage_store1(uint8_t* rows, int row, int part, uint4 u) {
   *reinterpret_cast<uint4*>(rows + row * MT_PITCH + 16 * part) = u;
-}
-__device__ __forceinline__ void mt_stage_store(uint8_t* rows, int row, int part, uint4 u0, uint4 u1) {
-  uint4* d = reinterpret_cast<uint4*>(rows + row * MT_PITCH + 32 * part);
-  d[0] = u0;
-  d[1] = u1;
 }
 
 // Products of one staged chunk with a wave's gate and up tiles (scale words
@@ -198,7 +187,7 @@ __device__ __forceinline__ void mt_tile(int cols, int& slot, int& col) {
 }
 
 // ------------------------------------------------------------- gate/up --
-// Workgroup (64 intermediate indices, slot): wave w takes indices
+// Workgroup (MT_GU_J = 128 intermediate indices, slot): wave w takes indices
 // j0 + 16w .. + 15 as a gate tile and an up tile over the expert's tokens, so
 // h = SiLU(g) * u is formed in registers.
 __global__ __launch_bounds__(MT_GU_WAVES * kWave) void gateup_mt_kernel(ForwardArgs a) {
@@ -207,7 +196,7 @@ __global__ __launch_bounds__(MT_GU_WAVES * kWave) void gateup_mt_kernel(ForwardA
   mt_tile(a.I / MT_GU_J, slot, col);
   if (slot >= mt_slots(a) || !mt_slot(a, slot, rec)) return;  // uniform over the workgroup
   __shared__ MtStage st;
-  extern __shared__ __align__(16) uint8_t mt_scale_lds[];     // 64 gate rows, then 64 up rows
+  extern __shared__ __align__(16) uint8_t mt_scale_lds[];     // the gate rows, then the up rows
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int g = lane >> 4, j = lane & 15;
   const int jw = col * MT_GU_J + 16 * wave;
@@ -285,17 +274,17 @@ __global__ __launch_bounds__(MT_GU_WAVES * kWave) void gateup_mt_kernel(ForwardA
 }
 
 // ---------------------------------------------------------------- down --
-// Workgroup (128 output rows, slot): wave w takes rows r0 + 32w .. + 31 as two
-// 16-row tiles over the expert's tokens; y[t][r] += w_t * (h_t . Wd[r]).
+// Workgroup (MT_DN_R = 256 output rows, slot): wave w takes rows r0 + 32w ..
+// + 31 as two 16-row tiles over the expert's tokens; y[t][r] += w_t * (h_t . Wd[r]).
 // h = hi + lo (two bf16 terms, each staged and multiplied); W4A8 layers carry
 // their MXFP8 h in hi alone.
-__global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a) {
+__global__ __launch_bounds__(MT_DN_WAVES * kWave) void down_mt_kernel(ForwardArgs a) {
   SlotRec rec;
   int slot, col;
   mt_tile(a.H / MT_DN_R, slot, col);
   if (slot >= mt_slots(a) || !mt_slot(a, slot, rec)) return;
   __shared__ MtStage st, stl;
-  extern __shared__ __align__(16) uint8_t mt_scale_lds[];     // the workgroup's 128 rows
+  extern __shared__ __align__(16) uint8_t mt_scale_lds[];     // the workgroup's rows
   const bool two = !a.act8;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int g = lane >> 4, j = lane & 15;
@@ -308,56 +297,56 @@ __global__ __launch_bounds__(MT_WAVES * kWave) void down_mt_kernel(ForwardArgs a
   const int sp = mt_scale_pitch(I);
   const uint8_t* s0l = mt_scale_lds + (32 * wave + j) * sp;
   const uint8_t* s1l = s0l + 16 * sp;
-  const int srow = threadIdx.x >> 4, part = threadIdx.x & 15;
+  const int srow = threadIdx.x >> 5, part = threadIdx.x & 31;   // 16 rows x 32 parts of 16 bytes
   const bool sv = srow < rec.n;
   const uint16_t* hsrc = a.h + ((int64_t)rec.hrow0 + (sv ? srow : 0)) * I;
   const uint16_t* lsrc = a.hlo + ((int64_t)rec.hrow0 + (sv ? srow : 0)) * I;
   const int nk = I / MT_KC;
   const uint4 z = make_uint4(0, 0, 0, 0);
   // prologue: the first chunk's weights and h rows, then the scales
-  uint4 x0, x1, l0 = z, l1 = z;
+  uint4 x0, l0 = z;
   MtRowChunk a0 = mt_load_row(q0, 0, g), a1 = mt_load_row(q1, 0, g), b0, b1;
-  mt_stage_load(x0, x1, hsrc, 0, part);
-  if (two) mt_stage_load(l0, l1, lsrc, 0, part);
+  mt_stage_load1(x0, hsrc, 0, part);
+  if (two) mt_stage_load1(l0, lsrc, 0, part);
   const uint8_t* ssrc = a.w2_s + wrow0 * (I / 32);
   mt_stage_scales(mt_scale_lds, ssrc, ssrc, MT_DN_R * sp / 16, MT_DN_R * sp / 16);
-  mt_stage_store(st.rows[0], srow, part, x0, x1);
-  if (two) mt_stage_store(stl.rows[0], srow, part, l0, l1);
+  mt_stage_store1(st.rows[0], srow, part, x0);
+  if (two) mt_stage_store1(stl.rows[0], srow, part, l0);
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   // the same alternation as gate/up
   int kc = 0;
   for (; kc + 2 < nk; kc += 2) {
-    mt_stage_load(x0, x1, hsrc, kc + 1, part);
-    if (two) mt_stage_load(l0, l1, lsrc, kc + 1, part);
+    mt_stage_load1(x0, hsrc, kc + 1, part);
+    if (two) mt_stage_load1(l0, lsrc, kc + 1, part);
     b0 = mt_load_row(q0, kc + 1, g);
     b1 = mt_load_row(q1, kc + 1, g);
     __builtin_amdgcn_sched_barrier(0);
     mt_down_products(acc0, acc1, a0, a1, mt_scales(s0l, kc, g), mt_scales(s1l, kc, g), st.rows[0], stl.rows[0], two,
                      g, j);
-    mt_stage_store(st.rows[1], srow, part, x0, x1);
-    if (two) mt_stage_store(stl.rows[1], srow, part, l0, l1);
+    mt_stage_store1(st.rows[1], srow, part, x0);
+    if (two) mt_stage_store1(stl.rows[1], srow, part, l0);
     block_barrier_lds();
-    mt_stage_load(x0, x1, hsrc, kc + 2, part);
-    if (two) mt_stage_load(l0, l1, lsrc, kc + 2, part);
+    mt_stage_load1(x0, hsrc, kc + 2, part);
+    if (two) mt_stage_load1(l0, lsrc, kc + 2, part);
     a0 = mt_load_row(q0, kc + 2, g);
     a1 = mt_load_row(q1, kc + 2, g);
     __builtin_amdgcn_sched_barrier(0);
     mt_down_products(acc0, acc1, b0, b1, mt_scales(s0l, kc + 1, g), mt_scales(s1l, kc + 1, g), st.rows[1],
                      stl.rows[1], two, g, j);
-    mt_stage_store(st.rows[0], srow, part, x0, x1);
-    if (two) mt_stage_store(stl.rows[0], srow, part, l0, l1);
+    mt_stage_store1(st.rows[0], srow, part, x0);
+    if (two) mt_stage_store1(stl.rows[0], srow, part, l0);
     block_barrier_lds();
   }
   if (kc + 1 < nk) {
-    mt_stage_load(x0, x1, hsrc, kc + 1, part);
-    if (two) mt_stage_load(l0, l1, lsrc, kc + 1, part);
+    mt_stage_load1(x0, hsrc, kc + 1, part);
+    if (two) mt_stage_load1(l0, lsrc, kc + 1, part);
     b0 = mt_load_row(q0, kc + 1, g);
     b1 = mt_load_row(q1, kc + 1, g);
     mt_down_products(acc0, acc1, a0, a1, mt_scales(s0l, kc, g), mt_scales(s1l, kc, g), st.rows[0], stl.rows[0], two,
                      g, j);
-    mt_stage_store(st.rows[1], srow, part, x0, x1);
-    if (two) mt_stage_store(stl.rows[1], srow, part, l0, l1);
+    mt_stage_store1(st.rows[1], srow, part, x0);
+    if (two) mt_stage_store1(stl.rows[1], srow, part, l0);
     block_barrier_lds();
     mt_down_products(acc0, acc1, b0, b1, mt_scales(s0l, kc + 1, g), mt_scales(s1l, kc + 1, g), st.rows[1],
                      stl.rows[1], two, g, j);
@@ -404,7 +393,7 @@ hipError_t launch_gateup_mt(const ForwardArgs& a, hipStream_t s) {
 hipError_t launch_down_mt(const ForwardArgs& a, hipStream_t s) {
   const int slots8 = mt_grid_slots(a);
   const size_t shmem = (size_t)MT_DN_R * (a.I / 32) + 16;
-  down_mt_kernel<<<dim3((a.H / MT_DN_R) * slots8), dim3(MT_WAVES * kWave), shmem, s>>>(a);
+  down_mt_kernel<<<dim3((a.H / MT_DN_R) * slots8), dim3(MT_DN_WAVES * kWave), shmem, s>>>(a);
   return hipGetLastError();
 }
 
