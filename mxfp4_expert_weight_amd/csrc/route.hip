@@ -279,6 +279,155 @@ __global__ __launch_bounds__(RM_THREADS) void router_mfma_kernel(const uint16_t*
   }
 }
 
+// Batches with rows a multiple of 128 on the bf16 matrix cores, without LDS
+// staging: workgroup = 32 tokens x 32 experts, and its four waves take the
+// four quarters of K (whole 128-element blocks), so there are four times as
+// many waves as output tiles of this size and each wave holds a 32 x 32 tile
+// (2 x 2 fragments) whose operands come straight from global memory.  In
+// step j of a block, lane (r, g) of a 16-row fragment holds K elements
+// 32 j + 8 g .. + 7 of its row, the same for x and the weights, so every
+// pairing of the matrix product is the one of the definition; the four lanes
+// of a row read one contiguous run (64 bytes of x, 128 of the weights), so a
+// load instruction touches 16 rows' lines, not 64 scattered pieces.  The
+// weights are split exactly into three bf16 parts as in router_mfma_kernel.
+// A step's leaf is three chained matrix-core dots, smallest part first from
+// zero: the accumulator carried into the next dot is at most 2^-7 of the
+// products it meets (|w2| < 2^-7 |w|, |w3| < 2^-14 |w|), so the leaf's error
+// is within 33 u of the sum of |x w| over its 32 elements (32 roundings for
+// the last dot's own sum, whatever its order).  Leaves add into the wave's
+// sum in K order, then the four waves' sums in K order through LDS, then the
+// bias: a logit's longest rounding chain is 33 + 4 ceil(H / 512) + 3 + 1.
+// QB > 0: every wave has exactly QB blocks (H = 512 QB) and the block loop is
+// unrolled; QB = 0: any multiple of 128.
+constexpr int RS_T = 32, RS_E = 32, RS_KB = 128, RS_WAVES = 4, RS_PITCH = RS_E + 4;
+__device__ __forceinline__ void router_split3(const float4& lo, const float4& hi, uint4& p1, uint4& p2, uint4& p3) {
+  const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t q1[4], q2[4], q3[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t u[3][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const float w = f[2 * i + r];
+      const float r1 = w - __uint_as_float(__float_as_uint(w) & 0xFFFF0000u);       // exact
+      const float r2 = r1 - __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);     // exact, <= 8 bits
+      u[0][r] = __float_as_uint(w);
+      u[1][r] = __float_as_uint(r1);
+      u[2][r] = __float_as_uint(r2);
+    }
+    // the high halves of a pair (bytes 2, 3 of each word): element 2i low, 2i + 1 high
+    q1[i] = __builtin_amdgcn_perm(u[0][1], u[0][0], 0x07060302u);
+    q2[i] = __builtin_amdgcn_perm(u[1][1], u[1][0], 0x07060302u);
+    q3[i] = __builtin_amdgcn_perm(u[2][1], u[2][0], 0x07060302u);
+  }
+  p1 = make_uint4(q1[0], q1[1], q1[2], q1[3]);
+  p2 = make_uint4(q2[0], q2[1], q2[2], q2[3]);
+  p3 = make_uint4(q3[0], q3[1], q3[2], q3[3]);
+}
+
+struct RouterBlock {
+  uint4 x[2][4];      // two token rows: 8 bf16 per step
+  float4 w[2][8];     // two expert rows: 8 fp32 per step
+};
+
+template <int QB>
+__global__ __launch_bounds__(RS_WAVES * kWave) void router_split_kernel(const uint16_t* __restrict__ x,
+                                                                       const float* __restrict__ w_router,
+                                                                       const float* __restrict__ bias,
+                                                                       int64_t bias_stride, int M, int H, int E,
+                                                                       float* __restrict__ logits) {
+  __shared__ float red[RS_WAVES][RS_T][RS_PITCH];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int t0 = blockIdx.y * RS_T, e0 = blockIdx.x * RS_E;
+  const int fr = lane & 15, g = lane >> 4;
+  const int nb = H / RS_KB, qb = QB > 0 ? QB : (nb + RS_WAVES - 1) / RS_WAVES;
+  const int b0 = min(wave * qb, nb), nbw = min(b0 + qb, nb) - b0;   // this wave's blocks (may be none)
+  const int ba0 = min(b0, nb - 1);                                    // addressed block: inside the row
+  const uint16_t* xr[2];
+  const float* wr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    xr[i] = x + (size_t)min(t0 + 16 * i + fr, M - 1) * H + (size_t)ba0 * RS_KB + 8 * g;
+    wr[i] = w_router + (size_t)min(e0 + 16 * i + fr, E - 1) * H + (size_t)ba0 * RS_KB + 8 * g;
+  }
+  auto load = [&](RouterBlock& B, int b) {     // block b of this wave (clamped: always in the row)
+    const int o = min(b, max(nbw - 1, 0)) * RS_KB;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) B.x[i][j] = *reinterpret_cast<const uint4*>(xr[i] + o + 32 * j);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) B.w[i][j] = *reinterpret_cast<const float4*>(wr[i] + o + 32 * (j >> 1) + 4 * (j & 1));
+    }
+  };
+  const rv4f zero = {0.f, 0.f, 0.f, 0.f};
+  rv4f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) acc[i][k] = zero;
+  auto compute = [&](const RouterBlock& B) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 bw[2][3];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) router_split3(B.w[k][2 * j], B.w[k][2 * j + 1], bw[k][0], bw[k][1], bw[k][2]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const rv8bf a = __builtin_bit_cast(rv8bf, B.x[i][j]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          rv4f t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(rv8bf, bw[k][2]), zero, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(rv8bf, bw[k][1]), t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(rv8bf, bw[k][0]), t, 0, 0, 0);
+          acc[i][k] += t;
+        }
+      }
+    }
+  };
+  // two register sets alternate: block b + 1 is in flight while block b is multiplied
+  RouterBlock ba, bb;
+  if constexpr (QB > 0) {
+    load(ba, 0);
+#pragma unroll
+    for (int b = 0; b < QB; b += 2) {
+      if (b + 1 < QB) load(bb, b + 1);
+      compute(ba);
+      if (b + 1 < QB) {
+        if (b + 2 < QB) load(ba, b + 2);
+        compute(bb);
+      }
+    }
+  } else {
+    load(ba, 0);
+    for (int b = 0; b < nbw; b += 2) {
+      load(bb, b + 1);
+      compute(ba);
+      if (b + 1 >= nbw) break;
+      load(ba, b + 2);
+      compute(bb);
+    }
+  }
+  // lane (r, g) holds D[4 g + q][r] of fragment (i, k): token 16 i + 4 g + q, expert 16 k + r
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[wave][16 * i + 4 * g + q][16 * k + fr] = acc[i][k][q];
+  __syncthreads();
+  for (int o = threadIdx.x; o < RS_T * RS_E; o += RS_WAVES * kWave) {
+    const int tt = o / RS_E, ee = o % RS_E, t = t0 + tt, e = e0 + ee;
+    float v = red[0][tt][ee];
+#pragma unroll
+    for (int w = 1; w < RS_WAVES; ++w) v += red[w][tt][ee];
+    if (t < M && e < E) {
+      if (bias) v += bias[(size_t)t * bias_stride + e];
+      logits[(size_t)t * E + e] = v;
+    }
+  }
+}
+
 // One wave per token.
 template <int C>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int M, int E,
@@ -339,6 +488,12 @@ __global__ __launch_bounds__(64 * kTopkSortMaxTokens) void topk_sort_small_kerne
 hipError_t launch_router_logits(const uint16_t* x, const float* w_router, const float* bias,
                                 int64_t bias_stride, int M, int H, int E, float* logits,
                                 hipStream_t s) {
+  if (M >= kRouterGemmMinTokens && H % RS_KB == 0) {
+    auto kern = (H == 5 * RS_WAVES * RS_KB) ? router_split_kernel<5> : router_split_kernel<0>;
+    kern<<<dim3((E + RS_E - 1) / RS_E, (M + RS_T - 1) / RS_T), dim3(RS_WAVES * kWave), 0, s>>>(
+        x, w_router, bias, bias_stride, M, H, E, logits);
+    return hipGetLastError();
+  }
   if (M >= kRouterGemmMinTokens) {
     auto kern = (H == 10 * RM_KC) ? router_mfma_kernel<10> : router_mfma_kernel<0>;
     kern<<<dim3((E + RM_E - 1) / RM_E, (M + RM_T - 1) / RM_T), dim3(RM_THREADS), 0, s>>>(

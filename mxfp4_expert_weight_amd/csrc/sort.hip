@@ -9,7 +9,7 @@ namespace moe {
 // records epilogue: then the epilogue reads nothing from global memory.  The
 // budget is the 160 KiB a CDNA4 workgroup can hold.
 constexpr size_t kSortLdsBytes = 160 * 1024;
-__host__ __device__ inline size_t sort_lds_extra(int nw, int N, int E) { return 3 * (size_t)N + E + 4 * nw + 7; }
+__host__ __device__ inline size_t sort_lds_extra(int nw, int N, int E) { return 4 * (size_t)N + E + 4 * nw + 8; }
 __host__ __device__ inline bool sort_keeps_lds(int nw, int N, int E) {
   return sizeof(int) * (sort_lds_ints(nw, E) + sort_lds_extra(nw, N, E)) <= kSortLdsBytes;
 }
@@ -25,13 +25,15 @@ __global__ __launch_bounds__(1024) void sort_by_expert_kernel(const int* __restr
   const size_t base = sort_lds_ints(nw, E);
   if (ro.rec && sort_keeps_lds(nw, N, E)) {
     // the records epilogue reads the sort from LDS: sorted pairs, active list,
-    // D and the offsets left at lds + nw*E, and the ids and weights
+    // D and the offsets left at lds + nw*E, the ids, weights and each pair's
+    // sorted position
     int* sp = lds + base;
     int* act = sp + N;
     int* na = act + E;
     int* scan = na + 1;
     int* ids_l = scan + 4 * nw + 4;                // N + 1 (a spare word)
     float* w_l = reinterpret_cast<float*>(ids_l + N + 1);   // N + 1
+    int* inv_l = ids_l + 2 * (N + 1);                        // N
     // ids (read twice: histogram, placement) and weights: one coalesced copy
     // first, 8 loads per thread in flight; loads at clamped indices and
     // stores past the end to the spare word, so no load waits in a branch
@@ -52,11 +54,11 @@ __global__ __launch_bounds__(1024) void sort_by_expert_kernel(const int* __restr
       }
     }
     __syncthreads();
-    block_sort_pairs(ids_l, N, E, ebits, lds, offsets, sorted_pairs, active, num_active, sp, act, na);
+    block_sort_pairs(ids_l, N, E, ebits, lds, offsets, sorted_pairs, active, num_active, sp, act, na, inv_l);
     __syncthreads();
     RecOut r = ro;
     r.topk_weights = w_l;
-    block_write_slot_records(r, E, max_slots(ro.M, ro.k, E), lds + (size_t)nw * E, sp, act, na, scan, ids_l);
+    block_write_slot_records(r, E, max_slots(ro.M, ro.k, E), lds + (size_t)nw * E, sp, act, na, scan, inv_l);
     return;
   }
   block_sort_pairs(ids, N, E, ebits, lds, offsets, sorted_pairs, active, num_active);

@@ -36,12 +36,17 @@ __host__ __device__ inline size_t sort_lds_ints(int nw, int E) { return (size_t)
 // Sort `N` pairs whose expert ids are ids[0..N) (global or LDS).  Uses
 // sort_lds_ints(nw, E) ints of LDS at `lds`; every thread of the block calls it.
 // With sp_lds / act_lds / na_lds non-null it also keeps sorted_pairs, the
-// active list and D in LDS (for an epilogue in the same block); the exclusive
-// offsets (E + 1 of them) stay at lds + nw*E after the call.
+// active list and D in LDS (for an epilogue in the same block); the pairs are
+// then placed in LDS and sorted_pairs goes out in one coalesced copy (one
+// workgroup's scattered 4-byte stores would queue behind each other in its
+// CU's memory pipeline).  With inv_lds non-null, inv_lds[p] receives the
+// sorted position of pair p (-1 for a dropped id).  The exclusive offsets
+// (E + 1 of them) stay at lds + nw*E after the call.
 __device__ inline void block_sort_pairs(const int* ids, int N, int E, int ebits, int* lds,
                                  int* __restrict__ offsets, int* __restrict__ sorted_pairs,
                                  int* __restrict__ active, int* __restrict__ num_active,
-                                 int* sp_lds = nullptr, int* act_lds = nullptr, int* na_lds = nullptr) {
+                                 int* sp_lds = nullptr, int* act_lds = nullptr, int* na_lds = nullptr,
+                                 int* inv_lds = nullptr) {
   const int nw = blockDim.x / kWave;
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -118,12 +123,22 @@ __device__ inline void block_sort_pairs(const int* ids, int N, int E, int ebits,
     if (valid) {
       const int rank = __popcll(match & lt_mask);
       const int pos = off[e] + cnt[w * E + e] + rank;
-      sorted_pairs[pos] = p;
-      if (sp_lds) sp_lds[pos] = p;
+      if (sp_lds)
+        sp_lds[pos] = p;
+      else
+        sorted_pairs[pos] = p;
+      if (inv_lds) inv_lds[p] = pos;
       __builtin_amdgcn_wave_barrier();
       if (rank == 0) cnt[w * E + e] += __popcll(match);
+    } else if (inv_lds && p < end) {
+      inv_lds[p] = -1;
     }
     __builtin_amdgcn_wave_barrier();
+  }
+  if (sp_lds) {
+    block_barrier_lds();
+    const int nvalid = off[E];
+    for (int i = threadIdx.x; i < nvalid; i += bd) sorted_pairs[i] = sp_lds[i];
   }
 }
 
@@ -159,6 +174,22 @@ __device__ __forceinline__ SlotRec make_slot_record(int slot, int D, const int* 
   return r;
 }
 
+// Expert and token count of `slot` (the first fields of its record), without
+// the per-token fields.
+__device__ __forceinline__ void slot_expert_tokens(int slot, int D, const int* off, const int* act, int M, int E,
+                                                   int has_shared, int& e, int& n) {
+  if (slot < D) {
+    e = act[slot];
+    n = off[e + 1] - off[e];
+  } else if (slot == D && has_shared) {
+    e = E;
+    n = M;
+  } else {
+    e = -1;
+    n = 0;
+  }
+}
+
 // Path of an expert with n tokens: 0 GEMV, 1 few-token matrix cores, 2 MFMA.
 __device__ __forceinline__ int expert_path(int n, int mt_min, int mt_max, int mfma_min) {
   return n >= mfma_min ? 2 : (n >= mt_min && n <= mt_max) ? 1 : 0;
@@ -171,27 +202,27 @@ __device__ __forceinline__ int expert_path(int n, int mt_min, int mt_max, int mf
 // experts at lists[nslots..), in slot order.  Then the path counters in the header and, with the MFMA path on,
 // its work items: (slot, 64-token tile) for every slot with at least
 // ro.mfma_min tokens, in slot order.  `lds` holds 4 * waves + 4 ints.
-// `ids` (optional): the pairs' expert ids, so the dropped pairs' -1 and the
-// others' positions go out in one pass with no ordering between them.
+// `inv_src` (optional): the sorted position of every pair (-1: dropped), as
+// block_sort_pairs leaves it in LDS; ro.inv is then a coalesced copy of it.
 __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nslots,
                                                 const int* __restrict__ offsets,
                                                 const int* __restrict__ sorted_pairs,
                                                 const int* __restrict__ active,
                                                 const int* __restrict__ num_active, int* lds,
-                                                const int* ids = nullptr) {
+                                                const int* inv_src = nullptr) {
   const int D = *num_active;
   const int bd = blockDim.x, tid = threadIdx.x;
   if (ro.inv) {   // sorted position of every flattened pair (-1: dropped id)
-    const int N = ro.M * ro.k, nvalid = offsets[E];
-    if (ids) {
-      for (int i = tid; i < N; i += bd)
-        if ((unsigned)ids[i] >= (unsigned)E) ro.inv[i] = -1;
+    const int N = ro.M * ro.k;
+    if (inv_src) {
+      for (int i = tid; i < N; i += bd) ro.inv[i] = inv_src[i];
     } else {
+      const int nvalid = offsets[E];
       for (int i = tid; i < N; i += bd) ro.inv[i] = -1;
       __threadfence_block();
       __syncthreads();
+      for (int i = tid; i < nvalid; i += bd) ro.inv[sorted_pairs[i]] = i;
     }
-    for (int i = tid; i < nvalid; i += bd) ro.inv[sorted_pairs[i]] = i;
   }
   const int per = (nslots + bd - 1) / bd;
   const int s0 = min(nslots, tid * per), s1 = min(nslots, s0 + per);
@@ -232,20 +263,20 @@ __device__ inline void block_write_slot_records(const RecOut& ro, int E, int nsl
   }
   if (ro.lists) {   // the GEMV and few-token experts' slots, each list in slot order
     for (int slot = s0; slot < s1; ++slot) {
-      const SlotRec r = make_slot_record(slot, D, offsets, sorted_pairs, active, ro.topk_weights, ro.M, ro.k,
-                                         E, ro.has_shared);
-      if (r.e < 0) continue;
-      const int path = expert_path(r.n, ro.mt_min, ro.mt_max, ro.mfma_min);
+      int e, n;
+      slot_expert_tokens(slot, D, offsets, active, ro.M, E, ro.has_shared, e, n);
+      if (e < 0) continue;
+      const int path = expert_path(n, ro.mt_min, ro.mt_max, ro.mfma_min);
       if (path == 0) ro.lists[pbase[0]++] = slot;
       if (path == 1) ro.lists[nslots + pbase[1]++] = slot;
     }
   }
   if (ro.items) {
     for (int slot = s0; slot < s1; ++slot) {
-      const SlotRec r = make_slot_record(slot, D, offsets, sorted_pairs, active, ro.topk_weights, ro.M, ro.k,
-                                         E, ro.has_shared);
-      if (r.e < 0 || r.n < ro.mfma_min) continue;
-      for (int t = 0; t * kMfmaTileTokens < r.n; ++t) ro.items[base++] = make_int2(slot, t);
+      int e, n;
+      slot_expert_tokens(slot, D, offsets, active, ro.M, E, ro.has_shared, e, n);
+      if (e < 0 || n < ro.mfma_min) continue;
+      for (int t = 0; t * kMfmaTileTokens < n; ++t) ro.items[base++] = make_int2(slot, t);
     }
   }
   if (tid == bd - 1) {

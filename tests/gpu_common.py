@@ -41,14 +41,20 @@ def router_rounding_chain(H, M):
     """Longest chain of fp32 roundings in a router logit.  Batches below 64
     tokens: each lane sums ceil(H/256) float4s (4 fmas each) in order, a
     6-level wave tree follows, then the bias; one more for slack:
-    4 ceil(H/256) + 8.  Larger batches (the
-    matrix cores, weights split exactly into three bf16 parts, so 3H exact
-    products): a 32-product dot per leaf (counted as 32 roundings, the most
-    any summation order of it can take), 16 leaves per group and weight part,
-    the groups into the total in order, the three last partial groups, then the
-    bias: 32 + 16 + 3 ceil(H/512) + 3 + 1."""
+    4 ceil(H/256) + 8.  Larger batches run on the matrix cores with the
+    weights split exactly into three bf16 parts, so 3H exact products, and a
+    32-product dot per leaf (counted as 32 roundings, the most any summation
+    order of it can take).  Rows a multiple of 128: a leaf chains the three
+    parts' dots smallest first, which keeps its error within 33 u of its sum
+    of |x w|; each of four waves adds its 4 ceil(H/512) leaves in order, then
+    the four waves' sums, then the bias: 33 + 4 ceil(H/512) + 3 + 1.
+    Other rows: 16 leaves per group and weight part, the groups into the
+    total in order, the three last partial groups, then the bias:
+    32 + 16 + 3 ceil(H/512) + 3 + 1."""
     if M < 64:
         return 4 * -(-H // 256) + 8
+    if H % 128 == 0:
+        return 33 + 4 * -(-H // 512) + 3 + 1
     return 32 + 16 + 3 * -(-H // 512) + 3 + 1
 
 

@@ -135,9 +135,11 @@ def test_sort_by_expert_exact(M, k, E, dist):
     (2, 32, 1, 1, None),            # one expert, one vector per row
     (15, 224, 77, 3, None),         # ragged E
     (63, 2560, 512, 8, "experts"),  # largest batch of the wave kernel
-    (64, 2560, 512, 8, "experts"),  # smallest batch of the tiled GEMM, 16-expert tiles
-    (65, 96, 40, 5, None),          # ragged token tile (65 = 2*32 + 1), one partial K chunk
+    (64, 2560, 512, 8, "experts"),  # smallest batch of the matrix-core router
+    (65, 96, 40, 5, None),          # rows not a multiple of 128 (LDS-staged kernel), ragged token tile, one partial K chunk
     (300, 8192, 1000, 8, None),     # 32-expert tiles, ragged E, longest H
+    (96, 384, 77, 4, "rows"),       # rows of three 128-blocks: the fourth wave of each tile has none
+    (128, 640, 64, 8, None),        # five blocks over four waves (2, 2, 1, 0)
     (512, 2560, 512, 8, None),      # the chunked-prefill router
 ])
 def test_router_logits_and_routing(M, H, E, k, bias):
