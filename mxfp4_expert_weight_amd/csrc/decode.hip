@@ -600,7 +600,6 @@ __device__ __forceinline__ void gateup_slot(const ForwardArgs& a, GateupLds<NB, 
 template <int C, int NB, int Q, bool A8, bool PROBE, bool MF>
 __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(Q >= 2 ? 3 : 4, Q >= 2 ? 3 : 4)))
 void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
-  constexpr int KB = NB * 16;                      // 32-element blocks per row
   static_assert(Q >= 1 && Q <= 4, "quads");
   static_assert(!MF || Q == 2, "a matrix-core wave covers 8 row pairs");
   using Lds = GateupLds<NB, Q>;
@@ -608,7 +607,7 @@ void decode_gateup_kernel(ForwardArgs a, RouteOut ro) {
   __shared__ __align__(16) Lds L;
   stamp<PROBE>(a.probe, kGuEntry);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int M = a.M, k = a.k, E = a.E, H = a.H, I = a.I;
+  const int M = a.M, k = a.k, E = a.E, H = a.H;
   const int srow = a.has_shared ? 1 : 0;
   const bool writer = blockIdx.y == srow;
   const bool shared_row = a.has_shared && blockIdx.y == 0;
@@ -875,13 +874,11 @@ __device__ __forceinline__ void down_slot(const ForwardArgs& a, DownLds<NBD>& L,
 template <int NBD, bool PROBE, bool MF>
 __global__ __launch_bounds__(DC_THREADS) __attribute__((amdgpu_waves_per_eu(6, 6)))
 void decode_down_kernel(ForwardArgs a) {
-  constexpr int KB = NBD * 8;                      // blocks per row (I / 32)
   __shared__ __align__(16) DownLds<NBD> L;
   stamp<PROBE>(a.probe, kDnEntry);
   PRec rec;
   prec_load(reinterpret_cast<const DecRec*>(a.rec) + blockIdx.y, rec);
-  const int rec_e = prec_e(rec), rec_n = prec_n(rec);
-  if (rec_e < 0) return;
+  if (prec_e(rec) < 0) return;
   stamp<PROBE>(a.probe, kDnRecord);
   down_slot<NBD, PROBE, MF, false>(a, L, rec);
 }
