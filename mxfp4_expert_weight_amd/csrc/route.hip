@@ -280,10 +280,11 @@ __global__ __launch_bounds__(RM_THREADS) void router_mfma_kernel(const uint16_t*
 }
 
 // Batches with rows a multiple of 128 on the bf16 matrix cores, without LDS
-// staging: workgroup = 32 tokens x 32 experts, and its four waves take the
+// staging: workgroup = 64 tokens x 16 experts, and its four waves take the
 // four quarters of K (whole 128-element blocks), so there are four times as
-// many waves as output tiles of this size and each wave holds a 32 x 32 tile
-// (2 x 2 fragments) whose operands come straight from global memory.  In
+// many waves as output tiles of this size and each wave holds a 64 x 16 tile
+// (4 token fragments on one expert fragment, so each weight is split once for
+// 64 tokens) whose operands come straight from global memory.  In
 // step j of a block, lane (r, g) of a 16-row fragment holds K elements
 // 32 j + 8 g .. + 7 of its row, the same for x and the weights, so every
 // pairing of the matrix product is the one of the definition; the four lanes
@@ -299,7 +300,8 @@ __global__ __launch_bounds__(RM_THREADS) void router_mfma_kernel(const uint16_t*
 // bias: a logit's longest rounding chain is 33 + 4 ceil(H / 512) + 3 + 1.
 // QB > 0: every wave has exactly QB blocks (H = 512 QB) and the block loop is
 // unrolled; QB = 0: any multiple of 128.
-constexpr int RS_T = 32, RS_E = 32, RS_KB = 128, RS_WAVES = 4, RS_PITCH = RS_E + 4;
+constexpr int RS_TT = 4, RS_ET = 1;                              // 16-row fragments per wave: tokens, experts
+constexpr int RS_T = 16 * RS_TT, RS_E = 16 * RS_ET, RS_KB = 128, RS_WAVES = 4, RS_PITCH = RS_E + 4;
 __device__ __forceinline__ void router_split3(const float4& lo, const float4& hi, uint4& p1, uint4& p2, uint4& p3) {
   const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   uint32_t q1[4], q2[4], q3[4];
@@ -326,8 +328,8 @@ __device__ __forceinline__ void router_split3(const float4& lo, const float4& hi
 }
 
 struct RouterBlock {
-  uint4 x[2][4];      // two token rows: 8 bf16 per step
-  float4 w[2][8];     // two expert rows: 8 fp32 per step
+  uint4 x[RS_TT][4];      // the token rows: 8 bf16 per step
+  float4 w[RS_ET][8];     // the expert rows: 8 fp32 per step
 };
 
 template <int QB>
@@ -343,40 +345,41 @@ __global__ __launch_bounds__(RS_WAVES * kWave) void router_split_kernel(const ui
   const int nb = H / RS_KB, qb = QB > 0 ? QB : (nb + RS_WAVES - 1) / RS_WAVES;
   const int b0 = min(wave * qb, nb), nbw = min(b0 + qb, nb) - b0;   // this wave's blocks (may be none)
   const int ba0 = min(b0, nb - 1);                                    // addressed block: inside the row
-  const uint16_t* xr[2];
-  const float* wr[2];
+  const uint16_t* xr[RS_TT];
+  const float* wr[RS_ET];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    xr[i] = x + (size_t)min(t0 + 16 * i + fr, M - 1) * H + (size_t)ba0 * RS_KB + 8 * g;
+  for (int i = 0; i < RS_TT; ++i) xr[i] = x + (size_t)min(t0 + 16 * i + fr, M - 1) * H + (size_t)ba0 * RS_KB + 8 * g;
+#pragma unroll
+  for (int i = 0; i < RS_ET; ++i)
     wr[i] = w_router + (size_t)min(e0 + 16 * i + fr, E - 1) * H + (size_t)ba0 * RS_KB + 8 * g;
-  }
   auto load = [&](RouterBlock& B, int b) {     // block b of this wave (clamped: always in the row)
     const int o = min(b, max(nbw - 1, 0)) * RS_KB;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < RS_TT; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) B.x[i][j] = *reinterpret_cast<const uint4*>(xr[i] + o + 32 * j);
 #pragma unroll
+    for (int i = 0; i < RS_ET; ++i)
+#pragma unroll
       for (int j = 0; j < 8; ++j) B.w[i][j] = *reinterpret_cast<const float4*>(wr[i] + o + 32 * (j >> 1) + 4 * (j & 1));
-    }
   };
   const rv4f zero = {0.f, 0.f, 0.f, 0.f};
-  rv4f acc[2][2];
+  rv4f acc[RS_TT][RS_ET];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RS_TT; ++i)
 #pragma unroll
-    for (int k = 0; k < 2; ++k) acc[i][k] = zero;
+    for (int k = 0; k < RS_ET; ++k) acc[i][k] = zero;
   auto compute = [&](const RouterBlock& B) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint4 bw[2][3];
+      uint4 bw[RS_ET][3];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) router_split3(B.w[k][2 * j], B.w[k][2 * j + 1], bw[k][0], bw[k][1], bw[k][2]);
+      for (int k = 0; k < RS_ET; ++k) router_split3(B.w[k][2 * j], B.w[k][2 * j + 1], bw[k][0], bw[k][1], bw[k][2]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < RS_TT; ++i) {
         const rv8bf a = __builtin_bit_cast(rv8bf, B.x[i][j]);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < RS_ET; ++k) {
           rv4f t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(rv8bf, bw[k][2]), zero, 0, 0, 0);
           t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(rv8bf, bw[k][1]), t, 0, 0, 0);
           t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(rv8bf, bw[k][0]), t, 0, 0, 0);
@@ -410,9 +413,9 @@ __global__ __launch_bounds__(RS_WAVES * kWave) void router_split_kernel(const ui
   }
   // lane (r, g) holds D[4 g + q][r] of fragment (i, k): token 16 i + 4 g + q, expert 16 k + r
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RS_TT; ++i)
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < RS_ET; ++k)
 #pragma unroll
       for (int q = 0; q < 4; ++q) red[wave][16 * i + 4 * g + q][16 * k + fr] = acc[i][k][q];
   __syncthreads();
