@@ -140,6 +140,7 @@ def test_sort_by_expert_exact(M, k, E, dist):
     (300, 8192, 1000, 8, None),     # 32-expert tiles, ragged E, longest H
     (96, 384, 77, 4, "rows"),       # rows of three 128-blocks: the fourth wave of each tile has none
     (128, 640, 64, 8, None),        # five blocks over four waves (2, 2, 1, 0)
+    (70, 256, 5, 2, "experts"),     # fewer experts than one 16-expert tile, a ragged 64-token tile
     (512, 2560, 512, 8, None),      # the chunked-prefill router
 ])
 def test_router_logits_and_routing(M, H, E, k, bias):
