@@ -139,6 +139,93 @@ __global__ __launch_bounds__(LH_WAVES * kWave) void lmhead_fp8_kernel(const uint
   }
 }
 
+// Two to MOE_LMHEAD_MAX_TOKENS tokens, H a multiple of 256: the bf16 matrix
+// cores (v_mfma_f32_16x16x32_bf16) take the products, so each code is decoded
+// once and no per-token dot instructions are issued.  The vocabulary rows are
+// the A rows (16-row tiles) and the tokens the B columns (columns past M
+// repeat the last token and are not stored).  A group of 4 waves takes RT
+// tiles, its waves the four quarters of K; a workgroup holds RG groups, which
+// share one LDS stage of x (at H = 2560: 2 tiles per wave, 2 groups, 64 rows
+// per workgroup; the stage is a quarter of the codes' bytes per workgroup).  A
+// wave issues all of its code loads first: for load p, lane (r, g) reads the
+// 16 codes K = k0 + 64 p + 16 g .. + 15 of row r, which are matrix-core steps
+// 2p and 2p + 1 (K slots 8g .. 8g + 7 of each), and the B fragments take the
+// same K elements of the staged x rows, so every pairing is the definition's.
+// Each step's 32-product dot starts from zero (a leaf) and adds into the
+// wave's sum in K order; the four waves' sums are added in K order through
+// LDS, then the scale multiplies: a logit's longest rounding chain is
+// 32 + H / 128 + 3 + 1.
+constexpr int LM_WAVES = 4, LM_MAX_LOADS = MOE_MAX_HIDDEN / 4 / 64;   // 16-byte loads per lane (32)
+constexpr int LM_RT = 2;                                                 // 16-row tiles per wave (H = 2560)
+constexpr int LM_RG = 2;                                                 // 4-wave row groups per workgroup (H = 2560)
+typedef __bf16 lv8bf __attribute__((ext_vector_type(8)));
+typedef float lv4f __attribute__((ext_vector_type(4)));
+template <int NL, bool EXACT, int RT, int RG>   // NL 16-byte code loads per lane and row tile: H = 256 NL
+                                                // (EXACT), or any H up to that; RT 16-row tiles per wave,
+                                                // RG groups of 4 waves (each its own rows) per workgroup
+__global__ __launch_bounds__(LM_WAVES * RG * kWave) void lmhead_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                      const uint8_t* __restrict__ codes,
+                                                                      const float* __restrict__ scales, int M,
+                                                                      int V, int H, float* __restrict__ logits) {
+  extern __shared__ uint4 xs[];                     // [M][H] bf16
+  __shared__ float red[LM_WAVES][16 * RT * RG][17];
+  const int lane = threadIdx.x & (kWave - 1), wave = (threadIdx.x / kWave) % LM_WAVES;
+  const int grp = threadIdx.x / (kWave * LM_WAVES);
+  const int r = lane & 15, g = lane >> 4;
+  const int vb = blockIdx.x * 16 * RT * RG, v0 = vb + grp * 16 * RT;
+  const int kw = wave * (H / LM_WAVES);             // this wave's quarter of K
+  const int nl = EXACT ? NL : H / 256;
+  uint4 cw[RT][NL];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const uint4* row = reinterpret_cast<const uint4*>(codes + (size_t)min(v0 + 16 * i + r, V - 1) * H + kw) + g;
+#pragma unroll
+    for (int p = 0; p < NL; ++p) cw[i][p] = row[4 * min(p, nl - 1)];   // issued before the x stage is waited for
+  }
+  const int nx = M * H / 8;
+  for (int i = threadIdx.x; i < nx; i += blockDim.x) xs[i] = reinterpret_cast<const uint4*>(x)[i];
+  block_barrier_lds();
+  const uint16_t* xt = reinterpret_cast<const uint16_t*>(xs) + (size_t)min(r, M - 1) * H + kw + 16 * g;
+  const lv4f zero = {0.f, 0.f, 0.f, 0.f};
+  lv4f acc[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i) acc[i] = zero;
+#pragma unroll
+  for (int p = 0; p < NL; ++p) {
+    if (p < nl) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {                   // codes 8s .. 8s + 7 of the lane's 16
+        const lv8bf b = __builtin_bit_cast(lv8bf, *reinterpret_cast<const uint4*>(xt + 64 * p + 8 * s));
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+        const uint32_t c4[4] = {cw[i][p].x, cw[i][p].y, cw[i][p].z, cw[i][p].w};
+        const bf16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[2 * s], 1.f, false);
+        const bf16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[2 * s], 1.f, true);
+        const bf16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[2 * s + 1], 1.f, false);
+        const bf16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c4[2 * s + 1], 1.f, true);
+        lv8bf a;
+        a[0] = w0.x; a[1] = w0.y; a[2] = w1.x; a[3] = w1.y;
+        a[4] = w2.x; a[5] = w2.y; a[6] = w3.x; a[7] = w3.y;
+        acc[i] += __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, zero, 0, 0, 0);
+        }
+      }
+    }
+  }
+  // lane (r, g) holds D[4 g + q][r]: vocabulary row v0 + 4 g + q, token r
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][16 * RT * grp + 16 * i + 4 * g + q][r] = acc[i][q];
+  __syncthreads();
+  for (int o = threadIdx.x; o < 256 * RT * RG; o += LM_WAVES * RG * kWave) {
+    const int vr = o >> 4, t = o & 15, v = vb + vr;
+    float sum = red[0][vr][t];
+#pragma unroll
+    for (int w = 1; w < LM_WAVES; ++w) sum += red[w][vr][t];
+    if (t < M && v < V) logits[(size_t)t * V + v] = sum * scales[v];
+  }
+}
+
 hipError_t launch_lmhead_quantize(const uint16_t* w, int V, int H, uint8_t* codes, float* scales,
                                   hipStream_t s) {
   lmhead_quantize_kernel<<<(V + 3) / 4, 256, 0, s>>>(w, V, H, codes, scales);
@@ -151,6 +238,12 @@ hipError_t launch_lmhead_fp8(const uint16_t* x, const uint8_t* codes, const floa
   const unsigned grid = (V + LH_WAVES * LH_RB - 1) / (LH_WAVES * LH_RB);
   const size_t shmem = (size_t)M * H * sizeof(uint16_t);
   void (*k)(const uint16_t*, const uint8_t*, const float*, int, int, int, float*);
+  if (M >= 2 && H % 256 == 0) {
+    k = H == 2560 ? lmhead_mfma_kernel<10, true, LM_RT, LM_RG> : lmhead_mfma_kernel<LM_MAX_LOADS, false, 1, 1>;
+    const int rows = H == 2560 ? 16 * LM_RT * LM_RG : 16, waves = H == 2560 ? LM_WAVES * LM_RG : LM_WAVES;
+    k<<<(V + rows - 1) / rows, waves * kWave, shmem, s>>>(x, codes, scales, M, V, H, logits);
+    return hipGetLastError();
+  }
   if (M == 1) {
     switch (ch) {
       case 1: k = lmhead_fp8_kernel<1, 1>; break;

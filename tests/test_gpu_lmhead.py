@@ -3,8 +3,10 @@
 Quantiser: codes and scales bit-exact (both sides decide in fp32: the scale
 amax / 448 and the quotient w / s are fp32 IEEE operations, the rounding to
 E4M3 is to nearest even).  Projection: within the fp32 rounding-chain bound of
-the kernel's summation (exact products; per lane 16 roundings per 16-byte
-chunk, a 6-level wave tree, the scale multiply)."""
+the kernel's summation (exact products; one token: per lane 16 roundings per
+16-byte chunk, a 6-level wave tree, the scale multiply; two or more tokens on
+rows a multiple of 256: matrix-core leaves added in K order per wave, the four
+waves' sums, the scale multiply)."""
 import numpy as np
 import pytest
 
@@ -33,10 +35,16 @@ def _logits(torch, x_bits, codes, scales):
 
 
 def _bound(x_bits, codes, scales, H):
-    """Rounding-chain bound per logit: (16 ceil(H/1024) + 6) u sum|x w| s + u |ref|."""
+    """Rounding-chain bound per logit, chain · u · sum|x w| · s (+ u |ref| at the
+    call).  One token, or rows not a multiple of 256: per lane 16 roundings per
+    16-byte chunk, a 6-level wave tree, the scale: 16 ceil(H/1024) + 6.  Two or
+    more tokens with rows a multiple of 256 (the matrix cores): a 32-product dot
+    per leaf (counted as 32 roundings), H/128 leaves per wave added in order,
+    the four waves' sums, the scale: 32 + H/128 + 3 + 1."""
     x = oracle.bf16_bits_to_f64(x_bits)
     w = np.abs(oracle.e4m3_decode(codes))
-    chain = 16 * -(-H // 1024) + 6
+    M = x_bits.shape[0]
+    chain = 32 + H // 128 + 4 if M >= 2 and H % 256 == 0 else 16 * -(-H // 1024) + 6
     return (chain * U * (np.abs(x) @ w.T) * scales.astype(np.float64)[None, :]) * 1.01
 
 
@@ -83,7 +91,8 @@ def test_projection_decodes_every_code_exactly():
 
 
 @pytest.mark.parametrize("M,V,H", [(1, 1000, 2560), (4, 777, 2560), (8, 513, 2560), (4, 100, 8192),
-                                   (2, 33, 96), (1, 5, 32), (3, 64, 1056), (5, 70, 6528), (6, 40, 5440)])
+                                   (2, 33, 96), (1, 5, 32), (3, 64, 1056), (5, 70, 6528), (6, 40, 5440),
+                                   (2, 17, 2560), (7, 31, 4096)])
 def test_projection_within_rounding_bound(M, V, H):
     torch = need_gpu()
     say(f"lmhead logits M={M} V={V} H={H}")
