@@ -92,14 +92,26 @@ __global__ __launch_bounds__(RL_WAVES * kWave) void router_lds_kernel(const uint
   }
   for (int t0 = blockIdx.y * RL_TOK; t0 < M; t0 += gridDim.y * RL_TOK) {
     // stage RL_TOK rows (clamped to the last token), 8 bf16 per thread step
+    // (all loads of a thread are issued before its first store, so the
+    // round trips overlap)
     constexpr int kPairs = RL_TOK * VMAX * kWave / 2;    // uint4 entries of the stage
-    for (int i = threadIdx.x; i < kPairs; i += RL_WAVES * kWave) {
+    constexpr int kSteps = kPairs / (RL_WAVES * kWave);
+    static_assert(kPairs % (RL_WAVES * kWave) == 0, "the stage is a whole number of thread steps");
+    uint4 u[kSteps];
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int i = threadIdx.x + j * RL_WAVES * kWave;
       const int q = i / (VMAX * kWave / 2), v2 = i - q * (VMAX * kWave / 2);   // uint2 entries 2 v2, 2 v2 + 1
       const uint4* xrow = reinterpret_cast<const uint4*>(x + (size_t)min(t0 + q, M - 1) * H);
-      const uint4 u = xrow[min(v2, nvec / 2 - 1)];
+      u[j] = xrow[min(v2, nvec / 2 - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int i = threadIdx.x + j * RL_WAVES * kWave;
+      const int q = i / (VMAX * kWave / 2), v2 = i - q * (VMAX * kWave / 2);
       const bool in0 = 2 * v2 < nvec, in1 = 2 * v2 + 1 < nvec;
-      xs[q][2 * v2] = in0 ? make_uint2(u.x, u.y) : make_uint2(0, 0);
-      xs[q][2 * v2 + 1] = in1 ? make_uint2(u.z, u.w) : make_uint2(0, 0);
+      xs[q][2 * v2] = in0 ? make_uint2(u[j].x, u[j].y) : make_uint2(0, 0);
+      xs[q][2 * v2 + 1] = in1 ? make_uint2(u[j].z, u[j].w) : make_uint2(0, 0);
     }
     __syncthreads();
 #pragma unroll
