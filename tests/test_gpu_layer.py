@@ -224,6 +224,35 @@ def test_ling_batch_sampled_tokens(name):
     assert_paths(g["hdr"], wl, g["ids"], name)
 
 
+@pytest.mark.parametrize("name,sets", [("ling_m32_zipf", [0, 7, 21]), ("ling_m512_prefill", [0])])
+def test_ling_batch_helper_streams_bitwise(name, sets):
+    """With the caller's helper streams a batch layer gives bit for bit the
+    output of the one-stream run: each expert path's arithmetic and the
+    fixed-order combine do not depend on the stream that runs them, and the
+    helper paths must cover every expert of their lists exactly once.  y is
+    filled with NaN before each run."""
+    torch = need_gpu()
+    from mxfp4_expert_weight_amd.layer import DeviceLayerSet, HelperStreams, LayerBuffers, run_layer
+    hs = HelperStreams()
+    for si in sets:
+        ls = synth.layer_set(name, si)
+        wl = ls.wl
+        say(f"helper streams vs one stream {name} set {si}")
+        d = DeviceLayerSet.from_host(ls)
+        b = LayerBuffers(wl.M, wl.k, wl.E, wl.H, wl.I)
+        b.y.fill_(float("nan"))
+        run_layer(d, b)
+        torch.cuda.synchronize()
+        ref = b.y.cpu().numpy().copy()
+        assert np.isfinite(ref).all()
+        for rep in range(2):
+            b.y.fill_(float("nan"))
+            run_layer(d, b, helpers=hs)
+            torch.cuda.synchronize()
+            got = b.y.cpu().numpy()
+            assert np.array_equal(got, ref), f"{name} set {si} run {rep}: helper-stream output differs"
+
+
 def test_token_independence_m4_vs_m1():
     """y_t of a 4-token batch equals y_t of token t run alone (dedup changes nothing)."""
     torch = need_gpu()
