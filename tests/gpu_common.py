@@ -20,7 +20,7 @@ def need_gpu():
 
 
 def say(msg: str):
-    """Name the case before each GPU step (flushed, so a lost box still shows it)."""
+    """Name the case before each GPU step (flushed, so a lost machine still shows it)."""
     print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
 
 
