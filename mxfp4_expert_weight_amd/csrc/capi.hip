@@ -135,6 +135,9 @@ moe_status check_opts(const moe_exec_opts* o) {
 // atomics into y, their down kernels wait for the GEMV gate/up kernel that
 // zeroes y; when combining by rows nothing waits, and the combine kernel runs
 // after the join.  Without helpers every kernel goes on `s` in order.
+// Batches of at least this many tokens put most experts on the few-token path.
+constexpr int kMtFirstTokens = 256;
+
 hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, const moe_exec_opts* o) {
   const bool mfma = a.mfma_min == kMfmaMinTokens;
   const bool mt = a.mt_min != INT_MAX;
@@ -158,12 +161,19 @@ hipError_t launch_experts(const ForwardArgs& a, hipStream_t s, const moe_exec_op
     return e;
   }
   // the GEMV kernels go first (their few workgroups are then not queued
-  // behind the matrix-core paths' many); the fork point is before them
+  // behind the matrix-core paths' many); the fork point is before them.
+  // From kMtFirstTokens tokens the few-token gate/up kernel, then the
+  // longest path, is enqueued ahead of them.
   if ((e = hipEventRecord(q.fork, s)) != hipSuccess) return e;
+  const bool mt_first = mt && a.M >= kMtFirstTokens;
+  if (mt_first) {
+    if ((e = hipStreamWaitEvent(q.mt, q.fork, 0)) != hipSuccess) return e;
+    if ((e = launch_gateup_mt(a, q.mt)) != hipSuccess) return e;
+  }
   if ((e = launch_forward(a, s, tm, q.zeroed)) != hipSuccess) return e;
-  if (mt && (e = hipStreamWaitEvent(q.mt, q.fork, 0)) != hipSuccess) return e;
+  if (mt && !mt_first && (e = hipStreamWaitEvent(q.mt, q.fork, 0)) != hipSuccess) return e;
   if (mfma && (e = hipStreamWaitEvent(q.mfma, q.fork, 0)) != hipSuccess) return e;
-  if (mt && (e = launch_gateup_mt(a, q.mt)) != hipSuccess) return e;
+  if (mt && !mt_first && (e = launch_gateup_mt(a, q.mt)) != hipSuccess) return e;
   if (mt && a.act8 && (e = launch_h_round_trip(a, 1, q.mt)) != hipSuccess) return e;
   if (mfma) {
     if (!a.act8 && (e = launch_forward_mfma_front(a, q.mfma)) != hipSuccess) return e;
